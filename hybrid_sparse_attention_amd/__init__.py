@@ -1,0 +1,294 @@
+"""Python binding of liblgsa.so, the gfx950 Latent-Gated Sparse Attention forward library.
+
+Argument marshalling only: every step of the computation runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  The names and arguments mirror
+``include/lgsa.h`` (ERNIE 5.5 Flash Base release blog, section 2.1 "Latent-Gated Sparse
+Attention" defines what the calls compute).
+
+If the library has not been built (``python -m hybrid_sparse_attention_amd.build``) every
+call raises ``LibraryMissing``: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblgsa.so")
+
+LGSA_OK, LGSA_EINVAL, LGSA_EUNSUPPORTED, LGSA_EWORKSPACE, LGSA_EHIP = 0, -1, -2, -3, -4
+LGSA_F32, LGSA_BF16 = 0, 1
+
+EXPORTS = ["lgsa_last_error", "hca_compress", "latent_gate", "hca_attn_fwd",
+           "hca_attn_fwd_workspace", "dsa_index_topk", "dsa_index_topk_workspace",
+           "sparse_attn_fwd", "sparse_attn_fwd_workspace"]
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+class LgsaError(RuntimeError):
+    def __init__(self, name, code, msg):
+        super().__init__("%s failed with status %d: %s" % (name, code, msg))
+        self.code = code
+
+
+_P, _I, _SZ, _F, _LL = (ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float,
+                        ctypes.c_longlong)
+
+
+class HcaArgs(ctypes.Structure):
+    _fields_ = [("dt", _I), ("B", _I), ("Tq", _I), ("H", _I), ("d", _I), ("q", _P),
+                ("pos0", _P), ("max_pos", _I), ("k_win", _P), ("v_win", _P),
+                ("win_len", _I), ("window", _I), ("kc", _P), ("vc", _P), ("n_cap", _I),
+                ("block", _I), ("scale", _F), ("q_lat", _P), ("w_gate", _P), ("d_lat", _I),
+                ("out", _P), ("workspace", _P), ("workspace_bytes", _SZ)]
+
+
+class IndexArgs(ctypes.Structure):
+    _fields_ = [("B", _I), ("Tq", _I), ("S", _I), ("Hi", _I), ("di", _I), ("k", _I),
+                ("q_idx", _P), ("w_idx", _P), ("k_idx", _P), ("pos0", _P), ("max_pos", _I),
+                ("idx_out", _P), ("workspace", _P), ("workspace_bytes", _SZ)]
+
+
+class SparseArgs(ctypes.Structure):
+    _fields_ = [("dt", _I), ("B", _I), ("Tq", _I), ("H", _I), ("d_qk", _I), ("d_v", _I),
+                ("S", _I), ("k", _I), ("q", _P), ("k_lat", _P), ("k_row_stride", _LL),
+                ("v_lat", _P), ("v_row_stride", _LL), ("idx", _P), ("scale", _F),
+                ("q_lat", _P), ("w_gate", _P), ("d_lat", _I), ("out", _P),
+                ("workspace", _P), ("workspace_bytes", _SZ)]
+
+
+_lib = None
+
+
+def load():
+    """Load liblgsa.so (raises LibraryMissing if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryMissing("%s is not built: run python -m hybrid_sparse_attention_amd.build"
+                                 % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.lgsa_last_error.restype = ctypes.c_char_p
+        lib.lgsa_last_error.argtypes = []
+        lib.hca_compress.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
+        lib.latent_gate.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P]
+        for name, st in (("hca_attn_fwd", HcaArgs), ("dsa_index_topk", IndexArgs),
+                         ("sparse_attn_fwd", SparseArgs)):
+            getattr(lib, name).argtypes = [ctypes.POINTER(st), _P]
+            getattr(lib, name + "_workspace").argtypes = [ctypes.POINTER(st),
+                                                          ctypes.POINTER(_SZ)]
+        for name in EXPORTS[1:]:
+            getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def last_error() -> str:
+    return load().lgsa_last_error().decode()
+
+
+def _check(name, rc):
+    if rc != LGSA_OK:
+        raise LgsaError(name, rc, last_error())
+
+
+# ----------------------------------------------------------------------------- torch helpers
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dt(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return LGSA_BF16
+    if t.dtype == torch.float32:
+        return LGSA_F32
+    raise TypeError("tensors must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _dev(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(nbytes, device):
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    buf = torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+    return buf, int(nbytes)
+
+
+# ----------------------------------------------------------------------------- calls
+def hca_compress(k, v, kc=None, vc=None, block=128, stream=None):
+    """Mean of each complete block of `block` rows: k, v [B,T,d] -> kc, vc [B,T//block,d]."""
+    torch = _torch()
+    B, T, d = k.shape
+    if kc is None:
+        kc = torch.empty((B, T // block, d), dtype=k.dtype, device=k.device)
+    if vc is None:
+        vc = torch.empty((B, T // block, d), dtype=v.dtype, device=v.device)
+    rc = load().hca_compress(_dev(k, "k"), _dev(v, "v"), _dev(kc, "kc"), _dev(vc, "vc"), B, T,
+                             d, block, _dt(k), _stream(stream))
+    _check("hca_compress", rc)
+    return kc, vc
+
+
+def latent_gate(q_lat, w_gate, o, out=None, stream=None):
+    """out = o * sigmoid(q_lat @ w_gate) with q_lat [M,d_lat], w_gate [d_lat,N], o [M,N]."""
+    torch = _torch()
+    M, d_lat = q_lat.shape
+    N = w_gate.shape[1]
+    if out is None:
+        out = torch.empty_like(o)
+    rc = load().latent_gate(_dev(q_lat, "q_lat"), _dev(w_gate, "w_gate"), _dev(o, "o"),
+                            _dev(out, "out"), M, d_lat, N, _dt(o), _stream(stream))
+    _check("latent_gate", rc)
+    return out
+
+
+def hca_args(q, pos0, k_win, v_win, kc=None, vc=None, *, max_pos, window=128, block=128,
+             scale=None, q_lat=None, w_gate=None, out=None):
+    B, Tq, H, d = q.shape
+    a = HcaArgs()
+    a.dt = _dt(q)
+    a.B, a.Tq, a.H, a.d = B, Tq, H, d
+    a.q = _dev(q, "q")
+    a.pos0 = _dev(pos0, "pos0")
+    a.max_pos = int(max_pos)
+    a.k_win, a.v_win = _dev(k_win, "k_win"), _dev(v_win, "v_win")
+    a.win_len = k_win.shape[1]
+    a.window = window
+    a.kc = _dev(kc, "kc")
+    a.vc = _dev(vc, "vc")
+    a.n_cap = 0 if kc is None else kc.shape[1]
+    a.block = block
+    a.scale = 1.0 / math.sqrt(d) if scale is None else scale
+    a.q_lat = _dev(q_lat, "q_lat")
+    a.w_gate = _dev(w_gate, "w_gate")
+    a.d_lat = 0 if q_lat is None else q_lat.shape[-1]
+    a.out = _dev(out, "out")
+    return a
+
+
+def hca_attn_fwd(q, pos0, k_win, v_win, kc=None, vc=None, *, max_pos, window=128, block=128,
+                 scale=None, q_lat=None, w_gate=None, out=None, workspace=None, stream=None):
+    """Heavily Compressed Attention forward (optionally gated); see include/lgsa.h."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(q)
+    a = hca_args(q, pos0, k_win, v_win, kc, vc, max_pos=max_pos, window=window, block=block,
+                 scale=scale, q_lat=q_lat, w_gate=w_gate, out=out)
+    need = hca_attn_fwd_workspace(a)
+    if workspace is None:
+        workspace, _ = _workspace(need, q.device)
+    a.workspace = None if workspace is None else workspace.data_ptr()
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("hca_attn_fwd", load().hca_attn_fwd(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def hca_attn_fwd_workspace(a) -> int:
+    n = _SZ(0)
+    _check("hca_attn_fwd_workspace", load().hca_attn_fwd_workspace(ctypes.byref(a),
+                                                                   ctypes.byref(n)))
+    return n.value
+
+
+def index_args(q_idx, w_idx, k_idx, pos0, k, *, max_pos, idx_out=None):
+    B, Tq, Hi, di = q_idx.shape
+    a = IndexArgs()
+    a.B, a.Tq, a.S, a.Hi, a.di, a.k = B, Tq, k_idx.shape[1], Hi, di, k
+    a.q_idx, a.w_idx, a.k_idx = _dev(q_idx, "q_idx"), _dev(w_idx, "w_idx"), _dev(k_idx, "k_idx")
+    a.pos0 = _dev(pos0, "pos0")
+    a.max_pos = int(max_pos)
+    a.idx_out = _dev(idx_out, "idx_out")
+    return a
+
+
+def dsa_index_topk_workspace(a) -> int:
+    n = _SZ(0)
+    _check("dsa_index_topk_workspace", load().dsa_index_topk_workspace(ctypes.byref(a),
+                                                                       ctypes.byref(n)))
+    return n.value
+
+
+def dsa_index_topk(q_idx, w_idx, k_idx, pos0, k, *, max_pos, idx_out=None, workspace=None,
+                   stream=None):
+    """Indexer scores + per-query top-k positions (ascending, -1 padded); see lgsa.h."""
+    torch = _torch()
+    B, Tq = q_idx.shape[:2]
+    if idx_out is None:
+        idx_out = torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device)
+    a = index_args(q_idx, w_idx, k_idx, pos0, k, max_pos=max_pos, idx_out=idx_out)
+    if workspace is None:
+        workspace, _ = _workspace(dsa_index_topk_workspace(a), q_idx.device)
+    a.workspace = None if workspace is None else workspace.data_ptr()
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_index_topk", load().dsa_index_topk(ctypes.byref(a), _stream(stream)))
+    return idx_out
+
+
+def sparse_args(q, k_lat, idx, v_lat=None, *, scale=None, q_lat=None, w_gate=None, out=None,
+                d_qk=None, d_v=None):
+    B, Tq, H, dq = q.shape
+    if v_lat is None:
+        v_lat = k_lat
+    a = SparseArgs()
+    a.dt = _dt(q)
+    a.B, a.Tq, a.H = B, Tq, H
+    a.d_qk = dq if d_qk is None else d_qk
+    a.d_v = v_lat.shape[-1] if d_v is None else d_v
+    a.S = k_lat.shape[1]
+    a.k = idx.shape[-1]
+    a.q = _dev(q, "q")
+    a.k_lat, a.k_row_stride = _dev(k_lat, "k_lat"), k_lat.shape[-1]
+    a.v_lat, a.v_row_stride = _dev(v_lat, "v_lat"), v_lat.shape[-1]
+    a.idx = _dev(idx, "idx")
+    a.scale = 1.0 / math.sqrt(a.d_qk) if scale is None else scale
+    a.q_lat = _dev(q_lat, "q_lat")
+    a.w_gate = _dev(w_gate, "w_gate")
+    a.d_lat = 0 if q_lat is None else q_lat.shape[-1]
+    a.out = _dev(out, "out")
+    return a
+
+
+def sparse_attn_fwd_workspace(a) -> int:
+    n = _SZ(0)
+    _check("sparse_attn_fwd_workspace", load().sparse_attn_fwd_workspace(ctypes.byref(a),
+                                                                         ctypes.byref(n)))
+    return n.value
+
+
+def sparse_attn_fwd(q, k_lat, idx, v_lat=None, *, scale=None, q_lat=None, w_gate=None,
+                    out=None, workspace=None, stream=None):
+    """DSA sparse core attention over the latent rows listed in idx (optionally gated)."""
+    torch = _torch()
+    B, Tq, H, _ = q.shape
+    dv = (k_lat if v_lat is None else v_lat).shape[-1]
+    if out is None:
+        out = torch.empty((B, Tq, H, dv), dtype=q.dtype, device=q.device)
+    a = sparse_args(q, k_lat, idx, v_lat, scale=scale, q_lat=q_lat, w_gate=w_gate, out=out)
+    if workspace is None:
+        workspace, _ = _workspace(sparse_attn_fwd_workspace(a), q.device)
+    a.workspace = None if workspace is None else workspace.data_ptr()
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("sparse_attn_fwd", load().sparse_attn_fwd(ctypes.byref(a), _stream(stream)))
+    return out

@@ -1,0 +1,323 @@
+// C ABI of the Latent-Gated Sparse Attention library (declared in include/lgsa.h).
+// Every entry point validates its arguments on the host before it touches the HIP runtime,
+// so every error path is exercised without a GPU; then it hands over to the launchers.
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/lgsa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+lgsa_status fail(lgsa_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+lgsa_status ok() {
+  g_err.clear();
+  return LGSA_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+lgsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(LGSA_EHIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
+}
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+lgsa::HcaParams to_params(const lgsa_hca_args* a) {
+  lgsa::HcaParams p;
+  p.B = a->B;
+  p.Tq = a->Tq;
+  p.H = a->H;
+  p.d = a->d;
+  p.q = a->q;
+  p.pos0 = a->pos0;
+  p.max_pos = a->max_pos;
+  p.k_win = a->k_win;
+  p.v_win = a->v_win;
+  p.win_len = a->win_len;
+  p.window = a->window;
+  p.kc = a->kc;
+  p.vc = a->vc;
+  p.n_cap = a->n_cap;
+  p.block = a->block;
+  p.scale = a->scale;
+  p.q_lat = a->q_lat;
+  p.w_gate = a->w_gate;
+  p.d_lat = a->d_lat;
+  p.out = a->out;
+  p.ws = a->workspace;
+  p.ws_bytes = a->workspace_bytes;
+  return p;
+}
+
+lgsa_status check_hca(const lgsa_hca_args* a) {
+  REQUIRE(a != nullptr, LGSA_EINVAL, "hca_attn_fwd: args is NULL");
+  REQUIRE(a->dt == LGSA_F32 || a->dt == LGSA_BF16, LGSA_EINVAL, "hca_attn_fwd: unknown dt %d",
+          a->dt);
+  REQUIRE(a->B >= 1 && a->Tq >= 1 && a->H >= 1 && a->d >= 1, LGSA_EINVAL,
+          "hca_attn_fwd: B, Tq, H, d must be >= 1 (got %d, %d, %d, %d)", a->B, a->Tq, a->H,
+          a->d);
+  REQUIRE(a->q && a->pos0 && a->k_win && a->v_win && a->out, LGSA_EINVAL,
+          "hca_attn_fwd: q, pos0, k_win, v_win and out must be non-NULL");
+  REQUIRE(a->win_len >= 1 && a->window >= 1, LGSA_EINVAL,
+          "hca_attn_fwd: win_len and window must be >= 1");
+  // the window rows of one query must not alias in the ring: either the ring is at least a
+  // window long, or no position reaches past its end
+  REQUIRE(a->window <= a->win_len || a->max_pos < a->win_len, LGSA_EINVAL,
+          "hca_attn_fwd: window (%d) exceeds the rows held in k_win/v_win (%d)", a->window,
+          a->win_len);
+  REQUIRE(a->block >= 1, LGSA_EINVAL, "hca_attn_fwd: block must be >= 1");
+  REQUIRE(a->n_cap >= 0, LGSA_EINVAL, "hca_attn_fwd: n_cap must be >= 0");
+  REQUIRE(a->n_cap == 0 || (a->kc && a->vc), LGSA_EINVAL,
+          "hca_attn_fwd: kc and vc must be non-NULL when n_cap > 0");
+  REQUIRE(a->max_pos >= a->Tq - 1, LGSA_EINVAL,
+          "hca_attn_fwd: max_pos (%d) is below Tq - 1 (%d)", a->max_pos, a->Tq - 1);
+  REQUIRE(std::isfinite(a->scale), LGSA_EINVAL, "hca_attn_fwd: scale is not finite");
+  REQUIRE((a->q_lat == nullptr) == (a->w_gate == nullptr), LGSA_EINVAL,
+          "hca_attn_fwd: q_lat and w_gate must be both NULL or both non-NULL");
+  REQUIRE(a->q_lat == nullptr || a->d_lat >= 1, LGSA_EINVAL,
+          "hca_attn_fwd: d_lat must be >= 1 when gated");
+  if (a->dt == LGSA_BF16) {
+    REQUIRE(a->d == 512, LGSA_EUNSUPPORTED, "hca_attn_fwd: bf16 supports d == 512 (got %d)",
+            a->d);
+    REQUIRE(a->q_lat == nullptr || a->d_lat % 64 == 0, LGSA_EUNSUPPORTED,
+            "hca_attn_fwd: bf16 gate needs d_lat %% 64 == 0 (got %d)", a->d_lat);
+    const void* ptrs[] = {a->q, a->k_win, a->v_win, a->kc, a->vc, a->q_lat, a->w_gate, a->out};
+    for (const void* p : ptrs)
+      REQUIRE(aligned(p, 16), LGSA_EINVAL, "hca_attn_fwd: tensors must be 16-byte aligned");
+  } else {
+    REQUIRE(a->d <= 512 && a->d % 4 == 0, LGSA_EUNSUPPORTED,
+            "hca_attn_fwd: f32 supports d <= 512 with d %% 4 == 0 (got %d)", a->d);
+    const void* ptrs[] = {a->q, a->k_win, a->v_win, a->kc, a->vc, a->out};
+    for (const void* p : ptrs)
+      REQUIRE(aligned(p, 16), LGSA_EINVAL, "hca_attn_fwd: tensors must be 16-byte aligned");
+  }
+  return LGSA_OK;
+}
+
+size_t hca_ws(const lgsa_hca_args* a) {
+  const lgsa::HcaParams p = to_params(a);
+  return a->dt == LGSA_BF16 ? lgsa::hca_bf16_workspace(p) : lgsa::hca_f32_workspace(p);
+}
+
+lgsa::IndexParams to_params(const lgsa_index_args* a) {
+  lgsa::IndexParams p;
+  p.B = a->B;
+  p.Tq = a->Tq;
+  p.S = a->S;
+  p.Hi = a->Hi;
+  p.di = a->di;
+  p.k = a->k;
+  p.q_idx = a->q_idx;
+  p.w_idx = a->w_idx;
+  p.k_idx = a->k_idx;
+  p.pos0 = a->pos0;
+  p.max_pos = a->max_pos;
+  p.idx_out = a->idx_out;
+  p.ws = a->workspace;
+  p.ws_bytes = a->workspace_bytes;
+  return p;
+}
+
+lgsa_status check_index(const lgsa_index_args* a) {
+  REQUIRE(a != nullptr, LGSA_EINVAL, "dsa_index_topk: args is NULL");
+  REQUIRE(a->B >= 1 && a->Tq >= 1 && a->S >= 1, LGSA_EINVAL,
+          "dsa_index_topk: B, Tq, S must be >= 1");
+  REQUIRE(a->Hi >= 1 && a->di >= 1 && a->k >= 1, LGSA_EINVAL,
+          "dsa_index_topk: Hi, di, k must be >= 1");
+  REQUIRE(a->q_idx && a->w_idx && a->k_idx && a->pos0 && a->idx_out, LGSA_EINVAL,
+          "dsa_index_topk: q_idx, w_idx, k_idx, pos0 and idx_out must be non-NULL");
+  REQUIRE(a->max_pos >= a->Tq - 1, LGSA_EINVAL,
+          "dsa_index_topk: max_pos (%d) is below Tq - 1 (%d)", a->max_pos, a->Tq - 1);
+  REQUIRE(a->max_pos < a->S, LGSA_EINVAL,
+          "dsa_index_topk: max_pos (%d) must be below S (%d): keys s <= t must exist",
+          a->max_pos, a->S);
+  REQUIRE(a->di == 64, LGSA_EUNSUPPORTED, "dsa_index_topk: di must be 64 (got %d)", a->di);
+  REQUIRE(a->Hi <= 4, LGSA_EUNSUPPORTED, "dsa_index_topk: Hi must be <= 4 (got %d)", a->Hi);
+  REQUIRE(a->k <= 4096, LGSA_EUNSUPPORTED, "dsa_index_topk: k must be <= 4096 (got %d)", a->k);
+  REQUIRE(aligned(a->q_idx, 16) && aligned(a->k_idx, 16), LGSA_EINVAL,
+          "dsa_index_topk: q_idx and k_idx must be 16-byte aligned");
+  return LGSA_OK;
+}
+
+lgsa::SparseParams to_params(const lgsa_sparse_args* a) {
+  lgsa::SparseParams p;
+  p.B = a->B;
+  p.Tq = a->Tq;
+  p.H = a->H;
+  p.d_qk = a->d_qk;
+  p.d_v = a->d_v;
+  p.S = a->S;
+  p.k = a->k;
+  p.q = a->q;
+  p.k_lat = a->k_lat;
+  p.k_stride = a->k_row_stride;
+  p.v_lat = a->v_lat;
+  p.v_stride = a->v_row_stride;
+  p.idx = a->idx;
+  p.scale = a->scale;
+  p.q_lat = a->q_lat;
+  p.w_gate = a->w_gate;
+  p.d_lat = a->d_lat;
+  p.out = a->out;
+  p.ws = a->workspace;
+  p.ws_bytes = a->workspace_bytes;
+  return p;
+}
+
+lgsa_status check_sparse(const lgsa_sparse_args* a) {
+  REQUIRE(a != nullptr, LGSA_EINVAL, "sparse_attn_fwd: args is NULL");
+  REQUIRE(a->dt == LGSA_F32 || a->dt == LGSA_BF16, LGSA_EINVAL,
+          "sparse_attn_fwd: unknown dt %d", a->dt);
+  REQUIRE(a->B >= 1 && a->Tq >= 1 && a->H >= 1 && a->d_qk >= 1 && a->d_v >= 1 && a->S >= 1 &&
+              a->k >= 1,
+          LGSA_EINVAL, "sparse_attn_fwd: B, Tq, H, d_qk, d_v, S, k must be >= 1");
+  REQUIRE(a->q && a->k_lat && a->v_lat && a->idx && a->out, LGSA_EINVAL,
+          "sparse_attn_fwd: q, k_lat, v_lat, idx and out must be non-NULL");
+  REQUIRE(a->k_row_stride >= a->d_qk && a->v_row_stride >= a->d_v, LGSA_EINVAL,
+          "sparse_attn_fwd: row strides must be >= the head dims");
+  REQUIRE(std::isfinite(a->scale), LGSA_EINVAL, "sparse_attn_fwd: scale is not finite");
+  REQUIRE((a->q_lat == nullptr) == (a->w_gate == nullptr), LGSA_EINVAL,
+          "sparse_attn_fwd: q_lat and w_gate must be both NULL or both non-NULL");
+  REQUIRE(a->q_lat == nullptr || a->d_lat >= 1, LGSA_EINVAL,
+          "sparse_attn_fwd: d_lat must be >= 1 when gated");
+  REQUIRE(a->dt == LGSA_BF16, LGSA_EUNSUPPORTED, "sparse_attn_fwd: only bf16 is built");
+  REQUIRE(a->d_qk == 256 && a->d_v == 256, LGSA_EUNSUPPORTED,
+          "sparse_attn_fwd: d_qk and d_v must be 256 (got %d, %d)", a->d_qk, a->d_v);
+  REQUIRE(a->H % 64 == 0, LGSA_EUNSUPPORTED, "sparse_attn_fwd: H must be a multiple of 64");
+  REQUIRE(a->k_row_stride % 8 == 0 && a->v_row_stride % 8 == 0, LGSA_EUNSUPPORTED,
+          "sparse_attn_fwd: row strides must be multiples of 8 elements");
+  REQUIRE(a->q_lat == nullptr || a->d_lat % 64 == 0, LGSA_EUNSUPPORTED,
+          "sparse_attn_fwd: gate needs d_lat %% 64 == 0 (got %d)", a->d_lat);
+  const void* ptrs[] = {a->q, a->k_lat, a->v_lat, a->q_lat, a->w_gate, a->out};
+  for (const void* p : ptrs)
+    REQUIRE(aligned(p, 16), LGSA_EINVAL, "sparse_attn_fwd: tensors must be 16-byte aligned");
+  return LGSA_OK;
+}
+
+lgsa_status check_workspace(const char* name, const void* ws, size_t have, size_t need) {
+  REQUIRE(have >= need, LGSA_EWORKSPACE, "%s: workspace of %zu bytes is below the %zu needed",
+          name, have, need);
+  REQUIRE(need == 0 || ws != nullptr, LGSA_EWORKSPACE, "%s: workspace is NULL", name);
+  REQUIRE(need == 0 || aligned(ws, 16), LGSA_EWORKSPACE, "%s: workspace must be 16-byte aligned",
+          name);
+  return LGSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lgsa_last_error(void) { return g_err.c_str(); }
+
+lgsa_status hca_compress(const void* k, const void* v, void* kc, void* vc, int B, int T, int d,
+                         int block, int dt, void* stream) {
+  REQUIRE(dt == LGSA_F32 || dt == LGSA_BF16, LGSA_EINVAL, "hca_compress: unknown dt %d", dt);
+  REQUIRE(B >= 0 && T >= 0, LGSA_EINVAL, "hca_compress: B and T must be >= 0");
+  REQUIRE(d >= 1 && block >= 1, LGSA_EINVAL, "hca_compress: d and block must be >= 1");
+  REQUIRE(k && v, LGSA_EINVAL, "hca_compress: k and v must be non-NULL");
+  REQUIRE((kc && vc) || T / block == 0 || B == 0, LGSA_EINVAL,
+          "hca_compress: kc and vc must be non-NULL when a block is complete");
+  REQUIRE(d % (dt == LGSA_BF16 ? 8 : 4) == 0, LGSA_EUNSUPPORTED,
+          "hca_compress: d must be a multiple of %d for this dtype", dt == LGSA_BF16 ? 8 : 4);
+  REQUIRE(aligned(k, 16) && aligned(v, 16) && aligned(kc, 16) && aligned(vc, 16), LGSA_EINVAL,
+          "hca_compress: tensors must be 16-byte aligned");
+  return hip_status(lgsa::launch_compress(k, v, kc, vc, B, T, d, block, dt, (hipStream_t)stream),
+                    "hca_compress");
+}
+
+lgsa_status latent_gate(const void* q_lat, const void* w_gate, const void* o, void* out, int M,
+                        int d_lat, int N, int dt, void* stream) {
+  REQUIRE(dt == LGSA_F32 || dt == LGSA_BF16, LGSA_EINVAL, "latent_gate: unknown dt %d", dt);
+  REQUIRE(M >= 0 && d_lat >= 1 && N >= 1, LGSA_EINVAL,
+          "latent_gate: M must be >= 0 and d_lat, N >= 1");
+  REQUIRE(q_lat && w_gate && o && out, LGSA_EINVAL,
+          "latent_gate: q_lat, w_gate, o, out must be non-NULL");
+  if (dt == LGSA_BF16) {
+    REQUIRE(d_lat % 64 == 0 && N % 16 == 0, LGSA_EUNSUPPORTED,
+            "latent_gate: bf16 needs d_lat %% 64 == 0 and N %% 16 == 0 (got %d, %d)", d_lat, N);
+    REQUIRE(aligned(q_lat, 16) && aligned(w_gate, 16) && aligned(o, 8) && aligned(out, 8),
+            LGSA_EINVAL, "latent_gate: q_lat and w_gate must be 16-byte aligned, o and out 8");
+  }
+  return hip_status(lgsa::launch_gate(q_lat, w_gate, o, out, M, d_lat, N, dt,
+                                      (hipStream_t)stream),
+                    "latent_gate");
+}
+
+lgsa_status hca_attn_fwd_workspace(const lgsa_hca_args* a, size_t* bytes) {
+  REQUIRE(bytes != nullptr, LGSA_EINVAL, "hca_attn_fwd_workspace: bytes is NULL");
+  const lgsa_status s = check_hca(a);
+  if (s != LGSA_OK) return s;
+  *bytes = hca_ws(a);
+  return ok();
+}
+
+lgsa_status hca_attn_fwd(const lgsa_hca_args* a, void* stream) {
+  const lgsa_status s = check_hca(a);
+  if (s != LGSA_OK) return s;
+  const lgsa_status w = check_workspace("hca_attn_fwd", a->workspace, a->workspace_bytes,
+                                        hca_ws(a));
+  if (w != LGSA_OK) return w;
+  const lgsa::HcaParams p = to_params(a);
+  const hipError_t e = a->dt == LGSA_BF16 ? lgsa::launch_hca_bf16(p, (hipStream_t)stream)
+                                          : lgsa::launch_hca_f32(p, (hipStream_t)stream);
+  return hip_status(e, "hca_attn_fwd");
+}
+
+lgsa_status dsa_index_topk_workspace(const lgsa_index_args* a, size_t* bytes) {
+  REQUIRE(bytes != nullptr, LGSA_EINVAL, "dsa_index_topk_workspace: bytes is NULL");
+  const lgsa_status s = check_index(a);
+  if (s != LGSA_OK) return s;
+  *bytes = lgsa::index_workspace(to_params(a));
+  return ok();
+}
+
+lgsa_status dsa_index_topk(const lgsa_index_args* a, void* stream) {
+  const lgsa_status s = check_index(a);
+  if (s != LGSA_OK) return s;
+  const lgsa::IndexParams p = to_params(a);
+  // the prefill path streams queries through the workspace in chunks, so it needs one row
+  // of scores at least; the decode path needs exactly what the query reports
+  const size_t need = lgsa::index_min_workspace(p);
+  const lgsa_status w = check_workspace("dsa_index_topk", a->workspace, a->workspace_bytes, need);
+  if (w != LGSA_OK) return w;
+  return hip_status(lgsa::launch_index(p, (hipStream_t)stream), "dsa_index_topk");
+}
+
+lgsa_status sparse_attn_fwd_workspace(const lgsa_sparse_args* a, size_t* bytes) {
+  REQUIRE(bytes != nullptr, LGSA_EINVAL, "sparse_attn_fwd_workspace: bytes is NULL");
+  const lgsa_status s = check_sparse(a);
+  if (s != LGSA_OK) return s;
+  *bytes = lgsa::sparse_workspace(to_params(a));
+  return ok();
+}
+
+lgsa_status sparse_attn_fwd(const lgsa_sparse_args* a, void* stream) {
+  const lgsa_status s = check_sparse(a);
+  if (s != LGSA_OK) return s;
+  const lgsa::SparseParams p = to_params(a);
+  const lgsa_status w = check_workspace("sparse_attn_fwd", a->workspace, a->workspace_bytes,
+                                        lgsa::sparse_workspace(p));
+  if (w != LGSA_OK) return w;
+  return hip_status(lgsa::launch_sparse(p, (hipStream_t)stream), "sparse_attn_fwd");
+}
+
+}  // extern "C"

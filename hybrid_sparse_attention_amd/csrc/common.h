@@ -1,0 +1,84 @@
+// Device-side helpers shared by the gfx950 kernels of the Latent-Gated Sparse Attention
+// library: bfloat16 conversion, MFMA wrappers and fragment types, wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lgsa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// A 16-byte fragment of eight bfloat16 values, viewed either as raw words or as the vector
+// type the MFMA builtins take.
+union Frag8 {
+  uint4 u;
+  bf16x8_t v;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// D = A(16x32) * B(32x16) + C in fp32.  Lane l supplies A row (l % 16) and B column (l % 16),
+// each with the eight contraction indices 8*(l/16) .. 8*(l/16)+7 (any fixed relabelling of
+// the contraction index used for both operands gives the same product).  Lane l receives
+// D rows 4*(l/16) .. 4*(l/16)+3 of column (l % 16).
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const Frag8& a, const Frag8& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max16(float v) {
+  // reduce over the four lanes l, l^16, l^32, l^48 that hold the same MFMA column
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum16(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Transposes an 8x8 block of bfloat16 held as eight 16-byte rows r[0..7] (row j holds
+// columns 0..7) into eight 16-byte columns c[0..7] (column i holds rows 0..7).
+__device__ __forceinline__ void transpose8x8(const uint4 r[8], uint4 c[8]) {
+  const uint32_t* w[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w[j] = reinterpret_cast<const uint32_t*>(&r[j]);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    // columns 2m (low halves) and 2m+1 (high halves) of every row
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const uint32_t x = w[2 * n][m], y = w[2 * n + 1][m];
+      lo[n] = (x & 0xFFFFu) | (y << 16);
+      hi[n] = (x >> 16) | (y & 0xFFFF0000u);
+    }
+    c[2 * m] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    c[2 * m + 1] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float sigmoidf_fast(float g) {
+  // 1 / (1 + e^-g) with e^-g = 2^(-g * log2 e)
+  return 1.0f / (1.0f + fast_exp2(-g * 1.4426950408889634f));
+}
+
+}  // namespace lgsa

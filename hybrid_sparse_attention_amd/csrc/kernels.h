@@ -1,0 +1,83 @@
+// Host-side launchers of the gfx950 kernels.  Arguments are validated by the C-ABI layer
+// (api.cpp) before any of these is called; the launchers only size grids and enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lgsa {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+hipError_t launch_compress(const void* k, const void* v, void* kc, void* vc, int B, int T,
+                           int d, int block, int dt, hipStream_t stream);
+
+// out[m, n] = o[m, n] * sigmoid(q_lat[m, :] . w[:, n]); out may equal o.
+hipError_t launch_gate(const void* q_lat, const void* w, const void* o, void* out, int M,
+                       int d_lat, int N, int dt, hipStream_t stream);
+
+struct HcaParams {
+  int B, Tq, H, d;
+  const void* q;
+  const int32_t* pos0;
+  int max_pos;
+  const void* k_win;
+  const void* v_win;
+  int win_len, window;
+  const void* kc;
+  const void* vc;
+  int n_cap, block;
+  float scale;
+  const void* q_lat;
+  const void* w_gate;
+  int d_lat;
+  void* out;
+  void* ws;
+  size_t ws_bytes;
+};
+
+// bfloat16, d == 512
+size_t hca_bf16_workspace(const HcaParams& p);
+hipError_t launch_hca_bf16(const HcaParams& p, hipStream_t stream);
+// float32, d <= 512
+size_t hca_f32_workspace(const HcaParams& p);
+hipError_t launch_hca_f32(const HcaParams& p, hipStream_t stream);
+
+struct IndexParams {
+  int B, Tq, S, Hi, di, k;
+  const float* q_idx;
+  const float* w_idx;
+  const float* k_idx;
+  const int32_t* pos0;
+  int max_pos;
+  int32_t* idx_out;
+  void* ws;
+  size_t ws_bytes;
+};
+
+size_t index_workspace(const IndexParams& p);      // recommended size
+size_t index_min_workspace(const IndexParams& p);  // smallest size a call accepts
+hipError_t launch_index(const IndexParams& p, hipStream_t stream);
+
+struct SparseParams {
+  int B, Tq, H, d_qk, d_v, S, k;
+  const void* q;
+  const void* k_lat;
+  long long k_stride;
+  const void* v_lat;
+  long long v_stride;
+  const int32_t* idx;
+  float scale;
+  const void* q_lat;
+  const void* w_gate;
+  int d_lat;
+  void* out;
+  void* ws;
+  size_t ws_bytes;
+};
+
+size_t sparse_workspace(const SparseParams& p);
+hipError_t launch_sparse(const SparseParams& p, hipStream_t stream);
+
+}  // namespace lgsa

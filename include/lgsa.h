@@ -1,0 +1,191 @@
+/*
+ * lgsa.h -- C ABI of the Latent-Gated Sparse Attention forward library for AMD gfx950.
+ *
+ * The library implements the attention forward pass of the ERNIE 5.5 Flash layers as the
+ * pages describe it:
+ *   - Heavily Compressed Attention (HCA): each query attends densely to one cache entry per
+ *     completed block of 128 tokens plus a window of the most recent raw tokens, with 512-wide
+ *     heads (ERNIE 5.5 Flash Base release blog, section 2.1 "Latent-Gated Sparse Attention";
+ *     the 128-token window size is from the xenospectrum.com article on ERNIE 5.5 Flash Base,
+ *     long-context section);
+ *   - DeepSeek Sparse Attention (DSA) in the MLA layers: a lightweight indexer scores every
+ *     past position, and core attention with 256-wide heads runs only on the top-k positions
+ *     (release blog, section 2.1);
+ *   - the low-rank output gate: the attention output is multiplied by a gate computed from
+ *     the query latent, which is 4x narrower than the hidden state (release blog, section
+ *     2.1, "low-rank gated attention").
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers (memory of the current HIP device), row-major
+ *     with the last dimension contiguous, unless a field says "host".
+ *   - The caller owns every buffer.  The library allocates nothing, keeps no pointer after a
+ *     call returns and never synchronises the stream: work is only enqueued on `stream`
+ *     (a hipStream_t passed as void*; NULL means the default stream).  Buffers must stay
+ *     alive until that work has completed.  Faults inside kernels surface at the caller's
+ *     next synchronisation, as for any HIP call.
+ *   - Scratch memory is passed in by the caller: query its size with the matching
+ *     *_workspace() call.  A workspace pointer may be NULL only when the query returns 0.
+ *   - Every call validates its arguments on the host before it enqueues anything; on error
+ *     it returns a negative status, enqueues nothing, and lgsa_last_error() describes the
+ *     problem.  No C++ exception crosses the ABI.
+ *   - Results are deterministic: no floating-point atomics, two identical calls give
+ *     bit-identical outputs.
+ *   - Calls are thread-safe and re-entrant (the error message is thread-local).
+ */
+#ifndef LGSA_H
+#define LGSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int lgsa_status;
+#define LGSA_OK 0
+#define LGSA_EINVAL (-1)       /* a pointer, size or relation between sizes is invalid */
+#define LGSA_EUNSUPPORTED (-2) /* valid, but outside the shapes/dtypes this build supports */
+#define LGSA_EWORKSPACE (-3)   /* workspace missing or smaller than the *_workspace query */
+#define LGSA_EHIP (-4)         /* the HIP runtime refused a launch */
+
+/* Element type of the floating-point tensors of a call. */
+#define LGSA_F32 0
+#define LGSA_BF16 1
+
+/* Message of the last non-OK status returned on this thread ("" if none). */
+const char* lgsa_last_error(void);
+
+/* ---------------------------------------------------------------------------------------
+ * hca_compress -- the HCA block compressor (release blog, section 2.1: every 128 tokens are
+ * compressed into one cache entry).  The compressor is read as a mean pool over complete
+ * blocks:  kc[b, e, :] = (1/block) * sum_{i<block} k[b, e*block + i, :], and likewise vc from
+ * v.  Accumulation is in fp32; results are stored in `dt`.
+ *   k, v   [B, T, d]            input keys and values (dt)
+ *   kc, vc [B, T/block, d]      outputs (dt); a trailing incomplete block is not written
+ *                               (kc, vc may be NULL when T < block: nothing is written)
+ * Supported: dt LGSA_F32 (d % 4 == 0) or LGSA_BF16 (d % 8 == 0); block >= 1.
+ * ------------------------------------------------------------------------------------- */
+lgsa_status hca_compress(const void* k, const void* v, void* kc, void* vc, int B, int T, int d,
+                         int block, int dt, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * latent_gate -- the low-rank output gate (release blog, section 2.1):
+ *     out[m, n] = o[m, n] * sigmoid( sum_i q_lat[m, i] * w_gate[i, n] )
+ * with fp32 accumulation; sigmoid(g) = 1 / (1 + exp(-g)).
+ *   q_lat  [M, d_lat]   query latent rows (dt)
+ *   w_gate [d_lat, N]   gate projection (dt)
+ *   o      [M, N]       attention output (dt);  out [M, N] (dt).  out may equal o.
+ * Supported: LGSA_BF16 with d_lat % 32 == 0 and N % 16 == 0; LGSA_F32 with any sizes.
+ * ------------------------------------------------------------------------------------- */
+lgsa_status latent_gate(const void* q_lat, const void* w_gate, const void* o, void* out, int M,
+                        int d_lat, int N, int dt, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * hca_attn_fwd -- Heavily Compressed Attention forward (release blog, section 2.1; window
+ * size from the xenospectrum.com article).  Query row i of sequence b sits at position
+ * t = pos0[b] + i and attends, with one shared key/value head for all H query heads, to
+ *   - compressed entry e < n_cap when e*block + block - 1 <= t (its block is complete), and
+ *   - raw position s for max(0, t - window + 1) <= s <= t, read from row s % win_len of
+ *     k_win / v_win (prefill: win_len = T and the raw k, v; decode: a ring of >= window rows).
+ * Both sets are used as they stand, also where they cover the same tokens.
+ *   O[b,i,h,:] = sum_j softmax_j(scale * <q[b,i,h,:], key_j>) * value_j
+ * and, when q_lat is non-NULL, out = O * sigmoid(q_lat[b,i,:] . w_gate[:, h*d + c]) fused
+ * into the epilogue; otherwise out = O.
+ * --------------------------------------------------------------------------------------- */
+typedef struct {
+  int dt;              /* LGSA_F32 or LGSA_BF16: q, k_win, v_win, kc, vc, q_lat, w_gate, out */
+  int B, Tq, H, d;     /* sequences, query rows per sequence, query heads, head dim */
+  const void* q;       /* [B, Tq, H, d] */
+  const int32_t* pos0; /* device [B]: position of query row 0 of each sequence (>= 0) */
+  int max_pos;         /* host: an upper bound of pos0[b] + Tq - 1 over b (sizes the launch
+                          and is checked against n_cap and win_len) */
+  const void* k_win;   /* [B, win_len, d] raw keys, position p in row p % win_len */
+  const void* v_win;   /* [B, win_len, d] raw values, same rows */
+  int win_len;         /* rows of k_win / v_win (>= window) */
+  int window;          /* raw window length (128 for ERNIE 5.5 Flash), >= 1 */
+  const void* kc;      /* [B, n_cap, d] compressed keys (may be NULL when n_cap == 0) */
+  const void* vc;      /* [B, n_cap, d] compressed values */
+  int n_cap;           /* entries held in kc / vc; must be >= min(needed, ...) see below */
+  int block;           /* tokens per compressed entry (128 for ERNIE 5.5 Flash), >= 1 */
+  float scale;         /* logit scale, normally 1/sqrt(d) */
+  const void* q_lat;   /* [B, Tq, d_lat] or NULL (ungated) */
+  const void* w_gate;  /* [d_lat, H*d] or NULL; NULL exactly when q_lat is NULL */
+  int d_lat;           /* query-latent width (1024 for ERNIE 5.5 Flash) */
+  void* out;           /* [B, Tq, H, d] */
+  void* workspace;     /* scratch, hca_attn_fwd_workspace() bytes */
+  size_t workspace_bytes;
+} lgsa_hca_args;
+/* Validation: every size >= 1 (n_cap >= 0); window <= win_len unless max_pos < win_len (then
+ * no window row wraps around the ring); max_pos >= Tq - 1; kc / vc non-NULL when n_cap > 0.
+ * Entries e >= n_cap are absent: a query sees min(n_cap, (t + 1) / block) entries.
+ * Supported: LGSA_BF16 with d == 512 and d_lat % 32 == 0; LGSA_F32 with d <= 512, d % 4 == 0.
+ * Positions beyond max_pos or below 0 never cause an out-of-bounds access: a row whose
+ * position is negative has no visible key and produces zeros. */
+lgsa_status hca_attn_fwd(const lgsa_hca_args* a, void* stream);
+lgsa_status hca_attn_fwd_workspace(const lgsa_hca_args* a, size_t* bytes);
+
+/* ---------------------------------------------------------------------------------------
+ * dsa_index_topk -- the DSA lightweight indexer and per-query top-k (release blog, section
+ * 2.1: the indexer scores the past positions of each query and core attention runs only on
+ * the k highest-scoring ones).  The indexer form taken here is
+ *     score(t, s) = sum_{h<Hi} w_idx[b,i,h] * max(0, <q_idx[b,i,h,:], k_idx[b,s,:]>)
+ * computed in fp32 for every causal position s <= t, t = pos0[b] + i.  The k highest
+ * scores are kept (all positions when t + 1 <= k); a tie is won by the lower position;
+ * -0.0 counts as +0.0.  idx_out[b,i,:] lists the kept positions in ascending order and
+ * holds -1 in the remaining slots.
+ * --------------------------------------------------------------------------------------- */
+typedef struct {
+  int B, Tq, S;          /* sequences, query rows per sequence, key positions held */
+  int Hi, di, k;         /* indexer heads, indexer head dim, positions kept per query */
+  const float* q_idx;    /* [B, Tq, Hi, di] fp32 */
+  const float* w_idx;    /* [B, Tq, Hi] fp32 */
+  const float* k_idx;    /* [B, S, di] fp32 */
+  const int32_t* pos0;   /* device [B] */
+  int max_pos;           /* host: upper bound of pos0[b] + Tq - 1; must be < S */
+  int32_t* idx_out;      /* [B, Tq, k] int32 */
+  void* workspace;       /* scratch, dsa_index_topk_workspace() bytes */
+  size_t workspace_bytes;
+} lgsa_index_args;
+/* Supported: di == 64, 1 <= Hi <= 8, 1 <= k <= 4096, S >= 1.  A position t >= S (caller
+ * broke the max_pos promise) is clamped to S - 1 for reading; it never reads out of bounds. */
+lgsa_status dsa_index_topk(const lgsa_index_args* a, void* stream);
+lgsa_status dsa_index_topk_workspace(const lgsa_index_args* a, size_t* bytes);
+
+/* ---------------------------------------------------------------------------------------
+ * sparse_attn_fwd -- DSA sparse core attention in the MLA layers (release blog, section 2.1:
+ * core attention only on the selected positions; 256-wide heads for query/key and value).
+ * For query row (b, i) and head h, with the positions listed in idx[b,i,:] (entries < 0 or
+ * >= S are skipped, every other entry is one key, order is irrelevant):
+ *   O[b,i,h,:] = sum_j softmax_j(scale * <q[b,i,h,:], K_j>) * V_j
+ *   K_j = k_lat[b*S*k_row_stride + s_j*k_row_stride + 0 .. d_qk)
+ *   V_j = v_lat[b*S*v_row_stride + s_j*v_row_stride + 0 .. d_v)     (v_lat may equal k_lat)
+ * and, when q_lat is non-NULL, out = O * sigmoid(q_lat[b,i,:] . w_gate[:, h*d_v + c]).
+ * A row with no valid entry produces zeros.
+ * --------------------------------------------------------------------------------------- */
+typedef struct {
+  int dt;                /* LGSA_BF16 */
+  int B, Tq, H, d_qk, d_v, S, k;
+  const void* q;         /* [B, Tq, H, d_qk] */
+  const void* k_lat;     /* [B, S, k_row_stride] latent key rows */
+  long long k_row_stride;/* elements between consecutive positions (>= d_qk) */
+  const void* v_lat;     /* [B, S, v_row_stride] latent value rows (may equal k_lat) */
+  long long v_row_stride;
+  const int32_t* idx;    /* [B, Tq, k] int32 */
+  float scale;           /* normally 1/sqrt(d_qk) */
+  const void* q_lat;     /* [B, Tq, d_lat] or NULL */
+  const void* w_gate;    /* [d_lat, H*d_v] or NULL */
+  int d_lat;
+  void* out;             /* [B, Tq, H, d_v] */
+  void* workspace;       /* scratch, sparse_attn_fwd_workspace() bytes */
+  size_t workspace_bytes;
+} lgsa_sparse_args;
+/* Supported: LGSA_BF16, d_qk == d_v == 256, H % 16 == 0, row strides % 8 == 0,
+ * d_lat % 32 == 0. */
+lgsa_status sparse_attn_fwd(const lgsa_sparse_args* a, void* stream);
+lgsa_status sparse_attn_fwd_workspace(const lgsa_sparse_args* a, size_t* bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LGSA_H */

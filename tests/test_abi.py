@@ -1,0 +1,211 @@
+"""The C-ABI library loads, exports every symbol include/lgsa.h declares, and rejects bad
+arguments on the host with the documented status codes before touching the GPU.
+
+These run without a GPU: every call here is made with arguments that fail validation (or is a
+workspace query, which is host arithmetic only), so no kernel is ever enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hybrid_sparse_attention_amd as lgsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lgsa.h")
+FAKE = 0x10000  # a 16-byte aligned non-NULL address; never dereferenced on these paths
+FAKE_ODD = 0x10002
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lgsa.LIB_PATH):
+        from hybrid_sparse_attention_amd import build
+
+        build.build()
+    return lgsa.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(?:lgsa_status|const char\*)\s+(\w+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = _declared()
+    for n in ("hca_compress", "hca_attn_fwd", "dsa_index_topk", "sparse_attn_fwd",
+              "latent_gate"):
+        assert n in names
+    assert sorted(names) == sorted(lgsa.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    # and the binding declares argument lists for all of them
+    for name in lgsa.EXPORTS:
+        assert getattr(lib, name).argtypes is not None or name == "lgsa_last_error"
+
+
+def _status(rc):
+    return rc, lgsa.last_error()
+
+
+def test_compress_validation(lib):
+    f = lib.hca_compress
+    assert _status(f(None, FAKE, FAKE, FAKE, 1, 256, 512, 128, 1, None))[0] == lgsa.LGSA_EINVAL
+    assert "non-NULL" in lgsa.last_error()
+    assert f(FAKE, FAKE, None, FAKE, 1, 256, 512, 128, 1, None) == lgsa.LGSA_EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 256, 512, 128, 7, None) == lgsa.LGSA_EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 256, 512, 0, 1, None) == lgsa.LGSA_EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 256, 12, 128, 1, None) == lgsa.LGSA_EUNSUPPORTED
+    assert f(FAKE_ODD, FAKE, FAKE, FAKE, 1, 256, 512, 128, 1, None) == lgsa.LGSA_EINVAL
+    assert "aligned" in lgsa.last_error()
+
+
+def test_gate_validation(lib):
+    f = lib.latent_gate
+    assert f(FAKE, FAKE, FAKE, FAKE, 10, 0, 64, 1, None) == lgsa.LGSA_EINVAL
+    assert f(FAKE, None, FAKE, FAKE, 10, 64, 64, 1, None) == lgsa.LGSA_EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, 10, 100, 64, 1, None) == lgsa.LGSA_EUNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 10, 64, 24, 1, None) == lgsa.LGSA_EUNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 10, 64, 64, 5, None) == lgsa.LGSA_EINVAL
+
+
+def _hca(**kw):
+    a = lgsa.HcaArgs()
+    vals = dict(dt=1, B=1, Tq=256, H=64, d=512, q=FAKE, pos0=FAKE, max_pos=255, k_win=FAKE,
+                v_win=FAKE, win_len=256, window=128, kc=FAKE, vc=FAKE, n_cap=2, block=128,
+                scale=0.0441941738, q_lat=FAKE, w_gate=FAKE, d_lat=1024, out=FAKE,
+                workspace=None, workspace_bytes=0)
+    vals.update(kw)
+    for k, v in vals.items():
+        setattr(a, k, v)
+    return a
+
+
+def _call(lib, name, a):
+    return getattr(lib, name)(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(B=0), lgsa.LGSA_EINVAL, "must be >= 1"),
+    (dict(q=None), lgsa.LGSA_EINVAL, "non-NULL"),
+    (dict(window=300, max_pos=300, win_len=256), lgsa.LGSA_EINVAL, "exceeds"),
+    (dict(block=0), lgsa.LGSA_EINVAL, "block"),
+    (dict(kc=None), lgsa.LGSA_EINVAL, "kc and vc"),
+    (dict(max_pos=10), lgsa.LGSA_EINVAL, "max_pos"),
+    (dict(w_gate=None), lgsa.LGSA_EINVAL, "both NULL"),
+    (dict(scale=float("inf")), lgsa.LGSA_EINVAL, "scale"),
+    (dict(dt=3), lgsa.LGSA_EINVAL, "dt"),
+    (dict(d=256), lgsa.LGSA_EUNSUPPORTED, "d == 512"),
+    (dict(d_lat=1000), lgsa.LGSA_EUNSUPPORTED, "d_lat"),
+    (dict(dt=0, d=600), lgsa.LGSA_EUNSUPPORTED, "d <= 512"),
+    (dict(q=FAKE_ODD), lgsa.LGSA_EINVAL, "aligned"),
+])
+def test_hca_validation(lib, kw, code, msg):
+    a = _hca(**kw)
+    assert _call(lib, "hca_attn_fwd", a) == code
+    assert msg in lgsa.last_error()
+    n = ctypes.c_size_t(0)
+    assert lib.hca_attn_fwd_workspace(ctypes.byref(a), ctypes.byref(n)) == code
+
+
+def test_hca_workspace_queries(lib):
+    n = ctypes.c_size_t(123)
+    # prefill needs no workspace
+    assert lib.hca_attn_fwd_workspace(ctypes.byref(_hca()), ctypes.byref(n)) == 0
+    assert n.value == 0
+    # decode of one long sequence is split over workgroups: partial (m, l, O) per split
+    a = _hca(B=1, Tq=1, max_pos=131071, win_len=128, n_cap=1024)
+    assert lib.hca_attn_fwd_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
+    assert n.value > 0 and n.value % (64 * 4) == 0
+    # a decode call without that workspace is refused before any launch
+    assert _call(lib, "hca_attn_fwd", a) == lgsa.LGSA_EWORKSPACE
+    a.workspace, a.workspace_bytes = FAKE, n.value - 1
+    assert _call(lib, "hca_attn_fwd", a) == lgsa.LGSA_EWORKSPACE
+
+
+def _idx(**kw):
+    a = lgsa.IndexArgs()
+    vals = dict(B=1, Tq=4096, S=4096, Hi=4, di=64, k=2048, q_idx=FAKE, w_idx=FAKE, k_idx=FAKE,
+                pos0=FAKE, max_pos=4095, idx_out=FAKE, workspace=None, workspace_bytes=0)
+    vals.update(kw)
+    for k, v in vals.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(S=0), lgsa.LGSA_EINVAL, ">= 1"),
+    (dict(k=0), lgsa.LGSA_EINVAL, ">= 1"),
+    (dict(max_pos=4096), lgsa.LGSA_EINVAL, "below S"),
+    (dict(max_pos=100), lgsa.LGSA_EINVAL, "max_pos"),
+    (dict(idx_out=None), lgsa.LGSA_EINVAL, "non-NULL"),
+    (dict(di=128), lgsa.LGSA_EUNSUPPORTED, "di"),
+    (dict(Hi=8), lgsa.LGSA_EUNSUPPORTED, "Hi"),
+    (dict(k=5000), lgsa.LGSA_EUNSUPPORTED, "k must"),
+    (dict(q_idx=FAKE_ODD), lgsa.LGSA_EINVAL, "aligned"),
+])
+def test_index_validation(lib, kw, code, msg):
+    a = _idx(**kw)
+    assert _call(lib, "dsa_index_topk", a) == code
+    assert msg in lgsa.last_error()
+
+
+def test_index_workspace(lib):
+    n = ctypes.c_size_t(0)
+    a = _idx()
+    assert lib.dsa_index_topk_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
+    assert n.value >= 4096 * 4  # at least one row of scores
+    assert _call(lib, "dsa_index_topk", a) == lgsa.LGSA_EWORKSPACE
+    d = _idx(B=8, Tq=1, S=1 << 20, max_pos=(1 << 20) - 1)
+    assert lib.dsa_index_topk_workspace(ctypes.byref(d), ctypes.byref(n)) == 0
+    # decode: 64 segments of 16384 positions, k candidates (key + position) each
+    assert n.value == 8 * 64 * 2048 * 8
+
+
+def _sp(**kw):
+    a = lgsa.SparseArgs()
+    vals = dict(dt=1, B=1, Tq=16, H=64, d_qk=256, d_v=256, S=4096, k=2048, q=FAKE, k_lat=FAKE,
+                k_row_stride=256, v_lat=FAKE, v_row_stride=256, idx=FAKE, scale=0.0625,
+                q_lat=None, w_gate=None, d_lat=0, out=FAKE, workspace=None, workspace_bytes=0)
+    vals.update(kw)
+    for k, v in vals.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(k=0), lgsa.LGSA_EINVAL, ">= 1"),
+    (dict(idx=None), lgsa.LGSA_EINVAL, "non-NULL"),
+    (dict(k_row_stride=128), lgsa.LGSA_EINVAL, "strides"),
+    (dict(q_lat=FAKE), lgsa.LGSA_EINVAL, "both NULL"),
+    (dict(dt=0), lgsa.LGSA_EUNSUPPORTED, "bf16"),
+    (dict(d_qk=128), lgsa.LGSA_EUNSUPPORTED, "256"),
+    (dict(H=48), lgsa.LGSA_EUNSUPPORTED, "multiple of 64"),
+    (dict(k_row_stride=260), lgsa.LGSA_EUNSUPPORTED, "multiples of 8"),
+    (dict(out=FAKE_ODD), lgsa.LGSA_EINVAL, "aligned"),
+])
+def test_sparse_validation(lib, kw, code, msg):
+    a = _sp(**kw)
+    assert _call(lib, "sparse_attn_fwd", a) == code
+    assert msg in lgsa.last_error()
+
+
+def test_sparse_workspace_split_for_few_rows(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.sparse_attn_fwd_workspace(ctypes.byref(_sp(Tq=4096)), ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.sparse_attn_fwd_workspace(ctypes.byref(_sp(B=8, Tq=1)), ctypes.byref(n)) == 0
+    assert n.value > 0
+    assert _call(lib, "sparse_attn_fwd", _sp(B=8, Tq=1)) == lgsa.LGSA_EWORKSPACE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(lgsa, "_lib", None)
+    monkeypatch.setattr(lgsa, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(lgsa.LibraryMissing):
+        lgsa.load()
