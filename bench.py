@@ -1,0 +1,354 @@
+"""Benchmark of the Latent-Gated Sparse Attention forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs 1,2,3,4] [--no-cpu]
+
+A step is one pass of the hot path over one batch of synthetic input of the HCA prefill at
+model shape (seq 32768, 64 query heads sharing one KV head, head dim 512, bf16, 256 mean-pooled
+compressed entries + 128-token window, gate from the 1024-wide query latent): hca_compress
+then hca_attn_fwd with the gate fused.  `value` is its algorithmic TFLOP/s (attention over the
+visible pairs + the gate GEMM).  The decode and MLA-DSA workloads are timed too and reported
+under "secondary" in the same JSON line.  Inputs are seeded synthetic data already resident
+in HBM when timing starts.  The CPU baseline times the fp64 oracle on a bounded sample of
+query rows of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HCA/DSA attention prefill TFLOP/s + decode GB/s; % of MI355X roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (matrix / packed vector)
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------- work formulas
+def hca_pairs(T, block=128, window=128, n_cap=None):
+    """Visible (query, key) pairs per head of an HCA prefill from position 0."""
+    t = np.arange(T, dtype=np.int64)
+    nc = (t + 1) // block
+    if n_cap is not None:
+        nc = np.minimum(nc, n_cap)
+    return int(np.sum(nc + np.minimum(t + 1, window)))
+
+
+def hca_prefill_flops(T, H, d=512, d_lat=1024, gated=True):
+    att = 4.0 * d * hca_pairs(T) * H
+    gate = 2.0 * T * d_lat * H * d if gated else 0.0
+    return att, gate
+
+
+def src_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------- timing helpers
+class Timer:
+    """HIP events recorded on the stream the kernels run on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def event(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        return e
+
+
+def flush_cache(torch, buf):
+    buf.add_(1)  # touches 1 GiB so the 256 MB Infinity Cache holds none of the inputs
+
+
+# --------------------------------------------------------------------------- workloads
+def run_c1(torch, lgsa, synth, to_dev, steps, warmup):
+    T, H, d = 32768, 64, 512
+    log("[bench] C1: generating inputs (seq %d, %d heads, d %d)" % (T, H, d))
+    x = synth.hca_prefill(1, T=T, H=H, d=d, bf16=True, qkv_scale=1.0 / math.sqrt(512))
+    dev = {k: to_dev(v) for k, v in x.items()}
+    kc = torch.empty((1, T // 128, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    out = torch.empty_like(dev["q"])
+    stream = torch.cuda.current_stream()
+    tm = Timer(torch, stream)
+
+    def step(evs=None):
+        lgsa.hca_compress(dev["k"], dev["v"], kc, vc)
+        if evs is not None:
+            evs.append(tm.event())
+        lgsa.hca_attn_fwd(dev["q"], dev["pos0"], dev["k"], dev["v"], kc, vc, max_pos=T - 1,
+                          q_lat=dev["q_lat"], w_gate=dev["w_gate"], out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log("[bench] C1: timing %d steps" % steps)
+    marks = []
+    t0 = tm.event()
+    for _ in range(steps):
+        step(marks)
+        marks.append(tm.event())
+    t1 = tm.event()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    # per-kernel: compress = [end of previous step, mark], attention = [mark, end of step]
+    starts = [t0] + marks[1::2][:-1]
+    comp_ms = [a.elapsed_time(b) for a, b in zip(starts, marks[0::2])]
+    attn_ms = [a.elapsed_time(b) for a, b in zip(marks[0::2], marks[1::2])]
+    att, gate = hca_prefill_flops(T, H, d)
+    return dict(ms_per_step=total_ms / steps, flops=att + gate, att_flops=att, gate_flops=gate,
+                attn_ms=float(np.mean(attn_ms)), compress_ms=float(np.mean(comp_ms)),
+                inputs=x)
+
+
+def run_c2(torch, lgsa, synth, to_dev, iters):
+    B, ctx, H, d = 64, 131072, 64, 512
+    log("[bench] C2: generating inputs (batch %d, context %d)" % (B, ctx))
+    x = synth.hca_decode(2, B=B, context=ctx, H=H)
+    dev = {k: to_dev(v) for k, v in x.items()}
+    out = torch.empty_like(dev["q"])
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    tm = Timer(torch, torch.cuda.current_stream())
+
+    def step():
+        lgsa.hca_attn_fwd(dev["q"], dev["pos0"], dev["k_win"], dev["v_win"], dev["kc"],
+                          dev["vc"], max_pos=ctx - 1, q_lat=dev["q_lat"], w_gate=dev["w_gate"],
+                          out=out)
+
+    for _ in range(3):
+        step()
+    ms = []
+    for _ in range(iters):
+        flush_cache(torch, flush)
+        a = tm.event()
+        step()
+        b = tm.event()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    nbytes = sum(int(v.nbytes) for k, v in x.items() if k != "pos0") + int(x["q"].nbytes)
+    return dict(ms=float(np.median(ms)), ms_min=float(np.min(ms)), bytes=nbytes)
+
+
+def run_c3(torch, lgsa, synth, to_dev, iters):
+    T, H, d, k = 65536, 64, 256, 2048
+    log("[bench] C3: generating inputs (seq %d, top-%d)" % (T, k))
+    xi = synth.dsa_index(3, B=1, Tq=T, S=T)
+    xs = synth.dsa_sparse(3, B=1, Tq=T, S=T, H=H, d=d)
+    di = {k_: to_dev(v) for k_, v in xi.items()}
+    ds = {k_: to_dev(v) for k_, v in xs.items()}
+    idx = torch.empty((1, T, k), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(ds["q"])
+    tm = Timer(torch, torch.cuda.current_stream())
+
+    def step(evs):
+        evs.append(tm.event())
+        lgsa.dsa_index_topk(di["q_idx"], di["w_idx"], di["k_idx"], di["pos0"], k,
+                            max_pos=T - 1, idx_out=idx)
+        evs.append(tm.event())
+        lgsa.sparse_attn_fwd(ds["q"], ds["kv_lat"], idx, q_lat=ds["q_lat"],
+                             w_gate=ds["w_gate"], out=out)
+        evs.append(tm.event())
+
+    step([])
+    torch.cuda.synchronize()
+    idx_ms, sp_ms = [], []
+    for _ in range(iters):
+        e = []
+        step(e)
+        torch.cuda.synchronize()
+        idx_ms.append(e[0].elapsed_time(e[1]))
+        sp_ms.append(e[1].elapsed_time(e[2]))
+    pairs = int(sum(min(k, t + 1) for t in range(T)))
+    sp_flops = 4.0 * d * pairs * H + 2.0 * T * 1024 * H * d
+    ind_pairs = T * (T + 1) // 2
+    ind_flops = ind_pairs * (4 * 2 * 64 + 8)
+    return dict(index_ms=float(np.median(idx_ms)), sparse_ms=float(np.median(sp_ms)),
+                sparse_flops=sp_flops, index_flops=float(ind_flops))
+
+
+def run_c4(torch, lgsa, synth, to_dev, iters):
+    B, ctx, H = 8, 1 << 20, 64
+    log("[bench] C4: generating inputs (batch %d, context %d)" % (B, ctx))
+    xh = synth.hca_decode(4, B=B, context=ctx, H=H)
+    xi = synth.dsa_index(4, B=B, Tq=1, S=ctx, pos0=[ctx - 1] * B)
+    xs = synth.dsa_sparse(4, B=B, Tq=1, S=ctx, H=H, qname="q_dsa", latname="q_lat_dsa",
+                          wname="w_gate_dsa")
+    dh = {k: to_dev(v) for k, v in xh.items()}
+    di = {k: to_dev(v) for k, v in xi.items()}
+    ds = {k: to_dev(v) for k, v in xs.items()}
+    del xs["kv_lat"]
+    out_h = torch.empty_like(dh["q"])
+    out_s = torch.empty_like(ds["q"])
+    idx = torch.empty((B, 1, 2048), dtype=torch.int32, device="cuda")
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    tm = Timer(torch, torch.cuda.current_stream())
+
+    def step(evs):
+        evs.append(tm.event())
+        lgsa.hca_attn_fwd(dh["q"], dh["pos0"], dh["k_win"], dh["v_win"], dh["kc"], dh["vc"],
+                          max_pos=ctx - 1, q_lat=dh["q_lat"], w_gate=dh["w_gate"], out=out_h)
+        evs.append(tm.event())
+        lgsa.dsa_index_topk(di["q_idx"], di["w_idx"], di["k_idx"], di["pos0"], 2048,
+                            max_pos=ctx - 1, idx_out=idx)
+        evs.append(tm.event())
+        lgsa.sparse_attn_fwd(ds["q"], ds["kv_lat"], idx, q_lat=ds["q_lat"],
+                             w_gate=ds["w_gate"], out=out_s)
+        evs.append(tm.event())
+
+    step([])
+    torch.cuda.synchronize()
+    tot, ind = [], []
+    for _ in range(iters):
+        flush_cache(torch, flush)
+        e = []
+        step(e)
+        torch.cuda.synchronize()
+        tot.append(e[0].elapsed_time(e[3]))
+        ind.append(e[1].elapsed_time(e[2]))
+    hbytes = sum(int(v.nbytes) for k, v in xh.items() if k != "pos0") + int(xh["q"].nbytes)
+    ibytes = sum(int(v.nbytes) for k, v in xi.items() if k != "pos0") + B * 2048 * 4
+    sbytes = (sum(int(v.nbytes) for v in xs.values()) + B * 2048 * 256 * 2 +
+              int(xs["q"].nbytes))
+    return dict(ms=float(np.median(tot)), index_ms=float(np.median(ind)),
+                bytes=hbytes + ibytes + sbytes, index_bytes=ibytes)
+
+
+# --------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(x, budget_s=15.0):
+    """The fp64 oracle on a bounded, evenly spread sample of query rows of the C1 workload."""
+    import oracle
+
+    oracle.build(force=False)
+    T, H, d = 32768, 64, 512
+    kc = oracle.hca_compress(x["k"])
+    vc = oracle.hca_compress(x["v"])
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.hca_attn(x["q"], x["pos0"], x["k"], x["v"], kc, vc, q_lat=x["q_lat"],
+                        w_gate=x["w_gate"], rows=rows)
+        return time.perf_counter() - t0
+
+    probe = np.arange(0, T, T // 16)
+    dt = run(probe)
+    n = int(max(16, min(T, budget_s / max(dt / len(probe), 1e-6))))
+    rows = np.unique(np.linspace(0, T - 1, n).astype(np.int64))
+    secs = run(rows)
+    t = rows
+    pairs = np.sum((t + 1) // 128 + np.minimum(t + 1, 128))
+    flops = 4.0 * d * pairs * H + 2.0 * len(rows) * 1024 * H * d
+    return dict(value=flops / secs / 1e12, unit="TFLOP/s", cores=oracle.max_threads(),
+                kind="oracle",
+                sample="%d of %d query rows (all %d heads, gated), evenly spaced; %.1f s"
+                       % (len(rows), T, H, secs))
+
+
+def traffic_record(kernel_src):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current source of the kernel."""
+    path = os.path.join(ROOT, "profiles", "hca_prefill_c1_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha") != src_sha(kernel_src):
+        return None
+    return float(rec["bytes_per_launch"])
+
+
+# --------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--configs", default="1,2,3,4",
+                    help="workloads to run; 1 is the headline, 2-4 are reported as secondary")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import hybrid_sparse_attention_amd as lgsa
+    from hybrid_sparse_attention_amd import synth
+
+    lgsa.load()  # fails loudly if the library is not built
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    cfgs = [int(c) for c in args.configs.split(",") if c]
+    r1 = run_c1(torch, lgsa, synth, to_dev, args.steps, args.warmup)
+    value = r1["flops"] / (r1["ms_per_step"] * 1e-3) / 1e12
+    att_tf = r1["flops"] / (r1["attn_ms"] * 1e-3) / 1e12
+    kernel_src = os.path.join(ROOT, "hybrid_sparse_attention_amd", "csrc", "hca_bf16.hip")
+    roofline = dict(bound="mfma", kernel="hca_prefill_kernel (attention + fused gate)",
+                    achieved=round(att_tf, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(att_tf / PEAK_BF16_TFLOPS, 4),
+                    traffic=traffic_record(kernel_src),
+                    launch_ms=round(r1["attn_ms"], 4),
+                    flops_per_launch=r1["flops"])
+    secondary = dict(c1_compress_ms=round(r1["compress_ms"], 4))
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] CPU baseline: fp64 oracle on a sample of C1 rows")
+        cpu = cpu_baseline(r1["inputs"])
+    del r1["inputs"]
+    if 2 in cfgs:
+        r2 = run_c2(torch, lgsa, synth, to_dev, 50)
+        gbps = r2["bytes"] / (r2["ms"] * 1e-3) / 1e9
+        secondary["c2_hca_decode"] = dict(ms=round(r2["ms"], 4), GBps=round(gbps, 1),
+                                          hbm_frac=round(gbps / PEAK_HBM_GBPS, 4),
+                                          bytes=r2["bytes"])
+    if 3 in cfgs:
+        r3 = run_c3(torch, lgsa, synth, to_dev, 3)
+        sp_tf = r3["sparse_flops"] / (r3["sparse_ms"] * 1e-3) / 1e12
+        ix_tf = r3["index_flops"] / (r3["index_ms"] * 1e-3) / 1e12
+        secondary["c3_dsa_prefill"] = dict(
+            sparse_gate_ms=round(r3["sparse_ms"], 3), sparse_gate_TFLOPs=round(sp_tf, 1),
+            sparse_mfma_frac=round(sp_tf / PEAK_BF16_TFLOPS, 4),
+            indexer_ms=round(r3["index_ms"], 3), indexer_TFLOPs=round(ix_tf, 1),
+            indexer_fp32_frac=round(ix_tf / PEAK_FP32_TFLOPS, 4))
+    if 4 in cfgs:
+        r4 = run_c4(torch, lgsa, synth, to_dev, 10)
+        gbps = r4["bytes"] / (r4["ms"] * 1e-3) / 1e9
+        igbps = r4["index_bytes"] / (r4["index_ms"] * 1e-3) / 1e9
+        secondary["c4_mixed_decode"] = dict(ms=round(r4["ms"], 4), GBps=round(gbps, 1),
+                                            hbm_frac=round(gbps / PEAK_HBM_GBPS, 4),
+                                            indexer_ms=round(r4["index_ms"], 4),
+                                            indexer_GBps=round(igbps, 1), bytes=r4["bytes"])
+    line = dict(
+        metric=METRIC, value=round(value, 2), unit="TFLOP/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=round(r1["ms_per_step"], 4), higher_is_better=True,
+        scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+        config=dict(workload="HCA prefill at model shape: seq 32768, 64 query heads + 1 shared "
+                             "KV head, head dim 512, bf16, 256 mean-pooled entries + 128-token "
+                             "window, fused low-rank gate (W_gate 1024x32768); step = "
+                             "hca_compress + hca_attn_fwd",
+                    seq_len=32768, heads=64, head_dim=512, batch=1, parallelism="none"),
+        roofline=roofline, cpu_baseline=cpu, secondary=secondary)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -82,3 +82,39 @@ __device__ __forceinline__ float sigmoidf_fast(float g) {
 }
 
 }  // namespace lgsa
+
+namespace lgsa {
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// LDS DMA: every lane fetches 16 bytes from its global address `src`; lane l's bytes land at
+// lds + 16 * l, where `lds` must be the same for all lanes of the wave (it is passed through
+// M0).  The data is in LDS once the wave's vector-memory counter has drained.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds, 16, 0, 0);
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i reads the
+// four 16-bit values R_i[0..3] at its own address; lane j = 4a + c then receives
+// { R_a[c], R_{a+4}[c], R_{a+8}[c], R_{a+12}[c] }.  With lane i pointing at row K_{i/4},
+// columns 4(i%4) .. 4(i%4)+3 of a row-major tile, lane j receives column j of rows K_0..K_3:
+// the strided operand an MFMA needs when the contraction runs over rows.
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t*)p);
+  uint2 u;
+  __builtin_memcpy(&u, &r, sizeof u);
+  return u;
+}
+
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Hides a value from the optimiser so that addresses derived from it are recomputed where
+// they are used instead of being hoisted (and kept live) across a loop.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+}  // namespace lgsa
