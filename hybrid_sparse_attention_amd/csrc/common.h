@@ -28,8 +28,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to a packed bfloat16 pair, round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // D = A(16x32) * B(32x16) + C in fp32.  Lane l supplies A row (l % 16) and B column (l % 16),
