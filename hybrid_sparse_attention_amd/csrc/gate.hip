@@ -123,6 +123,180 @@ __global__ __launch_bounds__(256) void gate_bf16_kernel(const uint16_t* __restri
   }
 }
 
+// Large-M bfloat16 path: 256 channels x 256 rows per workgroup, 8 waves of 128 x 64, K in
+// steps of 64.  Both operand tiles reach LDS by LDS DMA (no register staging), two stages
+// deep.  W rows (256 channels = 512 bytes) keep W row-major in LDS and the MFMA operand W^T
+// is read with the transposing LDS read; q_lat rows (64 k = 128 bytes) are read as 16-byte
+// fragments.  Bank conflicts are removed by XOR swizzles of 16-byte chunks, applied by
+// permuting which chunk each lane fetches; the swizzle bits a lane needs are constant per lane,
+// so fragment addresses are lane constants plus immediates.
+constexpr int G2_BN = 256, G2_BM = 256, G2_BK = 64;
+constexpr int G2_WROW = G2_BN * 2;              // bytes per staged W row
+constexpr int G2_QROW = G2_BK * 2;              // bytes per staged q_lat row
+constexpr int G2_WSTAGE = G2_BK * G2_WROW;      // 32 KiB
+constexpr int G2_QSTAGE = G2_BM * G2_QROW;      // 32 KiB
+constexpr int G2_STAGE = G2_WSTAGE + G2_QSTAGE;
+constexpr size_t G2_SMEM = 2 * G2_STAGE;
+
+__device__ __forceinline__ int g2_wswz(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+__device__ __forceinline__ int g2_qswz(int r) { return (r >> 1) & 7; }
+
+extern __shared__ __attribute__((aligned(1024))) char g2_smem[];
+
+__global__ __launch_bounds__(512, 1) void gate_bf16_big_kernel(const uint16_t* __restrict__ ql,
+                                                               const uint16_t* __restrict__ w,
+                                                               const uint16_t* o, uint16_t* out,
+                                                               int M, int d_lat, int N) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int wn = wave & 1, wm = wave >> 1;
+  // XCD-aware tile order: XCD x (= id % 8) takes a contiguous run of tiles.  Within the run,
+  // tiles are visited in groups of 4 channel tiles x 8 row tiles, so the ~32 workgroups an
+  // XCD runs at once share 4 W slices and 8 q_lat slices, which stay in its L2.
+  const int n_nt = (N + G2_BN - 1) / G2_BN, n_mt = (M + G2_BM - 1) / G2_BM;
+  const int tiles = n_nt * n_mt;
+  int lin = blockIdx.x;
+  if (tiles % 8 == 0) lin = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
+  int nt, mt;
+  if (n_nt % 4 == 0 && n_mt % 8 == 0) {
+    const int grp = lin / 32, in = lin % 32;
+    const int groups_m = n_mt / 8;
+    nt = (grp / groups_m) * 4 + in / 8;
+    mt = (grp % groups_m) * 8 + in % 8;
+  } else {
+    nt = lin / n_mt;
+    mt = lin % n_mt;
+  }
+  const int n0 = nt * G2_BN, m0 = mt * G2_BM;
+
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // DMA of one K step into stage s: 32 W instructions (2 k-rows each) and 32 q_lat
+  // instructions (8 rows each); 8 per wave.
+  auto dma = [&](int k0, int s) {
+    char* sw = g2_smem + s * G2_STAGE;
+    char* sq = sw + G2_WSTAGE;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ins = wave + 8 * u;                  // 0..31
+      const int kr = 2 * ins + (lane >> 5);          // k-row of this lane
+      const int chunk = (lane & 31) ^ g2_wswz(kr);   // 16-byte chunk it fetches
+      const int n = min(n0 + 8 * chunk, N - 8);      // columns past N repeat the last chunk
+      lds_dma16(w + (size_t)(k0 + kr) * N + n, sw + 2 * ins * G2_WROW);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ins = wave + 8 * u;                  // 0..31
+      const int r = 8 * ins + (lane >> 3);           // row of this lane
+      const int chunk = (lane & 7) ^ g2_qswz(r);
+      const int m = min(m0 + r, M - 1);              // rows past M repeat the last row
+      lds_dma16(ql + (size_t)m * d_lat + k0 + 8 * chunk, sq + 8 * ins * G2_QROW);
+    }
+  };
+
+  // lane-constant fragment offsets
+  const int a = l16 >> 2, c4 = l16 & 3;
+  const int wf = g2_wswz(8 * g + a);                 // same for k-rows 32ks + 8g + 4h + a
+  int wcol[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    wcol[i] = 16 * ((16 * wn + 2 * i + (c4 >> 1)) ^ wf) + 8 * (c4 & 1);
+  const int qf = g2_qswz(l16);
+  const int qrow = (64 * wm + l16) * G2_QROW;
+  const int qc0 = 16 * ((g) ^ qf), qc1 = 16 * ((4 + g) ^ qf);
+
+  const int nk = d_lat / G2_BK;
+  dma(0, 0);
+  wait_all();
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int s = kt & 1;
+    if (kt + 1 < nk) dma((kt + 1) * G2_BK, s ^ 1);
+    const char* sw = g2_smem + s * G2_STAGE;
+    const char* sq = sw + G2_WSTAGE;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      Frag8 bq[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bq[j].u = *(const uint4*)(sq + qrow + 16 * j * G2_QROW + (ks ? qc1 : qc0));
+      const char* wr = sw + (32 * ks + 8 * g + a) * G2_WROW;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        Frag8 aw;
+        const uint2 lo = lds_read_tr16(wr + wcol[i]);
+        const uint2 hi = lds_read_tr16(wr + wcol[i] + 4 * G2_WROW);
+        aw.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(aw, bq[j], acc[i][j]);
+      }
+    }
+    wait_all();
+    __syncthreads();
+  }
+  // epilogue: lane holds G[m = m0 + 64wm + 16j + l16][n = n0 + 128wn + 16i + 4g .. +3].
+  // In two halves (waves 0-3, then 4-7), the owners write their gate factors sigmoid(G) as
+  // fp32 rows [m][n] to LDS (16-byte chunk c of row r at chunk c ^ (r & 15), conflict free),
+  // then all 8 waves stream that half of the tile: 16 bytes of o per lane along the rows, all
+  // loads of a lane issued before the first multiply, and 16-byte stores of whole rows.
+  float* fs = (float*)g2_smem;  // [4 blocks][64 rows][128] fp32 = 128 KiB
+#pragma unroll 1
+  for (int half = 0; half < 2; ++half) {
+    if ((wave >> 2) == half) {
+      float* fw = fs + (wave & 3) * 64 * 128;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          f32x4_t f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) f[r] = sigmoidf_fast(acc[i][j][r]);
+          *(f32x4_t*)(fw + (16 * j + l16) * 128 + 4 * ((4 * i + g) ^ l16)) = f;
+        }
+    }
+    __syncthreads();
+    // the half covers blocks (wave & 3) = 0..3 of this half: wm = 2*half + (blk >> 1),
+    // wn = blk & 1; 4 blocks x 64 rows x 16 lanes-of-8-channels = 4096 chunks, 8 per lane
+    uint4 ov[8];
+    size_t off[8];
+    bool ok[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = tid + 512 * u;           // chunk index in the half
+      const int blk = c >> 10, rr = (c >> 4) & 63, cl = (c & 15) * 8;
+      const int m = m0 + 64 * (2 * half + (blk >> 1)) + rr;
+      const int n = n0 + 128 * (blk & 1) + cl;
+      ok[u] = m < M && n < N;
+      off[u] = (size_t)min(m, M - 1) * N + min(n, N - 8);
+      ov[u] = *(const uint4*)(o + off[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = tid + 512 * u;
+      const int blk = c >> 10, rr = (c >> 4) & 63, c0 = (c & 15) * 2;
+      const float* fw = fs + blk * 64 * 128 + rr * 128;
+      const f32x4_t f0 = *(const f32x4_t*)(fw + 4 * (c0 ^ (rr & 15)));
+      const f32x4_t f1 = *(const f32x4_t*)(fw + 4 * ((c0 + 1) ^ (rr & 15)));
+      uint4 r;
+      r.x = pack_bf16x2(__uint_as_float(ov[u].x << 16) * f0[0],
+                        __uint_as_float(ov[u].x & 0xFFFF0000u) * f0[1]);
+      r.y = pack_bf16x2(__uint_as_float(ov[u].y << 16) * f0[2],
+                        __uint_as_float(ov[u].y & 0xFFFF0000u) * f0[3]);
+      r.z = pack_bf16x2(__uint_as_float(ov[u].z << 16) * f1[0],
+                        __uint_as_float(ov[u].z & 0xFFFF0000u) * f1[1]);
+      r.w = pack_bf16x2(__uint_as_float(ov[u].w << 16) * f1[2],
+                        __uint_as_float(ov[u].w & 0xFFFF0000u) * f1[3]);
+      if (ok[u]) *(uint4*)(out + off[u]) = r;
+    }
+    __syncthreads();
+  }
+}
+
 // fp32: 64x64 output tile, each of 256 threads computes a 4x4 block.
 __global__ __launch_bounds__(256) void gate_f32_kernel(const float* __restrict__ ql,
                                                        const float* __restrict__ w,
@@ -177,7 +351,20 @@ __global__ __launch_bounds__(256) void gate_f32_kernel(const float* __restrict__
 hipError_t launch_gate(const void* q_lat, const void* w, const void* o, void* out, int M,
                        int d_lat, int N, int dt, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  if (dt == DT_BF16) {
+  if (dt == DT_BF16 && M >= G2_BM && N >= G2_BN) {
+    static bool attr_set = false;  // idempotent: racing threads set the same value
+    if (!attr_set) {
+      const hipError_t e = hipFuncSetAttribute((const void*)gate_bf16_big_kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)G2_SMEM);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    const int grid = ((N + G2_BN - 1) / G2_BN) * ((M + G2_BM - 1) / G2_BM);
+    hipLaunchKernelGGL(gate_bf16_big_kernel, dim3(grid), dim3(512), G2_SMEM, stream,
+                       (const uint16_t*)q_lat, (const uint16_t*)w, (const uint16_t*)o,
+                       (uint16_t*)out, M, d_lat, N);
+  } else if (dt == DT_BF16) {
     const int grid = ((N + GT_N - 1) / GT_N) * ((M + GT_M - 1) / GT_M);
     hipLaunchKernelGGL(gate_bf16_kernel, dim3(grid), dim3(256), 0, stream,
                        (const uint16_t*)q_lat, (const uint16_t*)w, (const uint16_t*)o,
