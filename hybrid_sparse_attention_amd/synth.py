@@ -165,3 +165,31 @@ def random_topk(config: int, B: int, Tq: int, S: int, k: int, pos0):
             else:
                 idx[b, i] = np.sort(g.choice(n, size=k, replace=False)).astype(np.int32)
     return idx
+
+
+def stratified_topk(config: int, B: int, Tq: int, S: int, k: int, pos0):
+    """A seeded index list per query row shaped like an indexer's output, cheap at any size:
+    row t keeps every causal position when t + 1 <= k; otherwise [0, t] is cut into k strata
+    at the integer boundaries floor(j (t+1) / k) and one position is drawn uniformly from each,
+    which gives k distinct positions in ascending order.  Unused slots hold -1."""
+    g = np.random.Generator(np.random.PCG64(seed_of(config, "idx")))
+    idx = np.full((B, Tq, k), -1, dtype=np.int32)
+    j = np.arange(k + 1, dtype=np.int64)
+    for b in range(B):
+        for i0 in range(0, Tq, 1024):
+            i1 = min(Tq, i0 + 1024)
+            t = int(pos0[b]) + np.arange(i0, i1, dtype=np.int64)
+            n = np.minimum(t + 1, S)
+            short = n <= k
+            bounds = (j[None, :] * n[:, None]) // k              # [rows, k+1]
+            width = bounds[:, 1:] - bounds[:, :-1]               # >= 1 when n >= k
+            u = g.random((i1 - i0, k))
+            pick = bounds[:, :-1] + np.floor(u * width).astype(np.int64)
+            blk = pick.astype(np.int32)
+            if short.any():
+                rows = np.nonzero(short)[0]
+                ar = np.arange(k, dtype=np.int64)[None, :]
+                full = np.where(ar < n[rows, None], ar, -1).astype(np.int32)
+                blk[rows] = full
+            idx[b, i0:i1] = blk
+    return idx
