@@ -4,9 +4,11 @@
 
 A step is one pass of the hot path over one batch of synthetic input of the HCA prefill at
 model shape (seq 32768, 64 query heads sharing one KV head, head dim 512, bf16, 256 mean-pooled
-compressed entries + 128-token window, gate from the 1024-wide query latent): hca_compress
-then hca_attn_fwd with the gate fused.  `value` is its algorithmic TFLOP/s (attention over the
-visible pairs + the gate GEMM).  The decode and MLA-DSA workloads are timed too and reported
+compressed entries + 128-token window, gate from the 1024-wide query latent): hca_compress,
+hca_attn_fwd, then latent_gate in place on the attention output (the same two kernels that
+hca_attn_fwd enqueues when given the gate operands).  `value` is its algorithmic TFLOP/s
+(attention over the visible pairs + the gate GEMM).  `roofline` describes the kernel that takes
+the largest share of the step, bounded by MFMA or HBM according to its algorithmic work.  The decode and MLA-DSA workloads are timed too and reported
 under "secondary" in the same JSON line.  Inputs are seeded synthetic data already resident
 in HBM when timing starts.  The CPU baseline times the fp64 oracle on a bounded sample of
 query rows of the same workload.
@@ -76,6 +78,9 @@ def flush_cache(torch, buf):
 
 # --------------------------------------------------------------------------- workloads
 def run_c1(torch, lgsa, synth, to_dev, steps, warmup):
+    """Step = hca_compress -> hca_attn_fwd -> latent_gate (in place on the attention output).
+    hca_attn_fwd called with q_lat/w_gate enqueues exactly these two kernels back to back;
+    calling the gate through its own entry point lets HIP events bracket each kernel."""
     T, H, d = 32768, 64, 512
     log("[bench] C1: generating inputs (seq %d, %d heads, d %d)" % (T, H, d))
     x = synth.hca_prefill(1, T=T, H=H, d=d, bf16=True, qkv_scale=1.0 / math.sqrt(512))
@@ -85,13 +90,18 @@ def run_c1(torch, lgsa, synth, to_dev, steps, warmup):
     out = torch.empty_like(dev["q"])
     stream = torch.cuda.current_stream()
     tm = Timer(torch, stream)
+    o2 = out.view(T, H * d)
+    ql2 = dev["q_lat"].view(T, -1)
 
     def step(evs=None):
         lgsa.hca_compress(dev["k"], dev["v"], kc, vc)
         if evs is not None:
             evs.append(tm.event())
         lgsa.hca_attn_fwd(dev["q"], dev["pos0"], dev["k"], dev["v"], kc, vc, max_pos=T - 1,
-                          q_lat=dev["q_lat"], w_gate=dev["w_gate"], out=out)
+                          out=out)
+        if evs is not None:
+            evs.append(tm.event())
+        lgsa.latent_gate(ql2, dev["w_gate"], o2, out=o2)
 
     for _ in range(warmup):
         step()
@@ -105,14 +115,53 @@ def run_c1(torch, lgsa, synth, to_dev, steps, warmup):
     t1 = tm.event()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    # per-kernel: compress = [end of previous step, mark], attention = [mark, end of step]
-    starts = [t0] + marks[1::2][:-1]
-    comp_ms = [a.elapsed_time(b) for a, b in zip(starts, marks[0::2])]
-    attn_ms = [a.elapsed_time(b) for a, b in zip(marks[0::2], marks[1::2])]
+    # marks per step: [after compress, after attention, after gate]
+    ends = [t0] + marks[2::3][:-1]
+    comp_ms = [a.elapsed_time(b) for a, b in zip(ends, marks[0::3])]
+    attn_ms = [a.elapsed_time(b) for a, b in zip(marks[0::3], marks[1::3])]
+    gate_ms = [a.elapsed_time(b) for a, b in zip(marks[1::3], marks[2::3])]
     att, gate = hca_prefill_flops(T, H, d)
-    return dict(ms_per_step=total_ms / steps, flops=att + gate, att_flops=att, gate_flops=gate,
-                attn_ms=float(np.mean(attn_ms)), compress_ms=float(np.mean(comp_ms)),
-                inputs=x)
+    gib = 1 << 30
+    # algorithmic bytes: each input read once, each output written once
+    att_bytes = (2 * gib + 2 * gib + 2 * (T * d * 2) + 2 * (T // 128) * d * 2)
+    gate_bytes = (T * 1024 * 2 + 1024 * H * d * 2 + 2 * gib + 2 * gib)
+    comp_bytes = 2 * T * d * 2 + 2 * (T // 128) * d * 2
+    kernels = [
+        dict(name="hca_prefill_kernel", call="hca_attn_fwd", ms=float(np.mean(attn_ms)),
+             flops=att, bytes=att_bytes, src="hca_bf16.hip"),
+        dict(name="gate_bf16_big_kernel", call="latent_gate", ms=float(np.mean(gate_ms)),
+             flops=gate, bytes=gate_bytes, src="gate.hip"),
+        dict(name="compress_kernel", call="hca_compress", ms=float(np.mean(comp_ms)),
+             flops=0.0, bytes=comp_bytes, src="compress.hip"),
+    ]
+    return dict(ms_per_step=total_ms / steps, flops=att + gate, kernels=kernels, inputs=x)
+
+
+def kernel_roofline(k, traffic):
+    """Roofline record of one kernel: bound by whichever of MFMA time and HBM time at peak is
+    larger for its algorithmic work."""
+    t_f = k["flops"] / (PEAK_BF16_TFLOPS * 1e12)
+    t_b = k["bytes"] / (PEAK_HBM_GBPS * 1e9)
+    sec = k["ms"] * 1e-3
+    if t_f >= t_b:
+        ach, peak, unit, bound = k["flops"] / sec / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        ach, peak, unit, bound = k["bytes"] / sec / 1e9, PEAK_HBM_GBPS, "GB/s", "hbm"
+    return dict(bound=bound, achieved=round(ach, 2), peak=peak, unit=unit,
+                frac=round(ach / peak, 4), traffic=traffic, kernel=k["name"],
+                entry_point=k["call"], launch_ms=round(k["ms"], 4),
+                flops_per_launch=k["flops"], bytes_per_launch=k["bytes"])
+
+
+def run_copy(torch, steps):
+    """A plain 1 GiB device-to-device copy, the calibration kernel of the traffic counters."""
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(copy_bytes_read=4 * n, copy_bytes_written=4 * n, launches=steps)))
 
 
 def run_c2(torch, lgsa, synth, to_dev, iters):
@@ -257,14 +306,25 @@ def cpu_baseline(x, budget_s=15.0):
                        % (len(rows), T, H, secs))
 
 
-def traffic_record(kernel_src):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
-    on the current source of the kernel."""
+def kernel_sources_sha(src):
+    """Hash of a kernel's source file and the shared device header it includes."""
+    h = hashlib.sha256()
+    for f in (src, "common.h"):
+        with open(os.path.join(ROOT, "hybrid_sparse_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(k):
+    """HBM bytes per launch of kernel k from the committed rocprofv3 counter summary (FETCH_SIZE
+    + WRITE_SIZE, scaled by the copy-kernel calibration), or None when that summary was taken on
+    another version of the kernel's source."""
     path = os.path.join(ROOT, "profiles", "hca_prefill_c1_traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
-    if rec.get("source_sha") != src_sha(kernel_src):
+    with open(path) as f:
+        rec = json.load(f).get("kernels", {}).get(k["name"])
+    if not rec or rec.get("source_sha") != kernel_sources_sha(k["src"]):
         return None
     return float(rec["bytes_per_launch"])
 
@@ -278,6 +338,8 @@ def main():
     ap.add_argument("--configs", default="1,2,3,4",
                     help="workloads to run; 1 is the headline, 2-4 are reported as secondary")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy", action="store_true",
+                    help="only run a 1 GiB device copy (calibrates the HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -285,6 +347,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy:
+        run_copy(torch, args.steps)
+        return
 
     import hybrid_sparse_attention_amd as lgsa
     from hybrid_sparse_attention_amd import synth
@@ -300,24 +366,20 @@ def main():
     cfgs = [int(c) for c in args.configs.split(",") if c]
     r1 = run_c1(torch, lgsa, synth, to_dev, args.steps, args.warmup)
     value = r1["flops"] / (r1["ms_per_step"] * 1e-3) / 1e12
-    att_tf = r1["flops"] / (r1["attn_ms"] * 1e-3) / 1e12
-    kernel_src = os.path.join(ROOT, "hybrid_sparse_attention_amd", "csrc", "hca_bf16.hip")
-    roofline = dict(bound="mfma", kernel="hca_prefill_kernel (attention + fused gate)",
-                    achieved=round(att_tf, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(att_tf / PEAK_BF16_TFLOPS, 4),
-                    traffic=traffic_record(kernel_src),
-                    launch_ms=round(r1["attn_ms"], 4),
-                    flops_per_launch=r1["flops"])
-    secondary = dict(c1_compress_ms=round(r1["compress_ms"], 4))
+    kern = [kernel_roofline(k, traffic_record(k)) for k in r1["kernels"]]
+    dom = max(range(len(kern)), key=lambda i: r1["kernels"][i]["ms"])
+    roofline = kern[dom]
+    secondary = dict(c1_kernels=[kern[i] for i in range(len(kern)) if i != dom])
     cpu = None
     if not args.no_cpu:
         log("[bench] CPU baseline: fp64 oracle on a sample of C1 rows")
         cpu = cpu_baseline(r1["inputs"])
     del r1["inputs"]
     if 2 in cfgs:
-        r2 = run_c2(torch, lgsa, synth, to_dev, 50)
+        r2 = run_c2(torch, lgsa, synth, to_dev, 200)
         gbps = r2["bytes"] / (r2["ms"] * 1e-3) / 1e9
-        secondary["c2_hca_decode"] = dict(ms=round(r2["ms"], 4), GBps=round(gbps, 1),
+        secondary["c2_hca_decode"] = dict(ms=round(r2["ms"], 4), ms_min=round(r2["ms_min"], 4),
+                                          GBps=round(gbps, 1),
                                           hbm_frac=round(gbps / PEAK_HBM_GBPS, 4),
                                           bytes=r2["bytes"])
     if 3 in cfgs:
@@ -330,7 +392,7 @@ def main():
             indexer_ms=round(r3["index_ms"], 3), indexer_TFLOPs=round(ix_tf, 1),
             indexer_fp32_frac=round(ix_tf / PEAK_FP32_TFLOPS, 4))
     if 4 in cfgs:
-        r4 = run_c4(torch, lgsa, synth, to_dev, 10)
+        r4 = run_c4(torch, lgsa, synth, to_dev, 30)
         gbps = r4["bytes"] / (r4["ms"] * 1e-3) / 1e9
         igbps = r4["index_bytes"] / (r4["index_ms"] * 1e-3) / 1e9
         secondary["c4_mixed_decode"] = dict(ms=round(r4["ms"], 4), GBps=round(gbps, 1),
@@ -343,8 +405,8 @@ def main():
         scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
         config=dict(workload="HCA prefill at model shape: seq 32768, 64 query heads + 1 shared "
                              "KV head, head dim 512, bf16, 256 mean-pooled entries + 128-token "
-                             "window, fused low-rank gate (W_gate 1024x32768); step = "
-                             "hca_compress + hca_attn_fwd",
+                             "window, low-rank sigmoid gate (W_gate 1024x32768); step = "
+                             "hca_compress + hca_attn_fwd + latent_gate",
                     seq_len=32768, heads=64, head_dim=512, batch=1, parallelism="none"),
         roofline=roofline, cpu_baseline=cpu, secondary=secondary)
     print(json.dumps(line))
