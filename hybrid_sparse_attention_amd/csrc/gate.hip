@@ -2,12 +2,16 @@
 // attention): out[m, n] = o[m, n] * sigmoid(q_lat[m, :] . w[:, n]), the gate logits computed
 // from the 1024-wide query latent and never written to memory.
 //
-// bfloat16 path: an MFMA GEMM computing the transposed product G^T = W^T q_lat^T so that
-// every lane ends with four consecutive output channels of one row, which it multiplies into
-// o and stores as 8 bytes.  The W tile is transposed while it is staged in LDS (the MFMA
-// wants the contraction index contiguous per lane, W has it strided).
-// Workgroup tile: 128 channels x 128 rows, four waves of 64 x 64, K staged 64 at a time in
-// double-buffered LDS.
+// bfloat16 paths: MFMA GEMMs computing the transposed product G^T = W^T q_lat^T, so that a
+// lane's accumulator holds four consecutive output channels of one row.
+//   - gate_bf16_big_kernel (M and N >= 256, the prefill shapes): 256 x 256 tiles fed by LDS
+//     DMA, W read through the transposing LDS read, tiles ordered so that the workgroups
+//     resident on one XCD share their q_lat and W tiles in that XCD's L2; the epilogue stages
+//     the fp32 gate factors in LDS and streams o and out with 16-byte accesses.
+//   - gate_bf16_kernel (small M or N, e.g. decode): 128 x 128 tiles, the W tile transposed
+//     while it is staged in LDS through registers, four waves of 64 x 64, K staged 64 at a
+//     time in double-buffered LDS; the lane multiplies its four channels into o and stores
+//     8 bytes.
 //
 // float32 path: a plain tiled FMA GEMM (used for the small fp32 configuration).
 #include "common.h"

@@ -45,7 +45,7 @@ extern "C" {
 typedef int lgsa_status;
 #define LGSA_OK 0
 #define LGSA_EINVAL (-1)       /* a pointer, size or relation between sizes is invalid */
-#define LGSA_EUNSUPPORTED (-2) /* valid, but outside the shapes/dtypes this build supports */
+#define LGSA_EUNSUPPORTED (-2) /* valid, but outside the shapes/dtypes the library implements */
 #define LGSA_EWORKSPACE (-3)   /* workspace missing or smaller than the *_workspace query */
 #define LGSA_EHIP (-4)         /* the HIP runtime refused a launch */
 
@@ -76,7 +76,8 @@ lgsa_status hca_compress(const void* k, const void* v, void* kc, void* vc, int B
  *   q_lat  [M, d_lat]   query latent rows (dt)
  *   w_gate [d_lat, N]   gate projection (dt)
  *   o      [M, N]       attention output (dt);  out [M, N] (dt).  out may equal o.
- * Supported: LGSA_BF16 with d_lat % 32 == 0 and N % 16 == 0; LGSA_F32 with any sizes.
+ * Supported: LGSA_BF16 with d_lat % 64 == 0 and N % 16 == 0 (q_lat, w_gate 16-byte aligned,
+ * o, out 8-byte aligned); LGSA_F32 with any sizes.  M == 0 enqueues nothing.
  * ------------------------------------------------------------------------------------- */
 lgsa_status latent_gate(const void* q_lat, const void* w_gate, const void* o, void* out, int M,
                         int d_lat, int N, int dt, void* stream);
@@ -90,8 +91,9 @@ lgsa_status latent_gate(const void* q_lat, const void* w_gate, const void* o, vo
  *     k_win / v_win (prefill: win_len = T and the raw k, v; decode: a ring of >= window rows).
  * Both sets are used as they stand, also where they cover the same tokens.
  *   O[b,i,h,:] = sum_j softmax_j(scale * <q[b,i,h,:], key_j>) * value_j
- * and, when q_lat is non-NULL, out = O * sigmoid(q_lat[b,i,:] . w_gate[:, h*d + c]) fused
- * into the epilogue; otherwise out = O.
+ * and, when q_lat is non-NULL, out = O * sigmoid(q_lat[b,i,:] . w_gate[:, h*d + c]) (the
+ * gate GEMM runs as a second kernel on the same stream and rescales out in place, exactly
+ * what latent_gate(q_lat, w_gate, out, out, B*Tq, d_lat, H*d) does); otherwise out = O.
  * --------------------------------------------------------------------------------------- */
 typedef struct {
   int dt;              /* LGSA_F32 or LGSA_BF16: q, k_win, v_win, kc, vc, q_lat, w_gate, out */
@@ -106,7 +108,7 @@ typedef struct {
   int window;          /* raw window length (128 for ERNIE 5.5 Flash), >= 1 */
   const void* kc;      /* [B, n_cap, d] compressed keys (may be NULL when n_cap == 0) */
   const void* vc;      /* [B, n_cap, d] compressed values */
-  int n_cap;           /* entries held in kc / vc; must be >= min(needed, ...) see below */
+  int n_cap;           /* entries held in kc / vc (>= 0); entries e >= n_cap are absent */
   int block;           /* tokens per compressed entry (128 for ERNIE 5.5 Flash), >= 1 */
   float scale;         /* logit scale, normally 1/sqrt(d) */
   const void* q_lat;   /* [B, Tq, d_lat] or NULL (ungated) */
@@ -119,7 +121,8 @@ typedef struct {
 /* Validation: every size >= 1 (n_cap >= 0); window <= win_len unless max_pos < win_len (then
  * no window row wraps around the ring); max_pos >= Tq - 1; kc / vc non-NULL when n_cap > 0.
  * Entries e >= n_cap are absent: a query sees min(n_cap, (t + 1) / block) entries.
- * Supported: LGSA_BF16 with d == 512 and d_lat % 32 == 0; LGSA_F32 with d <= 512, d % 4 == 0.
+ * Supported: LGSA_BF16 with d == 512 and d_lat % 64 == 0; LGSA_F32 with d <= 512, d % 4 == 0;
+ * every tensor 16-byte aligned.
  * Positions beyond max_pos or below 0 never cause an out-of-bounds access: a row whose
  * position is negative has no visible key and produces zeros. */
 lgsa_status hca_attn_fwd(const lgsa_hca_args* a, void* stream);
@@ -147,7 +150,7 @@ typedef struct {
   void* workspace;       /* scratch, dsa_index_topk_workspace() bytes */
   size_t workspace_bytes;
 } lgsa_index_args;
-/* Supported: di == 64, 1 <= Hi <= 8, 1 <= k <= 4096, S >= 1.  A position t >= S (caller
+/* Supported: di == 64, 1 <= Hi <= 4, 1 <= k <= 4096, S >= 1; q_idx and k_idx 16-byte aligned.  A position t >= S (caller
  * broke the max_pos promise) is clamped to S - 1 for reading; it never reads out of bounds. */
 lgsa_status dsa_index_topk(const lgsa_index_args* a, void* stream);
 lgsa_status dsa_index_topk_workspace(const lgsa_index_args* a, size_t* bytes);
@@ -180,8 +183,9 @@ typedef struct {
   void* workspace;       /* scratch, sparse_attn_fwd_workspace() bytes */
   size_t workspace_bytes;
 } lgsa_sparse_args;
-/* Supported: LGSA_BF16, d_qk == d_v == 256, H % 16 == 0, row strides % 8 == 0,
- * d_lat % 32 == 0. */
+/* Supported: LGSA_BF16, d_qk == d_v == 256, H % 64 == 0, row strides % 8 == 0,
+ * d_lat % 64 == 0; every tensor 16-byte aligned.  The gate, when requested, runs as a second
+ * kernel on the same stream that rescales out in place. */
 lgsa_status sparse_attn_fwd(const lgsa_sparse_args* a, void* stream);
 lgsa_status sparse_attn_fwd_workspace(const lgsa_sparse_args* a, size_t* bytes);
 

@@ -206,7 +206,7 @@ int orc_latent_gate(const void* q_lat, int dt_l, const void* w, int dt_w, const 
   return 0;
 }
 
-// Lightweight indexer of [blog 2.1] in the form fixed for this build:
+// Lightweight indexer of [blog 2.1] in the form taken here:
 //   score(t, s) = sum_{h < Hi} w[t, h] * max(0, <q_I[t, h], k_I[s]>),
 // evaluated in float64 from float32 inputs for s in [s0, s1) of query row (b, i).
 // q_idx [B,Tq,Hi,di]; w_idx [B,Tq,Hi]; k_idx [B,S,di]; out has s1 - s0 entries.

@@ -104,7 +104,7 @@ def test_hca_prefill_chunked_positions(torch, orc):
 
 
 def test_hca_prefill_f32_config0(torch, orc):
-    """configs[0]: T=1024, 4 heads, fp32, 8 compressed entries, gated."""
+    """The tiny fp32 workload: T=1024, 4 heads, 8 compressed entries, gated."""
     x = synth.hca_prefill(0, T=1024, H=4, bf16=False, qkv_scale=1.0)
     kc, vc = lgsa.hca_compress(to_dev(x["k"]), to_dev(x["v"]))
     out = _hca_gpu(x, kc, vc, 1023, True)
