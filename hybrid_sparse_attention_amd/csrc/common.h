@@ -114,6 +114,18 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
 
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS reads and writes
+// (lgkmcnt 0), not for its vector-memory loads, so LDS DMA transfers in flight stay in flight
+// (__syncthreads waits for those too).  Use it only where no wave reads LDS that a DMA still in
+// flight may write.  The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt and expcnt at their maxima, lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Hides a value from the optimiser so that addresses derived from it are recomputed where
 // they are used instead of being hoisted (and kept live) across a loop.
 __device__ __forceinline__ int opaque(int x) {

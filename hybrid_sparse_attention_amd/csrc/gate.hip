@@ -140,12 +140,16 @@ constexpr int G2_QROW = G2_BK * 2;              // bytes per staged q_lat row
 constexpr int G2_WSTAGE = G2_BK * G2_WROW;      // 32 KiB
 constexpr int G2_QSTAGE = G2_BM * G2_QROW;      // 32 KiB
 constexpr int G2_STAGE = G2_WSTAGE + G2_QSTAGE;
-constexpr size_t G2_SMEM = 2 * G2_STAGE;
 
 __device__ __forceinline__ int g2_wswz(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
 __device__ __forceinline__ int g2_qswz(int r) { return (r >> 1) & 7; }
 
-extern __shared__ __attribute__((aligned(1024))) char g2_smem[];
+// The two stages are separate LDS objects, each named directly wherever it is read or filled
+// (the K loop is unrolled by two).  The compiler then sees that the fragment reads of one stage
+// cannot touch the LDS DMA writes into the other and does not wait for that DMA before reading;
+// with one shared array it would, and the prefetch would not overlap the products at all.
+__shared__ __attribute__((aligned(1024))) char g2_stage0[G2_STAGE];
+__shared__ __attribute__((aligned(1024))) char g2_stage1[G2_STAGE];
 
 __global__ __launch_bounds__(512, 1) void gate_bf16_big_kernel(const uint16_t* __restrict__ ql,
                                                                const uint16_t* __restrict__ w,
@@ -182,8 +186,7 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_big_kernel(const uint16_t* _
 
   // DMA of one K step into stage s: 32 W instructions (2 k-rows each) and 32 q_lat
   // instructions (8 rows each); 8 per wave.
-  auto dma = [&](int k0, int s) {
-    char* sw = g2_smem + s * G2_STAGE;
+  auto dma = [&](int k0, char* sw) {
     char* sq = sw + G2_WSTAGE;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -215,14 +218,11 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_big_kernel(const uint16_t* _
   const int qc0 = 16 * ((g) ^ qf), qc1 = 16 * ((4 + g) ^ qf);
 
   const int nk = d_lat / G2_BK;
-  dma(0, 0);
-  wait_all();
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int s = kt & 1;
-    if (kt + 1 < nk) dma((kt + 1) * G2_BK, s ^ 1);
-    const char* sw = g2_smem + s * G2_STAGE;
-    const char* sq = sw + G2_WSTAGE;
+  // one K step on stage `cur` while the next step's tiles stream into `nxt`
+  auto step = [&](int kt, const char* cur, char* nxt) {
+    if (kt + 1 < nk) dma((kt + 1) * G2_BK, nxt);
+    const char* sw = cur;
+    const char* sq = cur + G2_WSTAGE;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       Frag8 bq[4];
@@ -242,17 +242,46 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_big_kernel(const uint16_t* _
     }
     wait_all();
     __syncthreads();
+  };
+  dma(0, g2_stage0);
+  wait_all();
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, g2_stage0, g2_stage1);
+    if (kt + 1 < nk) step(kt + 1, g2_stage1, g2_stage0);
   }
   // epilogue: lane holds G[m = m0 + 64wm + 16j + l16][n = n0 + 128wn + 16i + 4g .. +3].
   // In two halves (waves 0-3, then 4-7), the owners write their gate factors sigmoid(G) as
   // fp32 rows [m][n] to LDS (16-byte chunk c of row r at chunk c ^ (r & 15), conflict free),
-  // then all 8 waves stream that half of the tile: 16 bytes of o per lane along the rows, all
-  // loads of a lane issued before the first multiply, and 16-byte stores of whole rows.
-  float* fs = (float*)g2_smem;  // [4 blocks][64 rows][128] fp32 = 128 KiB
-#pragma unroll 1
+  // then all 8 waves stream that half of the tile: 16 bytes of o per lane along the rows and
+  // 16-byte stores of whole rows.
+  // [4 blocks][64 rows][128] fp32 = 128 KiB: blocks 0, 1 in stage 0, blocks 2, 3 in stage 1
+  auto fblk = [&](int blk) {
+    return (float*)(blk < 2 ? g2_stage0 : g2_stage1) + (blk & 1) * 64 * 128;
+  };
+  // chunk u of half hl for this thread: 4 blocks x 64 rows x 16 chunks of 8 channels per half
+  auto chunk_mn = [&](int hl, int u, int& blk, int& rr, int& m, int& n) {
+    const int c = tid + 512 * u;
+    blk = c >> 10;
+    rr = (c >> 4) & 63;
+    m = m0 + 64 * (2 * hl + (blk >> 1)) + rr;
+    n = n0 + 128 * (blk & 1) + (c & 15) * 8;
+  };
+  // the o loads of both halves are issued before any gate factor is staged, so the second
+  // half's loads are in flight while the first half is processed
+  uint4 ov[2][8];
+#pragma unroll
+  for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      int blk, rr, m, n;
+      chunk_mn(hl, u, blk, rr, m, n);
+      ov[hl][u] = *(const uint4*)(o + (size_t)min(m, M - 1) * N + min(n, N - 8));
+    }
+#pragma unroll
   for (int half = 0; half < 2; ++half) {
     if ((wave >> 2) == half) {
-      float* fw = fs + (wave & 3) * 64 * 128;
+      float* fw = fblk(wave & 3);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -263,41 +292,28 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_big_kernel(const uint16_t* _
           *(f32x4_t*)(fw + (16 * j + l16) * 128 + 4 * ((4 * i + g) ^ l16)) = f;
         }
     }
-    __syncthreads();
-    // the half covers blocks (wave & 3) = 0..3 of this half: wm = 2*half + (blk >> 1),
-    // wn = blk & 1; 4 blocks x 64 rows x 16 lanes-of-8-channels = 4096 chunks, 8 per lane
-    uint4 ov[8];
-    size_t off[8];
-    bool ok[8];
+    lds_barrier();
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int c = tid + 512 * u;           // chunk index in the half
-      const int blk = c >> 10, rr = (c >> 4) & 63, cl = (c & 15) * 8;
-      const int m = m0 + 64 * (2 * half + (blk >> 1)) + rr;
-      const int n = n0 + 128 * (blk & 1) + cl;
-      ok[u] = m < M && n < N;
-      off[u] = (size_t)min(m, M - 1) * N + min(n, N - 8);
-      ov[u] = *(const uint4*)(o + off[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = tid + 512 * u;
-      const int blk = c >> 10, rr = (c >> 4) & 63, c0 = (c & 15) * 2;
-      const float* fw = fs + blk * 64 * 128 + rr * 128;
+      int blk, rr, m, n;
+      chunk_mn(half, u, blk, rr, m, n);
+      const int c0 = (tid & 15) * 2;
+      const float* fw = fblk(blk) + rr * 128;
       const f32x4_t f0 = *(const f32x4_t*)(fw + 4 * (c0 ^ (rr & 15)));
       const f32x4_t f1 = *(const f32x4_t*)(fw + 4 * ((c0 + 1) ^ (rr & 15)));
+      const uint4 x = ov[half][u];
       uint4 r;
-      r.x = pack_bf16x2(__uint_as_float(ov[u].x << 16) * f0[0],
-                        __uint_as_float(ov[u].x & 0xFFFF0000u) * f0[1]);
-      r.y = pack_bf16x2(__uint_as_float(ov[u].y << 16) * f0[2],
-                        __uint_as_float(ov[u].y & 0xFFFF0000u) * f0[3]);
-      r.z = pack_bf16x2(__uint_as_float(ov[u].z << 16) * f1[0],
-                        __uint_as_float(ov[u].z & 0xFFFF0000u) * f1[1]);
-      r.w = pack_bf16x2(__uint_as_float(ov[u].w << 16) * f1[2],
-                        __uint_as_float(ov[u].w & 0xFFFF0000u) * f1[3]);
-      if (ok[u]) *(uint4*)(out + off[u]) = r;
+      r.x = pack_bf16x2(__uint_as_float(x.x << 16) * f0[0],
+                        __uint_as_float(x.x & 0xFFFF0000u) * f0[1]);
+      r.y = pack_bf16x2(__uint_as_float(x.y << 16) * f0[2],
+                        __uint_as_float(x.y & 0xFFFF0000u) * f0[3]);
+      r.z = pack_bf16x2(__uint_as_float(x.z << 16) * f1[0],
+                        __uint_as_float(x.z & 0xFFFF0000u) * f1[1]);
+      r.w = pack_bf16x2(__uint_as_float(x.w << 16) * f1[2],
+                        __uint_as_float(x.w & 0xFFFF0000u) * f1[3]);
+      if (m < M && n < N) *(uint4*)(out + (size_t)m * N + n) = r;
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -356,16 +372,8 @@ hipError_t launch_gate(const void* q_lat, const void* w, const void* o, void* ou
                        int d_lat, int N, int dt, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   if (dt == DT_BF16 && M >= G2_BM && N >= G2_BN) {
-    static bool attr_set = false;  // idempotent: racing threads set the same value
-    if (!attr_set) {
-      const hipError_t e = hipFuncSetAttribute((const void*)gate_bf16_big_kernel,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)G2_SMEM);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
     const int grid = ((N + G2_BN - 1) / G2_BN) * ((M + G2_BM - 1) / G2_BM);
-    hipLaunchKernelGGL(gate_bf16_big_kernel, dim3(grid), dim3(512), G2_SMEM, stream,
+    hipLaunchKernelGGL(gate_bf16_big_kernel, dim3(grid), dim3(512), 0, stream,
                        (const uint16_t*)q_lat, (const uint16_t*)w, (const uint16_t*)o,
                        (uint16_t*)out, M, d_lat, N);
   } else if (dt == DT_BF16) {

@@ -78,31 +78,36 @@ struct Src {
   }
 };
 
-// The calling wave DMAs rows r0, r0 + step, ... of one tile (K or V).
+// The calling wave DMAs rows r0, r0 + step, ... of one tile (K or V).  The row address is
+// wave-uniform and the lane adds a 32-bit offset made opaque at the point of use, so no 64-bit
+// per-lane pointer is kept live across the key loop (the instruction takes the scalar base).
 __device__ __forceinline__ void dma_rows(const Src& src, const Tile& t, bool is_v, char* dst,
                                          int ld, int r0, int step, int lane) {
   const char* base = t.kind == 0 ? (is_v ? src.vc : src.kc) : (is_v ? src.vw : src.kw);
-  for (int j = r0; j < KT; j += step)
-    lds_dma16(base + src.row(t, j) * ROWB + 16 * lane, dst + j * ld);
+  for (int j = r0; j < KT; j += step) {
+    const char* rowp = base + src.row(t, j) * ROWB;
+    lds_dma16(rowp + (uint32_t)opaque(16 * lane), dst + j * ld);
+  }
 }
 
-// Per query row: position t, number of visible compressed entries, first visible raw position
-// (a row with t < 0 sees nothing).
-struct RowVis {
-  int t, ncv, wlo;
+// Positions of a wave's 32 query rows, all fields wave-uniform: row r (= 16nb + l16) is at
+// position t0 + step * r when r < n_rows and has no position (sees nothing) otherwise.
+// Prefill rows are consecutive tokens (step 1); decode rows are heads of one token (step 0).
+// The lane's own row is formed where it is needed, so no per-lane row state stays live.
+struct RowPos {
+  int t0, n_rows, step, window, block;
 };
 
-__device__ __forceinline__ RowVis row_vis(int t, int window, int block) {
-  RowVis v;
-  v.t = t;
-  v.ncv = t >= 0 ? (t + 1) / block : 0;
-  v.wlo = t >= 0 ? t - window + 1 : t + 1;
-  return v;
+__device__ __forceinline__ int row_t(const RowPos& rp, int r) {
+  return r < rp.n_rows ? rp.t0 + rp.step * r : -1;
 }
 
-__device__ __forceinline__ bool visible(const Tile& t, int j, const RowVis& v) {
+// Key j of tile t is visible to a row at position tr: compressed entry e when its block is
+// complete (block * e + block - 1 <= tr), raw position s when tr - window + 1 <= s <= tr.
+__device__ __forceinline__ bool visible(const Tile& t, int j, int tr, const RowPos& rp) {
   const int s = t.start + j;
-  const bool in_set = t.kind == 0 ? (s < v.ncv) : ((s <= v.t) & (s >= v.wlo));
+  const bool in_set = t.kind == 0 ? (rp.block * s + rp.block - 1 <= tr)
+                                  : ((s <= tr) & (s + rp.window - 1 >= tr));
   return (j < t.count) & in_set;
 }
 
@@ -155,7 +160,7 @@ __device__ __forceinline__ void partial_scores(f32x4_t (&s)[2][2], const Frag8 (
 // Online softmax of the full scores (masked unless the tile is fully visible) and
 // O-half += V-half^T P^T.
 __device__ __forceinline__ void softmax_pv(HalfState& st, const f32x4_t (&s)[2][2],
-                                           const char* vs, const Tile& t, const RowVis (&rv)[2],
+                                           const char* vs, const Tile& t, const RowPos& rp,
                                            float scale_log2, int hf, int lane) {
   const int l16 = lane & 15, g = lane >> 4;
   float x[2][2][4];  // [nb][mb][r]
@@ -168,13 +173,15 @@ __device__ __forceinline__ void softmax_pv(HalfState& st, const f32x4_t (&s)[2][
         for (int r = 0; r < 4; ++r) x[nb][mb][r] = s[mb][nb][r] * scale_log2;
   } else {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < 2; ++nb) {
+      const int tr = row_t(rp, 16 * nb + opaque(l16));
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          x[nb][mb][r] = visible(t, 16 * mb + 4 * g + r, rv[nb]) ? s[mb][nb][r] * scale_log2
+          x[nb][mb][r] = visible(t, 16 * mb + 4 * g + r, tr, rp) ? s[mb][nb][r] * scale_log2
                                                                  : NEG_BIG;
+    }
   }
   float m_new[2];
 #pragma unroll
@@ -255,11 +262,16 @@ __device__ __forceinline__ void store4(uint16_t* dst, const f32x4_t& v) {
   *(uint2*)dst = r;
 }
 
-extern __shared__ __attribute__((aligned(1024))) char hca_smem[];
-
-// LDS layout of both kernels: K tile [0, KTILE), V stages [KTILE, KTILE + 2 VTILE), exchange.
-constexpr int V_OFF = KTILE;
-constexpr int XS_OFF = KTILE + 2 * VTILE;
+// LDS of both kernels: the K tile, two V stages and the score exchange, each its own LDS
+// object.  Every access below names its object directly (the key loop is unrolled by two so
+// that the V stage is known statically): the compiler can then prove that the reads of K, V_ti
+// and the exchange do not overlap the LDS DMA into V_{ti+1} or the refill of K, and does not
+// wait for those transfers before reading, which is what lets them overlap the products.
+constexpr int XS_BYTES = 8 * 4 * 64 * 16;  // 8 waves x 4 fragments x 64 lanes x 16 bytes
+__shared__ __attribute__((aligned(1024))) char hca_k[KTILE];
+__shared__ __attribute__((aligned(1024))) char hca_v0[VTILE];
+__shared__ __attribute__((aligned(1024))) char hca_v1[VTILE];
+__shared__ __attribute__((aligned(1024))) char hca_xs[XS_BYTES];
 
 // The key loop shared by prefill and decode.  Per tile ti (V stage ti & 1):
 //   barrier A: K_ti and V_ti are in LDS;  DMA V_{ti+1} into the other V stage;
@@ -267,53 +279,138 @@ constexpr int XS_OFF = KTILE + 2 * VTILE;
 //   DMA K_{ti+1};  add the partner's partial scores;  softmax;  PV from V_ti;  drain own DMA.
 template <class TileOf>
 __device__ __forceinline__ void key_loop(HalfState& st, const Frag8 (&qf)[2][8],
-                                         const RowVis (&rv)[2], const Src& src,
+                                         const RowPos& rp, const Src& src,
                                          const TileOf& tile_of, int n_tiles, int wave,
-                                         int n_waves, int hf, int lane, float scale_log2,
-                                         char* smem) {
-  char* ks = smem;
-  char* xs = smem + XS_OFF;
+                                         int n_waves, int hf, int lane, float scale_log2) {
   if (n_tiles > 0) {
     const Tile t0 = tile_of(0);
-    dma_rows(src, t0, false, ks, KLD, wave, n_waves, lane);
-    dma_rows(src, t0, true, smem + V_OFF, VLD, wave, n_waves, lane);
+    dma_rows(src, t0, false, hca_k, KLD, wave, n_waves, lane);
+    dma_rows(src, t0, true, hca_v0, VLD, wave, n_waves, lane);
   }
   wait_all();
   __syncthreads();
-  for (int ti = 0; ti < n_tiles; ++ti) {
-    const int buf = ti & 1;
+  auto body = [&](int ti, const char* vcur, char* vnxt) {
     const Tile t = tile_of(ti);
     const bool more = ti + 1 < n_tiles;
     Tile tn;
     if (more) {
       tn = tile_of(ti + 1);
-      dma_rows(src, tn, true, smem + V_OFF + (buf ^ 1) * VTILE, VLD, wave, n_waves, lane);
+      dma_rows(src, tn, true, vnxt, VLD, wave, n_waves, lane);
     }
     f32x4_t s[2][2];
-    partial_scores(s, qf, ks, hf, lane);
-    xs_write(xs, wave, lane, s);
-    __syncthreads();
-    if (more) dma_rows(src, tn, false, ks, KLD, wave, n_waves, lane);
-    xs_add(xs, wave ^ 1, lane, s);
-    softmax_pv(st, s, smem + V_OFF + buf * VTILE, t, rv, scale_log2, hf, lane);
+    partial_scores(s, qf, hca_k, hf, lane);
+    xs_write(hca_xs, wave, lane, s);
+    lds_barrier();  // the exchange is written and K is read; the V DMA stays in flight
+    if (more) dma_rows(src, tn, false, hca_k, KLD, wave, n_waves, lane);
+    xs_add(hca_xs, wave ^ 1, lane, s);
+    softmax_pv(st, s, vcur, t, rp, scale_log2, hf, lane);
     wait_all();
     __syncthreads();
+  };
+  for (int ti = 0; ti < n_tiles; ti += 2) {
+    body(ti, hca_v0, hca_v1);
+    if (ti + 1 < n_tiles) body(ti + 1, hca_v1, hca_v0);
   }
 }
 
 // ------------------------------------------------------------------------------- prefill
-// One workgroup of 8 waves per (32 query tokens, 4 heads): pair p = head 4*hg + p, and every
-// pair sees the same 32 rows.  Workgroups are ordered XCD-aware: consecutive ids go to
-// different XCDs (round robin), so the head groups of one token tile get ids that share an
-// XCD and its key tiles are served from that XCD's L2.
-constexpr size_t PF_SMEM = XS_OFF + 8 * 4 * 64 * 16;
+// One workgroup of 8 waves per (32 query tokens, 4 heads); wave w owns head 4 * hg + (w & 3)
+// for rows 16 * (w >> 2) .. +15 of the token tile over the whole head dimension: Q in 64
+// registers, O in 128, two waves per SIMD.  No partial scores are exchanged; K and V tiles are
+// both double buffered, so one barrier per tile remains.  Workgroups are ordered XCD-aware:
+// consecutive ids go to different XCDs (round robin), so the head groups of one token tile get
+// ids that share an XCD and its key tiles are served from that XCD's L2.
+struct RowState {
+  f32x4_t o[32];  // o[cb][r] = O[row l16][16cb + 4g + r]
+  float m;        // reference max (log2 domain): p = 2^(x - m) <= 2^LAZY
+  float l;        // running partial sum of this lane's keys
+};
+
+__shared__ __attribute__((aligned(1024))) char pf_k0[KTILE];
+__shared__ __attribute__((aligned(1024))) char pf_k1[KTILE];
+__shared__ __attribute__((aligned(1024))) char pf_v0[VTILE];
+__shared__ __attribute__((aligned(1024))) char pf_v1[VTILE];
+
+// S^T of one key tile over the whole head dimension for the wave's 16 rows: A = key row
+// 16mb + l16 with dims 32kk + 8g .. +7, B = query row l16 with the same dims.
+__device__ __forceinline__ void row_scores(f32x4_t (&s)[2], const Frag8 (&qf)[16],
+                                           const char* ks, int lane) {
+  const int l16 = lane & 15, g = lane >> 4;
+  s[0] = s[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const char* a0 = ks + l16 * KLD + 16 * g;
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) {
+    Frag8 ka[2];
+    ka[0].u = *(const uint4*)(a0 + 64 * kk);
+    ka[1].u = *(const uint4*)(a0 + 64 * kk + 16 * KLD);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) s[mb] = mfma_16x16x32(ka[mb], qf[kk], s[mb]);
+  }
+}
+
+// Online softmax of one tile's scores (masked unless the tile is fully visible), then
+// O += V^T P^T over all 32 column blocks of the head.
+__device__ __forceinline__ void row_softmax_pv(RowState& st, const f32x4_t (&s)[2],
+                                               const char* vs, const Tile& t,
+                                               const RowPos& rp, float scale_log2, int lane) {
+  const int l16 = lane & 15, g = lane >> 4;
+  float x[2][4];  // [mb][r]: key 16mb + 4g + r
+  if (t.full) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[mb][r] = s[mb][r] * scale_log2;
+  } else {
+    const int tr = row_t(rp, opaque(l16));
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        x[mb][r] = visible(t, 16 * mb + 4 * g + r, tr, rp) ? s[mb][r] * scale_log2 : NEG_BIG;
+  }
+  float mx = x[0][0];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[mb][r]);
+  const float m_new = fmaxf(st.m, wave_max16(mx));
+  // lazy rescale: keep the reference max unless some row's max grew by more than LAZY
+  if (__any(m_new > st.m + LAZY)) {
+    const float alpha = fast_exp2(st.m - m_new);
+    st.m = m_new;
+    st.l *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < 32; ++cb) st.o[cb] *= alpha;
+  }
+  float pr[2][4];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pr[mb][r] = fast_exp2(x[mb][r] - st.m);
+      st.l += pr[mb][r];
+    }
+  Frag8 pf;
+  pf.u = make_uint4(pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
+                    pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3]));
+  // V^T fragment of column block cb: transposed reads of rows 4g + a (slots 8g..8g+3) and
+  // 16 + 4g + a (slots 8g+4..8g+7), a = l16 / 4, columns 16cb + 4(l16 % 4) + 0..3.
+  const char* v0 = vs + (4 * g + (l16 >> 2)) * VLD + 8 * (l16 & 3);
+#pragma unroll
+  for (int cb = 0; cb < 32; ++cb) {
+    Frag8 va;
+    const uint2 lo = lds_read_tr16(v0 + 32 * cb);
+    const uint2 hi = lds_read_tr16(v0 + 32 * cb + 16 * VLD);
+    va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    st.o[cb] = mfma_16x16x32(va, pf, st.o[cb]);
+  }
+}
 
 __global__ __launch_bounds__(512, 1) void hca_prefill_kernel(HcaParams p) {
-  char* smem = hca_smem;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const int pair = wave >> 1, hf = wave & 1;
+  const int hw = wave & 3, rh = wave >> 2;  // head within the group, half of the token tile
   const int n_hg = (p.H + 3) / 4;
   const int n_qt = (p.Tq + 31) / 32;
   const int n_units = p.B * n_qt;
@@ -325,8 +422,8 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_kernel(HcaParams p) {
     hgi = blockIdx.x % n_hg;
   }
   const int b = unit / n_qt, qt = unit % n_qt;
-  const int h_raw = hgi * 4 + pair;
-  const bool h_ok = h_raw < p.H;  // a head count that is not a multiple of 4 leaves pairs idle
+  const int h_raw = hgi * 4 + hw;
+  const bool h_ok = h_raw < p.H;  // a head count that is not a multiple of 4 leaves waves idle
   const int h = h_ok ? h_raw : p.H - 1;
   const int pos = p.pos0[b];
   const int i_first = qt * 32;
@@ -338,6 +435,7 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_kernel(HcaParams p) {
   const int s_lo = max(0, t_first - p.window + 1);
   const int nw = max(0, t_last - s_lo + 1);
   const int tiles_c = (ne + KT - 1) / KT, tiles_w = (nw + KT - 1) / KT;
+  const int n_tiles = tiles_c + tiles_w;
   auto tile_of = [&](int ti) {
     Tile t;
     if (ti < tiles_c) {
@@ -361,32 +459,61 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_kernel(HcaParams p) {
   src.vw = (const char*)p.v_win + (size_t)b * p.win_len * ROWB;
   src.win_len = p.win_len;
 
-  RowVis rv[2];
-  Frag8 qf[2][8];
-  const uint16_t* qb = (const uint16_t*)p.q;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int i = i_first + 16 * nb + l16;
-    rv[nb] = row_vis(i < i_end ? pos + i : -1, p.window, p.block);
+  const int r_first = i_first + 16 * rh;  // token of the wave's row 0
+  RowPos rp;
+  rp.t0 = pos + r_first;
+  rp.n_rows = i_end - r_first;  // may be <= 0: the wave's rows all lie past the end
+  rp.step = 1;
+  rp.window = p.window;
+  rp.block = p.block;
+  Frag8 qf[16];
+  {
+    const int i = r_first + l16;
     const int ic = min(i, i_end - 1);  // rows past the end read the last row, never stored
-    const uint16_t* qr = qb + (((size_t)b * p.Tq + ic) * p.H + h) * D + hf * HALF;
+    const uint16_t* qr = (const uint16_t*)p.q + (((size_t)b * p.Tq + ic) * p.H + h) * D;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[nb][kk].u = *(const uint4*)(qr + 32 * kk + 8 * g);
+    for (int kk = 0; kk < 16; ++kk) qf[kk].u = *(const uint4*)(qr + 32 * kk + 8 * g);
   }
-  HalfState st;
-  init_state(st);
-  key_loop(st, qf, rv, src, tile_of, tiles_c + tiles_w, wave, 8, hf, lane, p.scale * LOG2E,
-           smem);
+  RowState st;
+#pragma unroll
+  for (int cb = 0; cb < 32; ++cb) st.o[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = NEG_BIG;
+  st.l = 0.f;
+  const float scale_log2 = p.scale * LOG2E;
 
-  uint16_t* out = (uint16_t*)p.out;
+  // Key loop, unrolled by two so that every LDS access names its buffer: tile ti is read from
+  // (k0, v0) or (k1, v1) while tile ti + 1 streams into the other pair by LDS DMA.
+  if (n_tiles > 0) {
+    const Tile t0 = tile_of(0);
+    dma_rows(src, t0, false, pf_k0, KLD, wave, 8, lane);
+    dma_rows(src, t0, true, pf_v0, VLD, wave, 8, lane);
+  }
+  wait_all();
+  __syncthreads();
+  auto body = [&](int ti, const char* kcur, const char* vcur, char* knxt, char* vnxt) {
+    const Tile t = tile_of(ti);
+    if (ti + 1 < n_tiles) {
+      const Tile tn = tile_of(ti + 1);
+      dma_rows(src, tn, false, knxt, KLD, wave, 8, lane);
+      dma_rows(src, tn, true, vnxt, VLD, wave, 8, lane);
+    }
+    f32x4_t s[2];
+    row_scores(s, qf, kcur, lane);
+    row_softmax_pv(st, s, vcur, t, rp, scale_log2, lane);
+    wait_all();  // this wave's transfers of tile ti + 1 have landed
+    __syncthreads();
+  };
+  for (int ti = 0; ti < n_tiles; ti += 2) {
+    body(ti, pf_k0, pf_v0, pf_k1, pf_v1);
+    if (ti + 1 < n_tiles) body(ti + 1, pf_k1, pf_v1, pf_k0, pf_v0);
+  }
+
+  const int i = r_first + l16;
+  const float inv = final_scale(st.m, wave_sum16(st.l));
+  if (i < i_end && h_ok) {
+    uint16_t* orow = (uint16_t*)p.out + (((size_t)b * p.Tq + i) * p.H + h) * D;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int i = i_first + 16 * nb + l16;
-    const float inv = final_scale(st.m[nb], wave_sum16(st.l[nb]));
-    if (i >= i_end || !h_ok) continue;
-    uint16_t* orow = out + (((size_t)b * p.Tq + i) * p.H + h) * D + hf * HALF;
-#pragma unroll
-    for (int cb = 0; cb < 16; ++cb) store4(orow + 16 * cb + 4 * g, st.o[cb][nb] * inv);
+    for (int cb = 0; cb < 32; ++cb) store4(orow + 16 * cb + 4 * g, st.o[cb] * inv);
   }
 }
 
@@ -394,11 +521,8 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_kernel(HcaParams p) {
 // One workgroup of 4 waves = 2 pairs (heads 0..31, 32..63 of a 64-head group) per
 // (sequence, key split).  Keys of a sequence: compressed entries 0..ne-1, then raw positions
 // s_lo..t; all rows are at position t.
-constexpr size_t DEC_SMEM = XS_OFF + 4 * 4 * 64 * 16;
-
 __global__ __launch_bounds__(256, 1) void hca_decode_kernel(HcaParams p, int n_split, int chunk,
                                                             float* part_o, float* part_ml) {
-  char* smem = hca_smem;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
@@ -440,8 +564,12 @@ __global__ __launch_bounds__(256, 1) void hca_decode_kernel(HcaParams p, int n_s
   src.win_len = p.win_len;
 
   const int h0 = hg * 64 + 32 * pair;
-  const RowVis rv0 = row_vis(t, p.window, p.block);
-  const RowVis rv[2] = {rv0, rv0};
+  RowPos rp;
+  rp.t0 = t;
+  rp.n_rows = 32;
+  rp.step = 0;
+  rp.window = p.window;
+  rp.block = p.block;
   Frag8 qf[2][8];
   const uint16_t* qb = (const uint16_t*)p.q + (size_t)b * p.H * D;
 #pragma unroll
@@ -452,8 +580,7 @@ __global__ __launch_bounds__(256, 1) void hca_decode_kernel(HcaParams p, int n_s
   }
   HalfState st;
   init_state(st);
-  key_loop(st, qf, rv, src, tile_of, tiles_c + tiles_w, wave, 4, hf, lane, p.scale * LOG2E,
-           smem);
+  key_loop(st, qf, rp, src, tile_of, tiles_c + tiles_w, wave, 4, hf, lane, p.scale * LOG2E);
 
   float lt[2];
 #pragma unroll
@@ -542,16 +669,6 @@ size_t hca_bf16_workspace(const HcaParams& p) {
 }
 
 hipError_t launch_hca_bf16(const HcaParams& p, hipStream_t stream) {
-  static bool attr_set = false;  // idempotent: racing threads set the same values
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)hca_prefill_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)PF_SMEM);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)hca_decode_kernel,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)DEC_SMEM);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   hipError_t e;
   if (use_decode(p)) {
     int n_split, chunk;
@@ -559,7 +676,7 @@ hipError_t launch_hca_bf16(const HcaParams& p, hipStream_t stream) {
     float* part_o = (float*)p.ws;
     float* part_ml = part_o ? part_o + (size_t)p.B * n_split * p.H * D : nullptr;
     const long long grid = (long long)p.B * (p.H / 64) * n_split;
-    hipLaunchKernelGGL(hca_decode_kernel, dim3((unsigned)grid), dim3(256), DEC_SMEM, stream, p,
+    hipLaunchKernelGGL(hca_decode_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p,
                        n_split, chunk, part_o, part_ml);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -571,7 +688,7 @@ hipError_t launch_hca_bf16(const HcaParams& p, hipStream_t stream) {
     }
   } else {
     const long long grid = (long long)p.B * ((p.Tq + 31) / 32) * ((p.H + 3) / 4);
-    hipLaunchKernelGGL(hca_prefill_kernel, dim3((unsigned)grid), dim3(512), PF_SMEM, stream, p);
+    hipLaunchKernelGGL(hca_prefill_kernel, dim3((unsigned)grid), dim3(512), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
