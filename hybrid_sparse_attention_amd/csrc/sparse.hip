@@ -4,14 +4,18 @@
 // listed position is one key (negative or out-of-range entries are skipped), order is
 // irrelevant, and one latent row may serve as both key and value.
 //
-// Workgroup: one query row (all H heads share its index list) and a range of its list.
-// Waves 0,1 / 2,3 take heads 0..31 / 32..63 (as MFMA columns) of the even / odd 32-key
-// tiles; each pair of tiles is gathered together (coalesced 16-byte row reads, V transposed
-// while staged), the two halves merge through LDS.  The products are the transposed ones
-// (S^T = K Q^T, O^T = V^T P^T on v_mfma_f32_16x16x32_bf16) so the P fragment is the S^T
-// accumulator itself.  Long lists of few query rows are split over several workgroups,
-// whose partial (max, sum, O) a combine kernel merges.  The output gate runs afterwards as
-// the gate GEMM in place (a per-row workgroup would have to read the whole gate matrix).
+// Workgroup: one query row (its H heads share the index list), 64 heads, and a range of the
+// list.  Four waves take 16 heads each over the whole 256-wide head: Q in 32 registers, O in
+// 64.  Keys come in tiles of 32 gathered rows, brought to LDS by LDS DMA (one instruction
+// fetches two 512-byte rows) and double buffered.  When the value rows are the key rows the
+// single tile serves both products: S^T = K Q^T reads it row-wise, O^T = V^T P^T reads it
+// through the transposing LDS read, so each gathered row crosses the memory system once.
+// The 16-byte chunks of a row are XOR-swizzled (chunk c of row r sits at position c ^ sw(r))
+// so that both read patterns are free of bank conflicts; the DMA applies the swizzle by
+// choosing which chunk each lane fetches.  Long lists of few query rows are split over several
+// workgroups, whose partial (max, sum, O) a combine kernel merges.  The output gate runs
+// afterwards as the gate GEMM in place (a per-row workgroup would have to read the whole gate
+// matrix).
 #include "common.h"
 #include "kernels.h"
 
@@ -20,92 +24,111 @@ namespace lgsa {
 namespace {
 
 constexpr int D = 256;
-constexpr int KT = 32;
-constexpr int KS_LD = D + 8;
-constexpr int VT_LD = KT + 8;
-constexpr int KS_ELEMS = KT * KS_LD;
-constexpr int VT_ELEMS = D * VT_LD;
+constexpr int KT = 32;                  // keys per tile
+constexpr int TROW = 2 * D;             // bytes of one gathered row (no padding: swizzled)
+constexpr int TILE = KT * TROW;         // 16 KiB
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LAZY = 8.0f;            // rescale O only when the max grows by more (log2)
+constexpr float NEG_BIG = -1.0e30f;     // masked logit (finite: no inf - inf)
 
-__device__ __forceinline__ int slot_key(int p) {
-  const int g = p >> 3, j = p & 7;
-  return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
-}
-
-__shared__ __attribute__((aligned(16))) uint16_t sp_smem[2 * KS_ELEMS + 2 * VT_ELEMS];
-__shared__ int sp_idx[2 * KT];
+// chunk swizzle of row r: rows 0..7 -> 0, 2, .., 14; rows 8..15 -> 1, 3, .., 15 (period 16)
+__device__ __forceinline__ int sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 struct WaveState {
-  f32x4_t o[16][2];
-  float m[2], l[2];
+  f32x4_t o[16];  // o[cb][r] = O[head l16][16cb + 4g + r]
+  float m;        // reference max (log2 domain)
+  float l;        // running partial sum of this lane's keys
 };
 
-__device__ __forceinline__ void attend(WaveState& st, const Frag8 (&qf)[2][8],
-                                       const uint16_t* ks, const uint16_t* vt,
-                                       const int* tidx, float scale_log2, int lane) {
-  const int l16 = lane & 15, g = lane >> 4;
-  f32x4_t s[2][2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) s[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+// Gather one tile: DMA instruction i (of 16) loads tile rows 2i (lanes 0..31) and 2i + 1
+// (lanes 32..63); the wave issues i = w, w + n_waves, ...  `ix` holds, in lane j < 32, the
+// position of tile row j (-1 when skipped: the row is then read from position 0 and masked).
+__device__ __forceinline__ void gather_tile(const uint16_t* rows, long long stride, int ix,
+                                            char* tile, int w, int n_waves, int lane) {
+  const int hi = lane >> 5;
+  for (int i = w; i < KT / 2; i += n_waves) {
+    const int sa = __builtin_amdgcn_readlane(ix, 2 * i);
+    const int sb = __builtin_amdgcn_readlane(ix, 2 * i + 1);
+    const int s = max(hi ? sb : sa, 0);
+    const int r = 2 * i + hi;
+    const int chunk = (lane & 31) ^ sw(r);
+    lds_dma16(rows + (size_t)s * stride + 8 * chunk, tile + 2 * i * TROW);
+  }
+}
+
+// raw list entries of tile rows j0 .. j0 + 31 (lane j < 32; -1 past j_end).  The range check
+// is left to valid_ix, applied only once the load has been drained with the tile's transfers:
+// using the loaded value earlier would make the wave wait for the gathers issued before it.
+__device__ __forceinline__ int load_ix(const int32_t* idx, int j0, int j_end, int lane) {
+  const int j = j0 + lane;
+  return (lane < KT && j < j_end) ? idx[j] : -1;
+}
+
+// the entry as a position, or -1 when it is skipped (negative or beyond the rows held)
+__device__ __forceinline__ int valid_ix(int s, int S) { return (s >= 0 && s < S) ? s : -1; }
+
+__device__ __forceinline__ void scores(f32x4_t (&s)[2], const Frag8 (&qf)[8], const char* kt,
+                                       const int (&kb)[4]) {
+  s[0] = s[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
     Frag8 ka[2];
+    // key row 16mb + l16, chunk 4kk + g: position ((4(kk & 3) + g) ^ sw) + 16(kk >> 2)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
-      ka[mb].u = *(const uint4*)(ks + (16 * mb + l16) * KS_LD + 32 * kk + 8 * g);
+      ka[mb].u = *(const uint4*)(kt + kb[kk & 3] + 256 * (kk >> 2) + 16 * TROW * mb);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) s[mb][nb] = mfma_16x16x32(ka[mb], qf[nb][kk], s[mb][nb]);
+    for (int mb = 0; mb < 2; ++mb) s[mb] = mfma_16x16x32(ka[mb], qf[kk], s[mb]);
   }
-  bool valid[2][4];
+}
+
+__device__ __forceinline__ void softmax_pv(WaveState& st, const f32x4_t (&s)[2],
+                                           const char* vt, uint32_t valid, float scale_log2,
+                                           int vrow, int vsw, int vh, int lane) {
+  const int g = lane >> 4;
+  float x[2][4];  // [mb][r]: key 16mb + 4g + r
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) valid[mb][r] = tidx[16 * mb + 4 * g + r] >= 0;
-  float alpha[2];
-  Frag8 pf[2];
+    for (int r = 0; r < 4; ++r)
+      x[mb][r] = ((valid >> (16 * mb + 4 * g + r)) & 1u) ? s[mb][r] * scale_log2 : NEG_BIG;
+  float mx = x[0][0];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    float x[2][4];
-    float mx = -INFINITY;
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[mb][r]);
+  const float m_new = fmaxf(st.m, wave_max16(mx));
+  if (__any(m_new > st.m + LAZY)) {
+    const float alpha = fast_exp2(st.m - m_new);
+    st.m = m_new;
+    st.l *= alpha;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x[mb][r] = valid[mb][r] ? s[mb][nb][r] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, x[mb][r]);
-      }
-    mx = wave_max16(mx);
-    const float m_new = fmaxf(st.m[nb], mx);
-    alpha[nb] = st.m[nb] == -INFINITY ? 0.f : fast_exp2(st.m[nb] - m_new);
-    st.m[nb] = m_new;
-    float p[2][4], psum = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[mb][r] = x[mb][r] == -INFINITY ? 0.f : fast_exp2(x[mb][r] - m_new);
-        psum += p[mb][r];
-      }
-    st.l[nb] = st.l[nb] * alpha[nb] + psum;
-    pf[nb].u = make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
-                          pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3]));
+    for (int cb = 0; cb < 16; ++cb) st.o[cb] *= alpha;
   }
-  if (__any((alpha[0] != 1.f) | (alpha[1] != 1.f))) {
+  float pr[2][4];
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb)
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) st.o[cb][nb] *= alpha[nb];
-  }
+    for (int r = 0; r < 4; ++r) {
+      pr[mb][r] = fast_exp2(x[mb][r] - st.m);
+      st.l += pr[mb][r];
+    }
+  Frag8 pf;
+  pf.u = make_uint4(pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
+                    pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3]));
+  // V^T fragment of column block cb: transposed reads of rows vrow (slots 8g..8g+3) and
+  // vrow + 16 (slots 8g+4..8g+7), columns 16cb + 4(l16 % 4) .. +3 = chunk 2cb + vh, half
+  // l16 & 1 of it, the chunk found at its swizzled position
+  const int vh_t = opaque(vh);  // formed per tile, so the 16 positions are not kept live
 #pragma unroll
   for (int cb = 0; cb < 16; ++cb) {
+    const int pos = (2 * cb + vh_t) ^ vsw;
+    const char* a = vt + vrow + 16 * pos;
     Frag8 va;
-    va.u = *(const uint4*)(vt + (16 * cb + l16) * VT_LD + 8 * g);
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) st.o[cb][nb] = mfma_16x16x32(va, pf[nb], st.o[cb][nb]);
+    const uint2 lo = lds_read_tr16(a);
+    const uint2 hi = lds_read_tr16(a + 16 * TROW);
+    va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    st.o[cb] = mfma_16x16x32(va, pf, st.o[cb]);
   }
 }
 
@@ -116,11 +139,18 @@ __device__ __forceinline__ void store4(uint16_t* dst, const f32x4_t& v) {
   *(uint2*)dst = r;
 }
 
-// grid: (row r = b*Tq + i) x (head group of 64) x (split); n_split == 1 writes out directly
-__global__ __launch_bounds__(256, 2) void sparse_kernel(SparseParams p, int n_split,
-                                                        int chunk, float* part_o,
-                                                        float* part_ml) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// grid: (row r = b*Tq + i) x (head group of 64) x (split); n_split == 1 writes out directly.
+// ALIAS: the value rows are the key rows (one gathered tile per step); otherwise a second tile
+// of value rows is gathered beside it.
+template <bool ALIAS>
+__global__ __launch_bounds__(256, 2) void sparse_kernel(SparseParams p, int n_split, int chunk,
+                                                        float* part_o, float* part_ml) {
+  __shared__ __attribute__((aligned(1024))) char kt0[TILE];
+  __shared__ __attribute__((aligned(1024))) char kt1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vt0[ALIAS ? 16 : TILE];
+  __shared__ __attribute__((aligned(1024))) char vt1[ALIAS ? 16 : TILE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int n_hg = p.H / 64;
   const int sp = blockIdx.x % n_split;
@@ -128,130 +158,88 @@ __global__ __launch_bounds__(256, 2) void sparse_kernel(SparseParams p, int n_sp
   const int r = blockIdx.x / (n_split * n_hg);
   const int b = r / p.Tq;
   const int j_begin = sp * chunk, j_end = min(p.k, j_begin + chunk);
-  const int half = wave >> 1;
-  const int h0 = hg * 64 + 32 * (wave & 1);
+  const int n_tiles = max(0, (j_end - j_begin + KT - 1) / KT);
+  const int h = hg * 64 + 16 * wave + l16;  // this lane's head (MFMA column)
 
-  Frag8 qf[2][8];
-  const uint16_t* qb = (const uint16_t*)p.q + (size_t)r * p.H * D;
+  Frag8 qf[8];
+  {
+    const uint16_t* qr = (const uint16_t*)p.q + ((size_t)r * p.H + h) * D;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const uint16_t* qr = qb + (size_t)(h0 + 16 * nb + l16) * D;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[nb][kk].u = *(const uint4*)(qr + 32 * kk + 8 * g);
+    for (int kk = 0; kk < 8; ++kk) qf[kk].u = *(const uint4*)(qr + 32 * kk + 8 * g);
   }
   WaveState st;
 #pragma unroll
-  for (int cb = 0; cb < 16; ++cb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) st.o[cb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  st.m[0] = st.m[1] = -INFINITY;
-  st.l[0] = st.l[1] = 0.f;
+  for (int cb = 0; cb < 16; ++cb) st.o[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = NEG_BIG;
+  st.l = 0.f;
   const float scale_log2 = p.scale * LOG2E;
+
+  // lane-constant LDS offsets: key reads (row l16 / l16 + 16, chunk 4kk + g) and transposed
+  // value reads (rows 4g + l16/4 and +16, chunk 2cb + (l16 & 3)/2, half l16 & 1)
+  const int ksw = sw(l16);
+  int kb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) kb[q] = l16 * TROW + 16 * ((4 * q + g) ^ ksw);
+  const int vr = 4 * g + (l16 >> 2);
+  const int vrow = vr * TROW + 8 * (l16 & 1);
+  const int vsw = sw(vr);
+  const int vh = (l16 & 3) >> 1;
 
   const int32_t* idx = p.idx + (size_t)r * p.k;
   const uint16_t* kl = (const uint16_t*)p.k_lat + (size_t)b * p.S * p.k_stride;
   const uint16_t* vl = (const uint16_t*)p.v_lat + (size_t)b * p.S * p.v_stride;
-  for (int j0 = j_begin; j0 < j_end; j0 += 2 * KT) {
-    // positions of the two tiles (-1: skipped)
-    if (tid < 2 * KT) {
-      const int j = j0 + tid;
-      int s = j < j_end ? idx[j] : -1;
-      if (s >= p.S) s = -1;
-      sp_idx[tid] = s;
+
+  // prologue: tile 0 in flight, the positions of tile 1 loaded
+  const int ix_cur = valid_ix(load_ix(idx, j_begin, j_end, lane), p.S);
+  uint32_t valid_cur = (uint32_t)__ballot(ix_cur >= 0);
+  if (n_tiles > 0) {
+    gather_tile(kl, p.k_stride, ix_cur, kt0, wave, 4, lane);
+    if (!ALIAS) gather_tile(vl, p.v_stride, ix_cur, vt0, wave, 4, lane);
+  }
+  int ix_nxt = load_ix(idx, j_begin + KT, j_end, lane);
+  wait_all();
+  __syncthreads();
+
+  auto body = [&](int ti, const char* kc, const char* vc, char* kn, char* vn) {
+    uint32_t valid_nxt = 0;
+    if (ti + 1 < n_tiles) {
+      const int ixv = valid_ix(ix_nxt, p.S);
+      valid_nxt = (uint32_t)__ballot(ixv >= 0);
+      gather_tile(kl, p.k_stride, ixv, kn, wave, 4, lane);
+      if (!ALIAS) gather_tile(vl, p.v_stride, ixv, vn, wave, 4, lane);
     }
+    const int ix_after = load_ix(idx, j_begin + KT * (ti + 2), j_end, lane);
+    f32x4_t s[2];
+    scores(s, qf, kc, kb);
+    softmax_pv(st, s, ALIAS ? kc : vc, valid_cur, scale_log2, vrow, vsw, vh, lane);
+    wait_all();  // this wave's gathers of tile ti + 1 and the positions of tile ti + 2
     __syncthreads();
-    // K rows: 64 rows x 32 chunks of 16 bytes, 8 per thread
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = tid + 256 * u;
-      const int key = c >> 5, col = (c & 31) * 8;
-      const int s = sp_idx[key];
-      const uint4 v = s >= 0 ? *(const uint4*)(kl + (size_t)s * p.k_stride + col)
-                             : make_uint4(0, 0, 0, 0);
-      *(uint4*)(sp_smem + (key >> 5) * KS_ELEMS + (key & 31) * KS_LD + col) = v;
-    }
-    // V^T: thread -> tile u, slot group kg, column group cg; 8 rows, then an 8x8 transpose
-    {
-      const int u = tid >> 7, kg = tid & 3, cg = (tid >> 2) & 31;
-      uint4 rows[8], cols[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int s = sp_idx[KT * u + slot_key(8 * kg + jj)];
-        rows[jj] = s >= 0 ? *(const uint4*)(vl + (size_t)s * p.v_stride + 8 * cg)
-                          : make_uint4(0, 0, 0, 0);
-      }
-      transpose8x8(rows, cols);
-      uint16_t* vt = sp_smem + 2 * KS_ELEMS + u * VT_ELEMS;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) *(uint4*)(vt + (8 * cg + i) * VT_LD + 8 * kg) = cols[i];
-    }
-    __syncthreads();
-    if (j0 + KT * half < j_end)
-      attend(st, qf, sp_smem + half * KS_ELEMS, sp_smem + 2 * KS_ELEMS + half * VT_ELEMS,
-             sp_idx + KT * half, scale_log2, lane);
-    __syncthreads();
+    valid_cur = valid_nxt;
+    ix_nxt = ix_after;
+  };
+  for (int ti = 0; ti < n_tiles; ti += 2) {
+    body(ti, kt0, vt0, kt1, vt1);
+    if (ti + 1 < n_tiles) body(ti + 1, kt1, vt1, kt0, vt0);
   }
 
-  // merge the two tile halves through LDS
-  float* xo = (float*)sp_smem;              // [2][16][2][64][4] floats = 64 KB
-  float* xml = xo + 2 * 16 * 2 * 64 * 4;    // [2][2][2][64]
-  float lsum[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) lsum[nb] = wave_sum16(st.l[nb]);
-  const int wv = wave & 1;
-  if (half == 1) {
-#pragma unroll
-    for (int cb = 0; cb < 16; ++cb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        *(f32x4_t*)(xo + (((wv * 16 + cb) * 2 + nb) * 64 + lane) * 4) = st.o[cb][nb];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      xml[((wv * 2 + nb) * 2 + 0) * 64 + lane] = st.m[nb];
-      xml[((wv * 2 + nb) * 2 + 1) * 64 + lane] = lsum[nb];
-    }
-  }
-  __syncthreads();
-  if (half == 1) return;
-  float as[2], ao[2], mt[2], lt[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const float mo = xml[((wv * 2 + nb) * 2 + 0) * 64 + lane];
-    const float lo = xml[((wv * 2 + nb) * 2 + 1) * 64 + lane];
-    mt[nb] = fmaxf(st.m[nb], mo);
-    as[nb] = st.m[nb] == -INFINITY ? 0.f : fast_exp2(st.m[nb] - mt[nb]);
-    ao[nb] = mo == -INFINITY ? 0.f : fast_exp2(mo - mt[nb]);
-    lt[nb] = lsum[nb] * as[nb] + lo * ao[nb];
-  }
-#pragma unroll
-  for (int cb = 0; cb < 16; ++cb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const f32x4_t other = *(const f32x4_t*)(xo + (((wv * 16 + cb) * 2 + nb) * 64 + lane) * 4);
-      st.o[cb][nb] = st.o[cb][nb] * as[nb] + other * ao[nb];
-    }
+  const float lt = wave_sum16(st.l);
+  const bool seen = st.m > 0.5f * NEG_BIG;
   if (n_split == 1) {
-    uint16_t* out = (uint16_t*)p.out + (size_t)r * p.H * D;
+    const float inv = (seen && lt > 0.f) ? 1.f / lt : 0.f;
+    uint16_t* orow = (uint16_t*)p.out + ((size_t)r * p.H + h) * D;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const float inv = lt[nb] > 0.f ? 1.f / lt[nb] : 0.f;
-      uint16_t* orow = out + (size_t)(h0 + 16 * nb + l16) * D;
-#pragma unroll
-      for (int cb = 0; cb < 16; ++cb) store4(orow + 16 * cb + 4 * g, st.o[cb][nb] * inv);
-    }
+    for (int cb = 0; cb < 16; ++cb) store4(orow + 16 * cb + 4 * g, st.o[cb] * inv);
     return;
   }
+  const size_t pr = ((size_t)r * n_split + sp) * p.H + h;
+  float* po = part_o + pr * D;
+  // a split that saw no valid key contributes nothing: max -inf, sum 0, O 0
+  const float keep = seen ? 1.f : 0.f;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int hh = h0 + 16 * nb + l16;
-    const size_t pr = ((size_t)r * n_split + sp) * p.H + hh;
-    float* po = part_o + pr * D;
-#pragma unroll
-    for (int cb = 0; cb < 16; ++cb) *(f32x4_t*)(po + 16 * cb + 4 * g) = st.o[cb][nb];
-    if (g == 0) {
-      part_ml[pr * 2 + 0] = mt[nb];
-      part_ml[pr * 2 + 1] = lt[nb];
-    }
+  for (int cb = 0; cb < 16; ++cb) *(f32x4_t*)(po + 16 * cb + 4 * g) = st.o[cb] * keep;
+  if (g == 0) {
+    part_ml[pr * 2 + 0] = seen ? st.m : -INFINITY;
+    part_ml[pr * 2 + 1] = seen ? lt : 0.f;
   }
 }
 
@@ -283,13 +271,15 @@ __global__ __launch_bounds__(64) void sparse_combine_kernel(const float* __restr
   *(uint2*)(out + (size_t)rh * D + 4 * threadIdx.x) = o;
 }
 
+// Enough workgroups to fill the chip (four resident per CU) before a list is split.
 void sparse_plan(const SparseParams& p, int& n_split, int& chunk) {
   const long long wgs = (long long)p.B * p.Tq * (p.H / 64);
-  long long want = wgs >= 512 ? 1 : (512 + wgs - 1) / wgs;
-  const long long max_split = (p.k + 2 * KT - 1) / (2 * KT);
+  const long long target = 1024;
+  long long want = wgs >= target ? 1 : (target + wgs - 1) / wgs;
+  const long long max_split = (p.k + KT - 1) / KT;
   n_split = (int)std::max<long long>(1, std::min(want, max_split));
   long long c = (p.k + n_split - 1) / n_split;
-  c = (c + 2 * KT - 1) / (2 * KT) * (2 * KT);
+  c = (c + KT - 1) / KT * KT;
   chunk = (int)c;
   n_split = (int)((p.k + chunk - 1) / chunk);
 }
@@ -312,8 +302,13 @@ hipError_t launch_sparse(const SparseParams& p, hipStream_t stream) {
   float* part_o = (float*)p.ws;
   float* part_ml = part_o ? part_o + (size_t)rows * n_split * p.H * D : nullptr;
   const long long grid = rows * (p.H / 64) * n_split;
-  hipLaunchKernelGGL(sparse_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p, n_split,
-                     chunk, part_o, part_ml);
+  const bool alias = p.v_lat == p.k_lat && p.v_stride == p.k_stride;
+  if (alias)
+    hipLaunchKernelGGL(sparse_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, p,
+                       n_split, chunk, part_o, part_ml);
+  else
+    hipLaunchKernelGGL(sparse_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, p,
+                       n_split, chunk, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (n_split > 1) {
