@@ -13,9 +13,11 @@
 // key tile in LDS serves 64 queries; they are written as keys to the workspace, a chunk of
 // queries at a time, and a 1024-thread workgroup per query selects.
 // Decode (few queries, long context): one workgroup per (query, 16384-position segment)
-// streams its key rows through LDS once, scores them with fp32 FMA, selects the segment's
-// top-k in LDS and writes them as candidates; a second kernel selects the final top-k among
-// the candidates (the union of per-segment top-k sets contains the global top-k).
+// streams its key rows once, scores them with fp32 FMA, selects the segment's top-k in LDS and
+// writes them as a candidate list in ascending position; 4-way reductions of candidate lists
+// (each keeping the top k of four lists) then narrow 64 lists to one (the union of top-k sets
+// of disjoint parts contains the top k of the whole, and position order is kept throughout, so
+// the lower-index rule stays exact).
 #include "common.h"
 #include "kernels.h"
 
@@ -31,81 +33,156 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive rank of `flag` among the workgroup's threads (thread order), and the total.
+// Exclusive prefix sums, in thread order, of two per-thread counts, and their totals.
+// `wsum` holds 2 * NT / 64 ints.  Contains two workgroup barriers.
 template <int NT>
-__device__ __forceinline__ int block_rank(bool flag, int& total, int* wsum) {
+__device__ __forceinline__ void block_scan2(int a, int b, int& a_ex, int& b_ex, int& a_tot,
+                                            int& b_tot, int* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const unsigned long long bal = __ballot(flag);
-  const int in_wave = __popcll(bal & ((1ull << lane) - 1ull));
+  int ai = a, bi = b;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ya = __shfl_up(ai, off), yb = __shfl_up(bi, off);
+    if (lane >= off) {
+      ai += ya;
+      bi += yb;
+    }
+  }
+  if (lane == 63) {
+    wsum[2 * wave] = ai;
+    wsum[2 * wave + 1] = bi;
+  }
   __syncthreads();
-  if (lane == 0) wsum[wave] = __popcll(bal);
-  __syncthreads();
-  int before = 0, tot = 0;
+  int pa = 0, pb = 0, ta = 0, tb = 0;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) {
-    const int c = wsum[w];
-    before += w < wave ? c : 0;
-    tot += c;
+    const int ca = wsum[2 * w], cb = wsum[2 * w + 1];
+    pa += w < wave ? ca : 0;
+    pb += w < wave ? cb : 0;
+    ta += ca;
+    tb += cb;
   }
-  total = tot;
-  return before + in_wave;
+  a_ex = pa + ai - a;
+  b_ex = pb + bi - b;
+  a_tot = ta;
+  b_tot = tb;
+  __syncthreads();
 }
 
-// Finds the k-th largest key K* among get(0..n-1) (k <= n) and the number of keys equal to
-// K* that belong to the top k; 8-bit digits, most significant first.
+// Histogram of one radix digit, one private copy per wave (hist: NT / 64 x 256 counters), and
+// the selection of the digit that holds the kr-th largest key: thread t < 256 takes digit
+// 255 - t, the counts are scanned in that (descending) order across the first four waves, and
+// the one thread whose inclusive count first reaches kr writes sh[0] = digit and
+// sh[1] = kr - (keys in larger digits).
+template <int NT, class Get>
+__device__ void radix_digit(const Get& get, int n, uint32_t prefix, uint32_t hi_mask, int shift,
+                            int kr, uint32_t* hist, int* sh, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int x = tid; x < (NT / 64) * 256; x += NT) hist[x] = 0u;
+  __syncthreads();
+  uint32_t* mine = hist + wave * 256;
+  constexpr int PER = 8;  // loads in flight per thread; consecutive threads read consecutive keys
+  for (int c0 = tid; c0 < n; c0 += NT * PER) {
+    uint32_t u[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) u[j] = c0 + j * NT < n ? get(c0 + j * NT) : 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (c0 + j * NT < n && (u[j] & hi_mask) == prefix)
+        atomicAdd(&mine[(u[j] >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  int c = 0, incl = 0;
+  if (tid < 256) {
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) c += (int)hist[w * 256 + 255 - tid];
+    incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+  }
+  __syncthreads();
+  if (tid < 256) {
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    incl += before;
+    const int excl = incl - c;
+    if (incl >= kr && excl < kr) {
+      sh[0] = 255 - tid;
+      sh[1] = kr - excl;
+    }
+  }
+  __syncthreads();
+}
+
+// Finds the k-th largest key K* among get(0..n-1) (1 <= k <= n) and the number of keys equal
+// to K* that belong to the top k; 8-bit digits, most significant first.
 template <int NT, class Get>
 __device__ void radix_threshold(const Get& get, int n, int k, uint32_t* hist, int* sh,
-                                uint32_t& kstar, int& need_eq) {
+                                int* wsum, uint32_t& kstar, int& need_eq) {
   uint32_t prefix = 0u;
   int kr = k;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int x = threadIdx.x; x < 256; x += NT) hist[x] = 0u;
-    __syncthreads();
     const uint32_t hi_mask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int i = threadIdx.x; i < n; i += NT) {
-      const uint32_t u = get(i);
-      if ((u & hi_mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int cum = 0, dsel = 0;
-      for (int dg = 255; dg >= 0; --dg) {
-        const int c = (int)hist[dg];
-        if (cum + c >= kr) {
-          dsel = dg;
-          break;
-        }
-        cum += c;
-      }
-      sh[0] = dsel;
-      sh[1] = kr - cum;
-    }
-    __syncthreads();
+    radix_digit<NT>(get, n, prefix, hi_mask, shift, kr, hist, sh, wsum);
     prefix |= (uint32_t)sh[0] << shift;
     kr = sh[1];
-    __syncthreads();
+    __syncthreads();  // sh is rewritten by the next digit
   }
   kstar = prefix;
   need_eq = kr;
 }
 
+constexpr int EMIT_PER = 8;
+
 // Ascending pass: emit(slot, i, key) for every i whose key is above K*, and for the first
-// need_eq (in index order) whose key equals K*.
+// need_eq (in index order) whose key equals K*.  Each thread takes EMIT_PER consecutive
+// indices of a chunk of NT * EMIT_PER, so one block scan per chunk orders the whole chunk.
+// With a `stage` buffer (NT * EMIT_PER keys of LDS) each chunk is first copied there with
+// coalesced reads (for keys in global memory); without one, get() is read directly (LDS).
 template <int NT, class Get, class Emit>
 __device__ void emit_topk(const Get& get, int n, uint32_t kstar, int need_eq, int* wsum,
-                          const Emit& emit) {
+                          uint32_t* stage, const Emit& emit) {
+  constexpr int PER = EMIT_PER;
   int base = 0, eq_seen = 0;
-  for (int c0 = 0; c0 < n; c0 += NT) {
-    const int i = c0 + (int)threadIdx.x;
-    const uint32_t u = i < n ? get(i) : 0u;
-    const bool gt = i < n && u > kstar;
-    const bool eq = i < n && u == kstar;
-    int eq_tot, sel_tot;
-    const int eq_rank = block_rank<NT>(eq, eq_tot, wsum);
-    const bool sel = gt || (eq && eq_seen + eq_rank < need_eq);
-    const int r = block_rank<NT>(sel, sel_tot, wsum);
-    if (sel) emit(base + r, i, u);
-    base += sel_tot;
+  for (int c0 = 0; c0 < n; c0 += NT * PER) {
+    if (stage != nullptr) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int x = c0 + j * NT + (int)threadIdx.x;
+        stage[j * NT + threadIdx.x] = x < n ? get(x) : 0u;
+      }
+      __syncthreads();
+    }
+    const int i0 = c0 + (int)threadIdx.x * PER;
+    uint32_t u[PER];
+    int n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      u[j] = i0 + j < n ? (stage != nullptr ? stage[threadIdx.x * PER + j] : get(i0 + j)) : 0u;
+      n_gt += (i0 + j < n && u[j] > kstar) ? 1 : 0;
+      n_eq += (i0 + j < n && u[j] == kstar) ? 1 : 0;
+    }
+    int gt_ex, eq_ex, gt_tot, eq_tot;
+    block_scan2<NT>(n_gt, n_eq, gt_ex, eq_ex, gt_tot, eq_tot, wsum);
+    // equal keys of earlier threads in this chunk that are kept
+    const int eq_keep_before = min(max(need_eq - eq_seen, 0), eq_ex);
+    int slot = base + gt_ex + eq_keep_before;
+    int eq_rank = eq_seen + eq_ex;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (i0 + j >= n) continue;
+      bool sel = u[j] > kstar;
+      if (u[j] == kstar) {
+        sel = eq_rank < need_eq;
+        ++eq_rank;
+      }
+      if (sel) emit(slot++, i0 + j, u[j]);
+    }
+    base += gt_tot + min(max(need_eq - eq_seen, 0), eq_tot);
     eq_seen += eq_tot;
   }
 }
@@ -199,9 +276,10 @@ __global__ __launch_bounds__(SEL_NT) void index_select_rows_kernel(IndexParams p
                                                                    int i_begin,
                                                                    const uint32_t* ws,
                                                                    int s_ld) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[(SEL_NT / 64) * 256];
   __shared__ int sh[2];
-  __shared__ int wsum[SEL_NT / 64];
+  __shared__ int wsum[2 * SEL_NT / 64];
+  __shared__ uint32_t stage[SEL_NT * EMIT_PER];
   const int i = i_begin + blockIdx.x;
   const int t = min(p.pos0[b] + i, min(p.S, p.max_pos + 1) - 1);
   const int n = t >= 0 ? t + 1 : 0;
@@ -214,34 +292,43 @@ __global__ __launch_bounds__(SEL_NT) void index_select_rows_kernel(IndexParams p
   auto get = [&](int x) { return row[x]; };
   uint32_t kstar;
   int need_eq;
-  radix_threshold<SEL_NT>(get, n, p.k, hist, sh, kstar, need_eq);
-  emit_topk<SEL_NT>(get, n, kstar, need_eq, wsum,
+  radix_threshold<SEL_NT>(get, n, p.k, hist, sh, wsum, kstar, need_eq);
+  emit_topk<SEL_NT>(get, n, kstar, need_eq, wsum, stage,
                     [&](int slot, int x, uint32_t) { out[slot] = x; });
 }
 
 // ------------------------------------------------------------------------------ decode
 constexpr int SEG = 16384;       // positions per segment (>= the largest supported k)
 constexpr int DEC_NT = 256;
-constexpr int DK_LD = 64 + 4;
 
+// One workgroup per (query row, segment of SEG positions): every lane scores one key row per
+// batch of 64 (its 256 bytes read straight into registers, the next batch's rows already in
+// flight while this one is scored, the query from LDS), the segment's scores stay in LDS as
+// ordered keys, and the segment's top k are written as candidates in ascending position,
+// with their count.
 __global__ __launch_bounds__(DEC_NT) void index_segment_kernel(IndexParams p, int n_seg,
                                                                uint32_t* cand_key,
-                                                               int32_t* cand_pos) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t seg_smem[];
-  uint32_t* skey = seg_smem;                                   // [SEG]
-  float* stage = (float*)(seg_smem + SEG);                     // [4 waves][64][DK_LD]
-  float* sq = stage + 4 * 64 * DK_LD;                          // [4][64] query, [4] weights
-  uint32_t* hist = (uint32_t*)(sq + 4 * 64 + 4);               // [256]
-  int* sh = (int*)(hist + 256);                                // [2]
-  int* wsum = sh + 2;                                          // [4]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                                               int32_t* cand_pos,
+                                                               int* cand_cnt) {
+  __shared__ uint32_t skey[SEG];
+  __shared__ __attribute__((aligned(16))) float sq[4 * 64 + 4];
+  __shared__ uint32_t hist[(DEC_NT / 64) * 256];
+  __shared__ int sh[2];
+  __shared__ int wsum[2 * DEC_NT / 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = blockIdx.x / n_seg, seg = blockIdx.x % n_seg;  // r = b * Tq + i
-  const int b = r / p.Tq, i = r % p.Tq;
-  const int t = min(p.pos0[b] + i, min(p.S, p.max_pos + 1) - 1);
+  const int b = r / p.Tq;
+  const int t = min(p.pos0[b] + r % p.Tq, min(p.S, p.max_pos + 1) - 1);
   const int n = t >= 0 ? t + 1 : 0;
   const int seg_start = seg * SEG;
-  if (n <= p.k || seg_start >= n) return;  // short rows are finished by the merge kernel
+  if (n <= p.k) return;  // short rows are finished by the last reduction
+  if (seg_start >= n) {  // a segment past the row's last position contributes nothing
+    if (tid == 0) cand_cnt[(size_t)r * n_seg + seg] = 0;
+    return;
+  }
   const int seg_n = min(SEG, n - seg_start);
+  if (tid == 0) cand_cnt[(size_t)r * n_seg + seg] = min(seg_n, p.k);
   for (int x = tid; x < 4 * 64; x += DEC_NT) {
     const int h = x >> 6;
     sq[x] = h < p.Hi ? p.q_idx[((size_t)r * p.Hi + h) * 64 + (x & 63)] : 0.f;
@@ -249,40 +336,39 @@ __global__ __launch_bounds__(DEC_NT) void index_segment_kernel(IndexParams p, in
   if (tid < 4) sq[256 + tid] = tid < p.Hi ? p.w_idx[(size_t)r * p.Hi + tid] : 0.f;
   __syncthreads();
   const float* kb = p.k_idx + ((size_t)b * p.S + seg_start) * 64;
-  float* st = stage + wave * 64 * DK_LD;
   const int n_batch = (seg_n + 63) / 64;
-  for (int bi = wave; bi < n_batch; bi += 4) {
-    const int k0 = bi * 64;
-    // 64 consecutive key rows = 16 KB contiguous: coalesced float4 loads into LDS rows
+  float4 kn[16];
+  auto load = [&](int bi) {
+    const int key = min(bi * 64 + lane, seg_n - 1);  // lanes past the end reread the last row
+    const float4* src = (const float4*)(kb + (size_t)key * 64);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int f = 64 * j + lane;  // float4 index within the batch
-      const int key = f >> 4, dim = (f & 15) * 4;
-      const float4 v = k0 + key < seg_n ? *(const float4*)(kb + (size_t)(k0 + key) * 64 + dim)
-                                        : make_float4(0.f, 0.f, 0.f, 0.f);
-      *(float4*)(st + key * DK_LD + dim) = v;
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    const float* kr = st + lane * DK_LD;
+    for (int j = 0; j < 16; ++j) kn[j] = src[j];
+  };
+  if (wave < n_batch) load(wave);
+  for (int bi = wave; bi < n_batch; bi += 4) {
+    float4 kv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) kv[j] = kn[j];
+    if (bi + 4 < n_batch) load(bi + 4);
+    // the query is read from LDS (a broadcast) per batch: an opaque offset keeps the compiler
+    // from holding all 256 values in registers
+    const float* qp = sq + opaque(0);
     float dot[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 64; c += 4) {
-      const float4 kv = *(const float4*)(kr + c);
+    for (int j = 0; j < 16; ++j) {
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const float4 qv = *(const float4*)(sq + h * 64 + c);
-        dot[h] = fmaf(qv.x, kv.x, dot[h]);
-        dot[h] = fmaf(qv.y, kv.y, dot[h]);
-        dot[h] = fmaf(qv.z, kv.z, dot[h]);
-        dot[h] = fmaf(qv.w, kv.w, dot[h]);
+        const float4 qv = *(const float4*)(qp + h * 64 + 4 * j);
+        dot[h] = fmaf(qv.x, kv[j].x, dot[h]);
+        dot[h] = fmaf(qv.y, kv[j].y, dot[h]);
+        dot[h] = fmaf(qv.z, kv[j].z, dot[h]);
+        dot[h] = fmaf(qv.w, kv[j].w, dot[h]);
       }
     }
     float sc = 0.f;
 #pragma unroll
     for (int h = 0; h < 4; ++h) sc = fmaf(sq[256 + h], fmaxf(dot[h], 0.f), sc);
-    if (k0 + lane < seg_n) skey[k0 + lane] = order_key(sc);
-    __builtin_amdgcn_wave_barrier();
+    if (bi * 64 + lane < seg_n) skey[bi * 64 + lane] = order_key(sc);
   }
   __syncthreads();
   const size_t cbase = ((size_t)r * n_seg + seg) * p.k;
@@ -296,44 +382,91 @@ __global__ __launch_bounds__(DEC_NT) void index_segment_kernel(IndexParams p, in
   }
   uint32_t kstar;
   int need_eq;
-  radix_threshold<DEC_NT>(get, seg_n, p.k, hist, sh, kstar, need_eq);
-  emit_topk<DEC_NT>(get, seg_n, kstar, need_eq, wsum, [&](int slot, int x, uint32_t u) {
+  radix_threshold<DEC_NT>(get, seg_n, p.k, hist, sh, wsum, kstar, need_eq);
+  emit_topk<DEC_NT>(get, seg_n, kstar, need_eq, wsum, nullptr,
+                    [&](int slot, int x, uint32_t u) {
     cand_key[cbase + slot] = u;
     cand_pos[cbase + slot] = seg_start + x;
   });
 }
 
-__global__ __launch_bounds__(SEL_NT) void index_merge_kernel(IndexParams p, int n_seg,
-                                                             const uint32_t* cand_key,
-                                                             const int32_t* cand_pos) {
-  __shared__ uint32_t hist[256];
+// One reduction level: workgroup (row, group g) takes the candidate lists g*RED_G ..
+// g*RED_G + RED_G - 1 of the previous level (each at most k entries in ascending position, the
+// lists themselves in ascending position order), concatenates them in LDS and keeps their top
+// k, still in ascending position.  The union of the top-k sets of disjoint lists holds the
+// top k of the whole, so levels of RED_G-way reductions end with the row's top k; the last
+// level (one group) writes it to idx_out.  Rows with at most k positions are written there
+// directly (all positions, then -1).
+constexpr int RED_G = 4;
+constexpr int RED_NT = 512;
+constexpr int KMAX = 4096;
+
+__global__ __launch_bounds__(RED_NT) void index_reduce_kernel(IndexParams p, int n_in,
+                                                              const uint32_t* in_key,
+                                                              const int32_t* in_pos,
+                                                              const int* in_cnt,
+                                                              uint32_t* out_key,
+                                                              int32_t* out_pos, int* out_cnt) {
+  __shared__ uint32_t rkey[RED_G * KMAX];
+  __shared__ int32_t rpos[RED_G * KMAX];
+  __shared__ uint32_t hist[(RED_NT / 64) * 256];
   __shared__ int sh[2];
-  __shared__ int wsum[SEL_NT / 64];
-  const int r = blockIdx.x;
+  __shared__ int wsum[2 * RED_NT / 64];
+  const int n_out = (n_in + RED_G - 1) / RED_G;
+  const bool last = n_out == 1;
+  const int r = blockIdx.x / n_out, grp = blockIdx.x % n_out;
   const int b = r / p.Tq, i = r % p.Tq;
   const int t = min(p.pos0[b] + i, min(p.S, p.max_pos + 1) - 1);
   const int n = t >= 0 ? t + 1 : 0;
-  int32_t* out = p.idx_out + (size_t)r * p.k;
-  if (n <= p.k) {
-    for (int j = threadIdx.x; j < p.k; j += SEL_NT) out[j] = j < n ? j : -1;
+  const int k = p.k;
+  int32_t* out = p.idx_out + (size_t)r * k;
+  if (n <= k) {
+    if (last)
+      for (int j = threadIdx.x; j < k; j += RED_NT) out[j] = j < n ? j : -1;
     return;
   }
-  // candidates: every segment but the last contributes exactly k, in ascending position
-  const int segs = (n + SEG - 1) / SEG;
-  const int last_n = n - (segs - 1) * SEG;
-  const int nc = (segs - 1) * p.k + min(p.k, last_n);
-  const uint32_t* ck = cand_key + (size_t)r * n_seg * p.k;
-  const int32_t* cp = cand_pos + (size_t)r * n_seg * p.k;
-  auto get = [&](int x) { return ck[x]; };
+  int total = 0;
+  for (int q = 0; q < RED_G; ++q) {
+    const int li = grp * RED_G + q;
+    if (li >= n_in) break;
+    const size_t src = (size_t)r * n_in + li;
+    const int c = in_cnt[src];
+    for (int x = threadIdx.x; x < c; x += RED_NT) {
+      rkey[total + x] = in_key[src * k + x];
+      rpos[total + x] = in_pos[src * k + x];
+    }
+    total += c;
+  }
+  __syncthreads();
+  const size_t dst = (size_t)r * n_out + grp;
+  if (total <= k) {  // nothing to drop
+    for (int x = threadIdx.x; x < k; x += RED_NT) {
+      if (last) {
+        out[x] = x < total ? rpos[x] : -1;
+      } else if (x < total) {
+        out_key[dst * k + x] = rkey[x];
+        out_pos[dst * k + x] = rpos[x];
+      }
+    }
+    if (!last && threadIdx.x == 0) out_cnt[dst] = total;
+    return;
+  }
+  auto get = [&](int x) { return rkey[x]; };
   uint32_t kstar;
   int need_eq;
-  radix_threshold<SEL_NT>(get, nc, p.k, hist, sh, kstar, need_eq);
-  emit_topk<SEL_NT>(get, nc, kstar, need_eq, wsum,
-                    [&](int slot, int x, uint32_t) { out[slot] = cp[x]; });
+  radix_threshold<RED_NT>(get, total, k, hist, sh, wsum, kstar, need_eq);
+  if (last) {
+    emit_topk<RED_NT>(get, total, kstar, need_eq, wsum, nullptr,
+                      [&](int slot, int x, uint32_t) { out[slot] = rpos[x]; });
+  } else {
+    emit_topk<RED_NT>(get, total, kstar, need_eq, wsum, nullptr,
+                      [&](int slot, int x, uint32_t u) {
+                        out_key[dst * k + slot] = u;
+                        out_pos[dst * k + slot] = rpos[x];
+                      });
+    if (threadIdx.x == 0) out_cnt[dst] = k;
+  }
 }
-
-constexpr size_t SEG_SMEM = (size_t)SEG * 4 + (size_t)4 * 64 * DK_LD * 4 + (4 * 64 + 4) * 4 +
-                            256 * 4 + 2 * 4 + 4 * 4;
 
 bool use_decode_path(const IndexParams& p) { return p.Tq <= 4; }
 
@@ -347,10 +480,22 @@ int n_segments(const IndexParams& p) {
 
 }  // namespace
 
+// Candidate lists of the decode path: level 0 holds the segments' lists, each later level
+// RED_G times fewer; every list has room for k keys, k positions and a count.
+static size_t level_lists(int n_seg) {
+  size_t total = 0;
+  for (int n = n_seg;; n = (n + RED_G - 1) / RED_G) {
+    total += n;
+    if (n == 1) break;
+  }
+  return total;
+}
+
 size_t index_workspace(const IndexParams& p) {
   if (use_decode_path(p)) {
     const size_t rows = (size_t)p.B * p.Tq;
-    return rows * n_segments(p) * p.k * (sizeof(uint32_t) + sizeof(int32_t));
+    const size_t lists = rows * level_lists(n_segments(p));
+    return lists * p.k * (sizeof(uint32_t) + sizeof(int32_t)) + lists * sizeof(int);
   }
   const size_t q_chunk = std::min(p.Tq, 1024);
   return q_chunk * (size_t)key_bound(p) * sizeof(uint32_t);
@@ -359,25 +504,31 @@ size_t index_workspace(const IndexParams& p) {
 hipError_t launch_index(const IndexParams& p, hipStream_t stream) {
   if ((long long)p.B * p.Tq == 0) return hipSuccess;
   if (use_decode_path(p)) {
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)index_segment_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)SEG_SMEM);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
     const int n_seg = n_segments(p);
     const size_t rows = (size_t)p.B * p.Tq;
-    uint32_t* ck = (uint32_t*)p.ws;
-    int32_t* cp = (int32_t*)(ck + rows * n_seg * p.k);
-    hipLaunchKernelGGL(index_segment_kernel, dim3((unsigned)(rows * n_seg)), dim3(DEC_NT),
-                       SEG_SMEM, stream, p, n_seg, ck, cp);
+    const size_t lists = rows * level_lists(n_seg);
+    uint32_t* keys = (uint32_t*)p.ws;
+    int32_t* pos = (int32_t*)(keys + lists * p.k);
+    int* cnt = (int*)(pos + lists * p.k);
+    hipLaunchKernelGGL(index_segment_kernel, dim3((unsigned)(rows * n_seg)), dim3(DEC_NT), 0,
+                       stream, p, n_seg, keys, pos, cnt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(index_merge_kernel, dim3((unsigned)rows), dim3(SEL_NT), 0, stream, p,
-                       n_seg, ck, cp);
-    return hipGetLastError();
+    size_t off = 0;  // lists before the current level
+    for (int n_in = n_seg;;) {
+      const int n_out = (n_in + RED_G - 1) / RED_G;
+      const size_t in_off = off, out_off = off + rows * n_in;
+      hipLaunchKernelGGL(index_reduce_kernel, dim3((unsigned)(rows * n_out)), dim3(RED_NT), 0,
+                         stream, p, n_in, keys + in_off * p.k, pos + in_off * p.k,
+                         cnt + in_off, keys + out_off * p.k, pos + out_off * p.k,
+                         cnt + out_off);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      if (n_out == 1) break;
+      off = out_off;
+      n_in = n_out;
+    }
+    return hipSuccess;
   }
   const long long s_ld = key_bound(p);
   const long long q_chunk = std::min<long long>(p.Tq, (long long)(p.ws_bytes / (s_ld * 4)));

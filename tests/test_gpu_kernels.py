@@ -218,6 +218,22 @@ def test_index_decode(torch, orc, pos0):
     assert same >= 2
 
 
+def test_index_decode_heavy_ties(torch, orc):
+    """Row 0 scores every one of 131072 positions exactly 0 (its indexer query is zero), so
+    every segment's candidates tie at its k-th key and more candidates survive the merge's
+    lower bound than it holds on chip; the lower-index rule alone decides: 0 .. k-1.  Row 1 is
+    an ordinary row over the same keys, checked against the oracle."""
+    S, k = 131072, 2048
+    x = synth.dsa_index(268, B=2, Tq=1, S=S, pos0=[S - 1, S - 1])
+    x["q_idx"][0] = 0.0
+    idx = lgsa.dsa_index_topk(to_dev(x["q_idx"]), to_dev(x["w_idx"]), to_dev(x["k_idx"]),
+                              to_dev(x["pos0"]), k, max_pos=S - 1)
+    torch.cuda.synchronize()
+    g = idx.cpu().numpy()
+    assert g[0, 0].tolist() == list(range(k))
+    assert _check_index(orc, x, g, k, [1]) >= 0
+
+
 # ------------------------------------------------------------------------------ sparse
 @pytest.mark.parametrize("Tq,S,k,distinct_v,gated", [(300, 300, 128, False, True),
                                                      (200, 1000, 96, True, False),
