@@ -17,8 +17,9 @@
 //
 // Data movement.  Key and value tiles (32 rows x 1 KiB) go from global memory to LDS by LDS
 // DMA (global_load_lds_dwordx4: one 1 KiB row per wave instruction), never through registers.
-// Rows are padded (K by 16 bytes, V by 32) so that the fragment reads are bank-conflict free
-// and every fragment address is the lane's base plus an immediate.  V stays row-major; the
+// Rows are padded by 32 bytes so that the fragment reads are bank-conflict free (a 16-byte
+// pad leaves the row-wise K reads conflicting) and every fragment address is the lane's base
+// plus an immediate.  V stays row-major; the
 // MFMA operand V^T is read with the transposing LDS read (ds_read_b64_tr_b16).  V is double
 // buffered; K is single buffered and refilled as soon as the score exchange shows that every
 // wave is done with it, so both loads overlap compute.
@@ -45,7 +46,7 @@ constexpr int D = 512;
 constexpr int HALF = 256;
 constexpr int KT = 32;                 // keys per tile
 constexpr int ROWB = 1024;             // bytes of one 512-wide bf16 row in memory
-constexpr int KLD = ROWB + 16;         // LDS row of a key tile
+constexpr int KLD = ROWB + 32;         // LDS row of a key tile (32-byte pad: no bank conflicts)
 constexpr int VLD = ROWB + 32;         // LDS row of a value tile
 constexpr int KTILE = KT * KLD;
 constexpr int VTILE = KT * VLD;
