@@ -114,6 +114,15 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
 
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Waits until at most N of this wave's vector-memory operations are outstanding (they complete
+// in issue order), leaving the LDS and export counters alone.  s_waitcnt fields: vmcnt in bits
+// 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS reads and writes
 // (lgkmcnt 0), not for its vector-memory loads, so LDS DMA transfers in flight stay in flight
 // (__syncthreads waits for those too).  Use it only where no wave reads LDS that a DMA still in

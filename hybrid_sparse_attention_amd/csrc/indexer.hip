@@ -14,8 +14,8 @@
 // queries at a time, and a 1024-thread workgroup per query selects.
 // Decode (few queries, long context): one workgroup per (query, 16384-position segment)
 // streams its key rows once, scores them with fp32 FMA, selects the segment's top-k in LDS and
-// writes them as a candidate list in ascending position; 4-way reductions of candidate lists
-// (each keeping the top k of four lists) then narrow 64 lists to one (the union of top-k sets
+// writes them as a candidate list in ascending position; 8-way (4-way for k > 2048)
+// reductions of candidate lists (each keeping the top k of its lists) then narrow them to one (the union of top-k sets
 // of disjoint parts contains the top k of the whole, and position order is kept throughout, so
 // the lower-index rule stays exact).
 #include "common.h"
@@ -390,16 +390,18 @@ __global__ __launch_bounds__(DEC_NT) void index_segment_kernel(IndexParams p, in
   });
 }
 
-// One reduction level: workgroup (row, group g) takes the candidate lists g*RED_G ..
-// g*RED_G + RED_G - 1 of the previous level (each at most k entries in ascending position, the
+// One reduction level: workgroup (row, group g) takes the candidate lists g*G .. g*G + G - 1
+// (G = red_g(k)) of the previous level (each at most k entries in ascending position, the
 // lists themselves in ascending position order), concatenates them in LDS and keeps their top
 // k, still in ascending position.  The union of the top-k sets of disjoint lists holds the
-// top k of the whole, so levels of RED_G-way reductions end with the row's top k; the last
+// top k of the whole, so levels of G-way reductions end with the row's top k; the last
 // level (one group) writes it to idx_out.  Rows with at most k positions are written there
 // directly (all positions, then -1).
-constexpr int RED_G = 4;
 constexpr int RED_NT = 512;
-constexpr int KMAX = 4096;
+constexpr int RED_CAP = 16384;  // candidates a reduction holds in LDS: G * k
+
+// lists merged per reduction: eight while eight lists of k fit in LDS, else four
+__host__ __device__ inline int red_g(int k) { return 8 * k <= RED_CAP ? 8 : 4; }
 
 __global__ __launch_bounds__(RED_NT) void index_reduce_kernel(IndexParams p, int n_in,
                                                               const uint32_t* in_key,
@@ -407,12 +409,13 @@ __global__ __launch_bounds__(RED_NT) void index_reduce_kernel(IndexParams p, int
                                                               const int* in_cnt,
                                                               uint32_t* out_key,
                                                               int32_t* out_pos, int* out_cnt) {
-  __shared__ uint32_t rkey[RED_G * KMAX];
-  __shared__ int32_t rpos[RED_G * KMAX];
+  __shared__ uint32_t rkey[RED_CAP];
+  __shared__ int32_t rpos[RED_CAP];
   __shared__ uint32_t hist[(RED_NT / 64) * 256];
   __shared__ int sh[2];
   __shared__ int wsum[2 * RED_NT / 64];
-  const int n_out = (n_in + RED_G - 1) / RED_G;
+  const int G = red_g(p.k);
+  const int n_out = (n_in + G - 1) / G;
   const bool last = n_out == 1;
   const int r = blockIdx.x / n_out, grp = blockIdx.x % n_out;
   const int b = r / p.Tq, i = r % p.Tq;
@@ -426,8 +429,8 @@ __global__ __launch_bounds__(RED_NT) void index_reduce_kernel(IndexParams p, int
     return;
   }
   int total = 0;
-  for (int q = 0; q < RED_G; ++q) {
-    const int li = grp * RED_G + q;
+  for (int q = 0; q < G; ++q) {
+    const int li = grp * G + q;
     if (li >= n_in) break;
     const size_t src = (size_t)r * n_in + li;
     const int c = in_cnt[src];
@@ -481,10 +484,11 @@ int n_segments(const IndexParams& p) {
 }  // namespace
 
 // Candidate lists of the decode path: level 0 holds the segments' lists, each later level
-// RED_G times fewer; every list has room for k keys, k positions and a count.
-static size_t level_lists(int n_seg) {
+// red_g(k) times fewer; every list has room for k keys, k positions and a count.
+static size_t level_lists(int n_seg, int k) {
   size_t total = 0;
-  for (int n = n_seg;; n = (n + RED_G - 1) / RED_G) {
+  const int G = red_g(k);
+  for (int n = n_seg;; n = (n + G - 1) / G) {
     total += n;
     if (n == 1) break;
   }
@@ -494,7 +498,7 @@ static size_t level_lists(int n_seg) {
 size_t index_workspace(const IndexParams& p) {
   if (use_decode_path(p)) {
     const size_t rows = (size_t)p.B * p.Tq;
-    const size_t lists = rows * level_lists(n_segments(p));
+    const size_t lists = rows * level_lists(n_segments(p), p.k);
     return lists * p.k * (sizeof(uint32_t) + sizeof(int32_t)) + lists * sizeof(int);
   }
   const size_t q_chunk = std::min(p.Tq, 1024);
@@ -506,7 +510,7 @@ hipError_t launch_index(const IndexParams& p, hipStream_t stream) {
   if (use_decode_path(p)) {
     const int n_seg = n_segments(p);
     const size_t rows = (size_t)p.B * p.Tq;
-    const size_t lists = rows * level_lists(n_seg);
+    const size_t lists = rows * level_lists(n_seg, p.k);
     uint32_t* keys = (uint32_t*)p.ws;
     int32_t* pos = (int32_t*)(keys + lists * p.k);
     int* cnt = (int*)(pos + lists * p.k);
@@ -516,7 +520,7 @@ hipError_t launch_index(const IndexParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     size_t off = 0;  // lists before the current level
     for (int n_in = n_seg;;) {
-      const int n_out = (n_in + RED_G - 1) / RED_G;
+      const int n_out = (n_in + red_g(p.k) - 1) / red_g(p.k);
       const size_t in_off = off, out_off = off + rows * n_in;
       hipLaunchKernelGGL(index_reduce_kernel, dim3((unsigned)(rows * n_out)), dim3(RED_NT), 0,
                          stream, p, n_in, keys + in_off * p.k, pos + in_off * p.k,

@@ -271,12 +271,13 @@ __global__ __launch_bounds__(64) void sparse_combine_kernel(const float* __restr
   *(uint2*)(out + (size_t)rh * D + 4 * threadIdx.x) = o;
 }
 
-// Enough workgroups to fill the chip (four resident per CU) before a list is split.
+// Enough workgroups to fill the chip before a list is split, but at least four tiles per
+// split: shorter pieces cost more in partial results and merging than they gain.
 void sparse_plan(const SparseParams& p, int& n_split, int& chunk) {
   const long long wgs = (long long)p.B * p.Tq * (p.H / 64);
   const long long target = 1024;
   long long want = wgs >= target ? 1 : (target + wgs - 1) / wgs;
-  const long long max_split = (p.k + KT - 1) / KT;
+  const long long max_split = std::max<long long>(1, p.k / (4 * KT));
   n_split = (int)std::max<long long>(1, std::min(want, max_split));
   long long c = (p.k + n_split - 1) / n_split;
   c = (c + KT - 1) / KT * KT;

@@ -45,7 +45,8 @@ def test_compress(torch, orc, bf16, B, T):
 # ------------------------------------------------------------------------------ gate
 @pytest.mark.parametrize("M,d_lat,N,inplace", [(200, 128, 96, False), (130, 1024, 2048, True),
                                                (8, 1024, 512, False), (600, 1024, 800, True),
-                                               (512, 192, 1024, False)])
+                                               (512, 192, 1024, False), (37, 1024, 1008, True),
+                                               (64, 1024, 4096, False)])
 def test_gate_bf16(torch, orc, M, d_lat, N, inplace):
     ql = synth.normal(210, (M, d_lat), 1.0, True)
     w = synth.normal(211, (d_lat, N), 0.02, True)
