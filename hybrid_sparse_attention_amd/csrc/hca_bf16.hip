@@ -8,21 +8,18 @@
 // closed-form: position t sees compressed entry e iff e < (t + 1) / block, raw position s iff
 // t - window + 1 <= s <= t.
 //
-// On-chip budget for 512-wide heads.  A wave owning 32 query rows over the full head would
-// need 384 of a lane's 512 registers for Q and O alone, so the two waves of a pair share 32
-// rows and split the head dimension: each holds half of Q (64 registers) and half of O (128).
-// Each computes S^T over its half of the dimensions; the partial scores are swapped through
-// LDS and summed (both waves form the same sum, so their softmax is identical), then each
-// accumulates its half of O.
+// On-chip budget for 512-wide heads.  A wave owns 16 query rows over the whole head: Q in 64
+// registers and O in 128, which leaves room for two waves per SIMD (a wave of 32 rows would
+// need 384 registers for Q and O alone).  Each wave forms the full scores of its rows, so no
+// partial results are exchanged between waves.
 //
 // Data movement.  Key and value tiles (32 rows x 1 KiB) go from global memory to LDS by LDS
 // DMA (global_load_lds_dwordx4: one 1 KiB row per wave instruction), never through registers.
-// Rows are padded by 32 bytes so that the fragment reads are bank-conflict free (a 16-byte
-// pad leaves the row-wise K reads conflicting) and every fragment address is the lane's base
-// plus an immediate.  V stays row-major; the
-// MFMA operand V^T is read with the transposing LDS read (ds_read_b64_tr_b16).  V is double
-// buffered; K is single buffered and refilled as soon as the score exchange shows that every
-// wave is done with it, so both loads overlap compute.
+// Rows are padded by 32 bytes so that the fragment reads are bank-conflict free (a 16-byte pad
+// leaves the row-wise K reads conflicting) and every fragment address is the lane's base plus
+// an immediate.  V stays row-major; the MFMA operand V^T is read with the transposing LDS read
+// (ds_read_b64_tr_b16).  K and V are both double buffered: tile ti + 1 streams in while tile
+// ti is used, with one workgroup barrier per tile.
 //
 // Products on v_mfma_f32_16x16x32_bf16, transposed (S^T = K Q^T, O^T = V^T P^T): the tile in
 // LDS is the A operand, the query rows in registers the B operand; a lane owns one query row
@@ -30,11 +27,10 @@
 // of the first (the two transposed reads pick the key rows that lane group's accumulator
 // holds, so no data moves between lanes).
 //
-// Prefill: one workgroup of 8 waves (4 pairs) per (32 query tokens, 4 heads); all pairs see
-// the same masks.  Decode: one workgroup of 4 waves (2 pairs = 64 heads of one token) per
-// (sequence, key split); partial (max, sum, O) of a split go to the workspace and a combine
-// kernel merges them.  When gated, the gate GEMM then multiplies sigmoid(q_lat W) into O in
-// place.
+// Prefill: one workgroup of 8 waves per (32 query tokens, 4 heads).  Decode: one workgroup of
+// 4 waves (the 64 heads of one token) per (sequence, key split); partial (max, sum, O) of a
+// split go to the workspace and a combine kernel merges them.  When gated, the gate GEMM then
+// multiplies sigmoid(q_lat W) into O in place.
 #include "common.h"
 #include "kernels.h"
 
@@ -43,7 +39,6 @@ namespace lgsa {
 namespace {
 
 constexpr int D = 512;
-constexpr int HALF = 256;
 constexpr int KT = 32;                 // keys per tile
 constexpr int ROWB = 1024;             // bytes of one 512-wide bf16 row in memory
 constexpr int KLD = ROWB + 32;         // LDS row of a key tile (32-byte pad: no bank conflicts)
@@ -120,140 +115,9 @@ __device__ __forceinline__ bool tile_full(const Tile& t, int t_lo, int t_hi, int
   return t.start + KT - 1 <= t_lo && t.start >= t_hi - window + 1;
 }
 
-// Per-wave state: 32 query rows (column blocks nb = 0, 1), one half of the head dimension.
-struct HalfState {
-  f32x4_t o[16][2];  // o[cb][nb][r] = O[row 16nb + l16][hf*256 + 16cb + 4g + r]
-  float m[2];        // reference max (log2 domain): p = 2^(x - m) <= 2^LAZY
-  float l[2];        // running partial sum of this lane's keys
-};
-
-__device__ __forceinline__ void init_state(HalfState& st) {
-#pragma unroll
-  for (int cb = 0; cb < 16; ++cb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) st.o[cb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  st.m[0] = st.m[1] = NEG_BIG;
-  st.l[0] = st.l[1] = 0.f;
-}
-
-// S^T over this wave's half of the head dimension: row 16mb + l16 of the key tile, chunk
-// hf*32 + 4kk + g -> base + 64kk + 16*KLD*mb.
-__device__ __forceinline__ void partial_scores(f32x4_t (&s)[2][2], const Frag8 (&qf)[2][8],
-                                               const char* ks, int hf, int lane) {
-  const int l16 = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) s[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const char* a0 = ks + l16 * KLD + 16 * (hf * 32 + g);
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    Frag8 ka[2];
-    ka[0].u = *(const uint4*)(a0 + 64 * kk);
-    ka[1].u = *(const uint4*)(a0 + 64 * kk + 16 * KLD);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) s[mb][nb] = mfma_16x16x32(ka[mb], qf[nb][kk], s[mb][nb]);
-  }
-}
-
-// Online softmax of the full scores (masked unless the tile is fully visible) and
-// O-half += V-half^T P^T.
-__device__ __forceinline__ void softmax_pv(HalfState& st, const f32x4_t (&s)[2][2],
-                                           const char* vs, const Tile& t, const RowPos& rp,
-                                           float scale_log2, int hf, int lane) {
-  const int l16 = lane & 15, g = lane >> 4;
-  float x[2][2][4];  // [nb][mb][r]
-  if (t.full) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x[nb][mb][r] = s[mb][nb][r] * scale_log2;
-  } else {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int tr = row_t(rp, 16 * nb + opaque(l16));
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          x[nb][mb][r] = visible(t, 16 * mb + 4 * g + r, tr, rp) ? s[mb][nb][r] * scale_log2
-                                                                 : NEG_BIG;
-    }
-  }
-  float m_new[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    float mx = x[nb][0][0];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[nb][mb][r]);
-    mx = wave_max16(mx);
-    m_new[nb] = fmaxf(st.m[nb], mx);
-  }
-  // lazy rescale: keep the reference max unless some row's max grew by more than LAZY
-  if (__any((m_new[0] > st.m[0] + LAZY) | (m_new[1] > st.m[1] + LAZY))) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const float alpha = fast_exp2(st.m[nb] - m_new[nb]);
-      st.m[nb] = m_new[nb];
-      st.l[nb] *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < 16; ++cb) st.o[cb][nb] *= alpha;
-    }
-  }
-  Frag8 pf[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    float p[2][4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[mb][r] = fast_exp2(x[nb][mb][r] - st.m[nb]);
-        st.l[nb] += p[mb][r];
-      }
-    pf[nb].u = make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
-                          pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3]));
-  }
-  // V^T fragment of column block cb: transposed reads of rows 4g + a (slots 8g..8g+3) and
-  // 16 + 4g + a (slots 8g+4..8g+7), a = l16 / 4, columns hf*256 + 16cb + 4(l16 % 4) + 0..3.
-  const char* v0 = vs + (4 * g + (l16 >> 2)) * VLD + hf * (2 * HALF) + 8 * (l16 & 3);
-#pragma unroll
-  for (int cb = 0; cb < 16; ++cb) {
-    Frag8 va;
-    const uint2 lo = lds_read_tr16(v0 + 32 * cb);
-    const uint2 hi = lds_read_tr16(v0 + 32 * cb + 16 * VLD);
-    va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) st.o[cb][nb] = mfma_16x16x32(va, pf[nb], st.o[cb][nb]);
-  }
-}
-
 // 1 / l for the final normalisation; 0 for a row that never saw a visible key
 __device__ __forceinline__ float final_scale(float m, float l_total) {
   return (m > 0.5f * NEG_BIG && l_total > 0.f) ? 1.f / l_total : 0.f;
-}
-
-// partial scores are swapped through LDS: xs[wave][q][lane] f32x4, q = mb * 2 + nb
-__device__ __forceinline__ void xs_write(char* xs, int wave, int lane, const f32x4_t (&s)[2][2]) {
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      *(f32x4_t*)(xs + ((wave * 4 + mb * 2 + nb) * 64 + lane) * 16) = s[mb][nb];
-}
-
-__device__ __forceinline__ void xs_add(const char* xs, int wave, int lane, f32x4_t (&s)[2][2]) {
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      s[mb][nb] += *(const f32x4_t*)(xs + ((wave * 4 + mb * 2 + nb) * 64 + lane) * 16);
 }
 
 __device__ __forceinline__ void store4(uint16_t* dst, const f32x4_t& v) {
@@ -263,64 +127,10 @@ __device__ __forceinline__ void store4(uint16_t* dst, const f32x4_t& v) {
   *(uint2*)dst = r;
 }
 
-// LDS of both kernels: the K tile, two V stages and the score exchange, each its own LDS
-// object.  Every access below names its object directly (the key loop is unrolled by two so
-// that the V stage is known statically): the compiler can then prove that the reads of K, V_ti
-// and the exchange do not overlap the LDS DMA into V_{ti+1} or the refill of K, and does not
-// wait for those transfers before reading, which is what lets them overlap the products.
-constexpr int XS_BYTES = 8 * 4 * 64 * 16;  // 8 waves x 4 fragments x 64 lanes x 16 bytes
-__shared__ __attribute__((aligned(1024))) char hca_k[KTILE];
-__shared__ __attribute__((aligned(1024))) char hca_v0[VTILE];
-__shared__ __attribute__((aligned(1024))) char hca_v1[VTILE];
-__shared__ __attribute__((aligned(1024))) char hca_xs[XS_BYTES];
-
-// The key loop shared by prefill and decode.  Per tile ti (V stage ti & 1):
-//   barrier A: K_ti and V_ti are in LDS;  DMA V_{ti+1} into the other V stage;
-//   partial scores from K, written to the exchange;  barrier B: every wave is done with K;
-//   DMA K_{ti+1};  add the partner's partial scores;  softmax;  PV from V_ti;  drain own DMA.
-template <class TileOf>
-__device__ __forceinline__ void key_loop(HalfState& st, const Frag8 (&qf)[2][8],
-                                         const RowPos& rp, const Src& src,
-                                         const TileOf& tile_of, int n_tiles, int wave,
-                                         int n_waves, int hf, int lane, float scale_log2) {
-  if (n_tiles > 0) {
-    const Tile t0 = tile_of(0);
-    dma_rows(src, t0, false, hca_k, KLD, wave, n_waves, lane);
-    dma_rows(src, t0, true, hca_v0, VLD, wave, n_waves, lane);
-  }
-  wait_all();
-  __syncthreads();
-  auto body = [&](int ti, const char* vcur, char* vnxt) {
-    const Tile t = tile_of(ti);
-    const bool more = ti + 1 < n_tiles;
-    Tile tn;
-    if (more) {
-      tn = tile_of(ti + 1);
-      dma_rows(src, tn, true, vnxt, VLD, wave, n_waves, lane);
-    }
-    f32x4_t s[2][2];
-    partial_scores(s, qf, hca_k, hf, lane);
-    xs_write(hca_xs, wave, lane, s);
-    lds_barrier();  // the exchange is written and K is read; the V DMA stays in flight
-    if (more) dma_rows(src, tn, false, hca_k, KLD, wave, n_waves, lane);
-    xs_add(hca_xs, wave ^ 1, lane, s);
-    softmax_pv(st, s, vcur, t, rp, scale_log2, hf, lane);
-    wait_all();
-    __syncthreads();
-  };
-  for (int ti = 0; ti < n_tiles; ti += 2) {
-    body(ti, hca_v0, hca_v1);
-    if (ti + 1 < n_tiles) body(ti + 1, hca_v1, hca_v0);
-  }
-}
-
-// ------------------------------------------------------------------------------- prefill
-// One workgroup of 8 waves per (32 query tokens, 4 heads); wave w owns head 4 * hg + (w & 3)
-// for rows 16 * (w >> 2) .. +15 of the token tile over the whole head dimension: Q in 64
-// registers, O in 128, two waves per SIMD.  No partial scores are exchanged; K and V tiles are
-// both double buffered, so one barrier per tile remains.  Workgroups are ordered XCD-aware:
-// consecutive ids go to different XCDs (round robin), so the head groups of one token tile get
-// ids that share an XCD and its key tiles are served from that XCD's L2.
+// ------------------------------------------------------------------------- the key loop
+// A wave owns 16 query rows over the whole head dimension: Q in 64 registers, O in 128.  No
+// partial scores are exchanged; K and V tiles are both double buffered, so one barrier per
+// tile remains.
 struct RowState {
   f32x4_t o[32];  // o[cb][r] = O[row l16][16cb + 4g + r]
   float m;        // reference max (log2 domain): p = 2^(x - m) <= 2^LAZY
@@ -407,6 +217,53 @@ __device__ __forceinline__ void row_softmax_pv(RowState& st, const f32x4_t (&s)[
   }
 }
 
+// Key loop shared by prefill and decode, unrolled by two so that every LDS access names its
+// buffer: tile ti is read from (k0, v0) or (k1, v1) while tile ti + 1 streams into the other
+// pair by LDS DMA.  The four buffers are separate LDS objects: the compiler can then prove that
+// reading one pair does not touch the transfers into the other and does not wait for them.
+template <class TileOf>
+__device__ __forceinline__ void row_key_loop(RowState& st, const Frag8 (&qf)[16],
+                                             const RowPos& rp, const Src& src,
+                                             const TileOf& tile_of, int n_tiles, int wave,
+                                             int n_waves, int lane, float scale_log2) {
+  if (n_tiles > 0) {
+    const Tile t0 = tile_of(0);
+    dma_rows(src, t0, false, pf_k0, KLD, wave, n_waves, lane);
+    dma_rows(src, t0, true, pf_v0, VLD, wave, n_waves, lane);
+  }
+  wait_all();
+  __syncthreads();
+  auto body = [&](int ti, const char* kcur, const char* vcur, char* knxt, char* vnxt) {
+    const Tile t = tile_of(ti);
+    if (ti + 1 < n_tiles) {
+      const Tile tn = tile_of(ti + 1);
+      dma_rows(src, tn, false, knxt, KLD, wave, n_waves, lane);
+      dma_rows(src, tn, true, vnxt, VLD, wave, n_waves, lane);
+    }
+    f32x4_t s[2];
+    row_scores(s, qf, kcur, lane);
+    row_softmax_pv(st, s, vcur, t, rp, scale_log2, lane);
+    wait_all();  // this wave's transfers of tile ti + 1 have landed
+    __syncthreads();
+  };
+  for (int ti = 0; ti < n_tiles; ti += 2) {
+    body(ti, pf_k0, pf_v0, pf_k1, pf_v1);
+    if (ti + 1 < n_tiles) body(ti + 1, pf_k1, pf_v1, pf_k0, pf_v0);
+  }
+}
+
+__device__ __forceinline__ void init_row_state(RowState& st) {
+#pragma unroll
+  for (int cb = 0; cb < 32; ++cb) st.o[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = NEG_BIG;
+  st.l = 0.f;
+}
+
+// ------------------------------------------------------------------------------- prefill
+// One workgroup of 8 waves per (32 query tokens, 4 heads); wave w owns head 4 * hg + (w & 3)
+// for rows 16 * (w >> 2) .. +15 of the token tile.  Workgroups are ordered XCD-aware:
+// consecutive ids go to different XCDs (round robin), so the head groups of one token tile get
+// ids that share an XCD and its key tiles are served from that XCD's L2.
 __global__ __launch_bounds__(512, 1) void hca_prefill_kernel(HcaParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -476,38 +333,8 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_kernel(HcaParams p) {
     for (int kk = 0; kk < 16; ++kk) qf[kk].u = *(const uint4*)(qr + 32 * kk + 8 * g);
   }
   RowState st;
-#pragma unroll
-  for (int cb = 0; cb < 32; ++cb) st.o[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  st.m = NEG_BIG;
-  st.l = 0.f;
-  const float scale_log2 = p.scale * LOG2E;
-
-  // Key loop, unrolled by two so that every LDS access names its buffer: tile ti is read from
-  // (k0, v0) or (k1, v1) while tile ti + 1 streams into the other pair by LDS DMA.
-  if (n_tiles > 0) {
-    const Tile t0 = tile_of(0);
-    dma_rows(src, t0, false, pf_k0, KLD, wave, 8, lane);
-    dma_rows(src, t0, true, pf_v0, VLD, wave, 8, lane);
-  }
-  wait_all();
-  __syncthreads();
-  auto body = [&](int ti, const char* kcur, const char* vcur, char* knxt, char* vnxt) {
-    const Tile t = tile_of(ti);
-    if (ti + 1 < n_tiles) {
-      const Tile tn = tile_of(ti + 1);
-      dma_rows(src, tn, false, knxt, KLD, wave, 8, lane);
-      dma_rows(src, tn, true, vnxt, VLD, wave, 8, lane);
-    }
-    f32x4_t s[2];
-    row_scores(s, qf, kcur, lane);
-    row_softmax_pv(st, s, vcur, t, rp, scale_log2, lane);
-    wait_all();  // this wave's transfers of tile ti + 1 have landed
-    __syncthreads();
-  };
-  for (int ti = 0; ti < n_tiles; ti += 2) {
-    body(ti, pf_k0, pf_v0, pf_k1, pf_v1);
-    if (ti + 1 < n_tiles) body(ti + 1, pf_k1, pf_v1, pf_k0, pf_v0);
-  }
+  init_row_state(st);
+  row_key_loop(st, qf, rp, src, tile_of, n_tiles, wave, 8, lane, p.scale * LOG2E);
 
   const int i = r_first + l16;
   const float inv = final_scale(st.m, wave_sum16(st.l));
@@ -519,15 +346,14 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_kernel(HcaParams p) {
 }
 
 // ------------------------------------------------------------------------------- decode
-// One workgroup of 4 waves = 2 pairs (heads 0..31, 32..63 of a 64-head group) per
-// (sequence, key split).  Keys of a sequence: compressed entries 0..ne-1, then raw positions
-// s_lo..t; all rows are at position t.
+// One workgroup of 4 waves (16 heads each: the 64 heads of a group) per (sequence, key split).
+// Keys of a sequence: compressed entries 0..ne-1, then raw positions s_lo..t; every row is at
+// position t.  A split writes its partial (max, sum, O) unless it is the only one.
 __global__ __launch_bounds__(256, 1) void hca_decode_kernel(HcaParams p, int n_split, int chunk,
                                                             float* part_o, float* part_ml) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const int pair = wave >> 1, hf = wave & 1;
   const int n_hg = p.H / 64;
   const int hg = blockIdx.x % n_hg;
   const int sp = (blockIdx.x / n_hg) % n_split;
@@ -564,55 +390,41 @@ __global__ __launch_bounds__(256, 1) void hca_decode_kernel(HcaParams p, int n_s
   src.vw = (const char*)p.v_win + (size_t)b * p.win_len * ROWB;
   src.win_len = p.win_len;
 
-  const int h0 = hg * 64 + 32 * pair;
+  const int h = hg * 64 + 16 * wave + l16;  // this lane's head (MFMA column)
   RowPos rp;
   rp.t0 = t;
-  rp.n_rows = 32;
+  rp.n_rows = 16;
   rp.step = 0;
   rp.window = p.window;
   rp.block = p.block;
-  Frag8 qf[2][8];
-  const uint16_t* qb = (const uint16_t*)p.q + (size_t)b * p.H * D;
+  Frag8 qf[16];
+  {
+    const uint16_t* qr = (const uint16_t*)p.q + ((size_t)b * p.H + h) * D;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const uint16_t* qr = qb + (size_t)(h0 + 16 * nb + l16) * D + hf * HALF;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[nb][kk].u = *(const uint4*)(qr + 32 * kk + 8 * g);
+    for (int kk = 0; kk < 16; ++kk) qf[kk].u = *(const uint4*)(qr + 32 * kk + 8 * g);
   }
-  HalfState st;
-  init_state(st);
-  key_loop(st, qf, rp, src, tile_of, tiles_c + tiles_w, wave, 4, hf, lane, p.scale * LOG2E);
+  RowState st;
+  init_row_state(st);
+  row_key_loop(st, qf, rp, src, tile_of, tiles_c + tiles_w, wave, 4, lane, p.scale * LOG2E);
 
-  float lt[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) lt[nb] = wave_sum16(st.l[nb]);
+  const float lt = wave_sum16(st.l);
   if (n_split == 1) {
-    uint16_t* out = (uint16_t*)p.out + (size_t)b * p.H * D;
+    const float inv = final_scale(st.m, lt);
+    uint16_t* orow = (uint16_t*)p.out + ((size_t)b * p.H + h) * D;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const float inv = final_scale(st.m[nb], lt[nb]);
-      uint16_t* orow = out + (size_t)(h0 + 16 * nb + l16) * D + hf * HALF;
-#pragma unroll
-      for (int cb = 0; cb < 16; ++cb) store4(orow + 16 * cb + 4 * g, st.o[cb][nb] * inv);
-    }
+    for (int cb = 0; cb < 32; ++cb) store4(orow + 16 * cb + 4 * g, st.o[cb] * inv);
     return;
   }
+  const size_t pr = ((size_t)b * n_split + sp) * p.H + h;
+  float* po = part_o + pr * D;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int hh = h0 + 16 * nb + l16;
-    const size_t pr = ((size_t)b * n_split + sp) * p.H + hh;
-    float* po = part_o + pr * D + hf * HALF;
-#pragma unroll
-    for (int cb = 0; cb < 16; ++cb) *(f32x4_t*)(po + 16 * cb + 4 * g) = st.o[cb][nb];
-    if (g == 0 && hf == 0) {
-      part_ml[pr * 2 + 0] = st.m[nb];
-      part_ml[pr * 2 + 1] = lt[nb];
-    }
+  for (int cb = 0; cb < 32; ++cb) *(f32x4_t*)(po + 16 * cb + 4 * g) = st.o[cb];
+  if (g == 0) {
+    part_ml[pr * 2 + 0] = st.m;
+    part_ml[pr * 2 + 1] = lt;
   }
 }
 
-// Merge of the key splits of one (sequence, head):
-//   O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
 __global__ __launch_bounds__(128) void hca_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           uint16_t* __restrict__ out, int H,

@@ -14,8 +14,8 @@
 // queries at a time, and a 1024-thread workgroup per query selects.
 // Decode (few queries, long context): one workgroup per (query, 16384-position segment)
 // streams its key rows once, scores them with fp32 FMA, selects the segment's top-k in LDS and
-// writes them as a candidate list in ascending position; 8-way (4-way for k > 2048)
-// reductions of candidate lists (each keeping the top k of its lists) then narrow them to one (the union of top-k sets
+// writes them as a candidate list in ascending position; 4-way reductions of candidate lists
+// (each keeping the top k of its four lists) then narrow them to one (the union of top-k sets
 // of disjoint parts contains the top k of the whole, and position order is kept throughout, so
 // the lower-index rule stays exact).
 #include "common.h"
@@ -400,8 +400,8 @@ __global__ __launch_bounds__(DEC_NT) void index_segment_kernel(IndexParams p, in
 constexpr int RED_NT = 512;
 constexpr int RED_CAP = 16384;  // candidates a reduction holds in LDS: G * k
 
-// lists merged per reduction: eight while eight lists of k fit in LDS, else four
-__host__ __device__ inline int red_g(int k) { return 8 * k <= RED_CAP ? 8 : 4; }
+// lists merged per reduction (eight-way levels measured slower: fewer, longer workgroups)
+__host__ __device__ inline int red_g(int) { return 4; }
 
 __global__ __launch_bounds__(RED_NT) void index_reduce_kernel(IndexParams p, int n_in,
                                                               const uint32_t* in_key,

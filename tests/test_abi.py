@@ -163,9 +163,9 @@ def test_index_workspace(lib):
     assert _call(lib, "dsa_index_topk", a) == lgsa.LGSA_EWORKSPACE
     d = _idx(B=8, Tq=1, S=1 << 20, max_pos=(1 << 20) - 1)
     assert lib.dsa_index_topk_workspace(ctypes.byref(d), ctypes.byref(n)) == 0
-    # decode: candidate lists of 64 segments of 16384 positions, then of the 8-way
-    # reductions (8, 1 lists); each list holds k keys, k positions and a count
-    lists = 8 * (64 + 8 + 1)
+    # decode: candidate lists of 64 segments of 16384 positions, then of the 4-way
+    # reductions (16, 4, 1 lists); each list holds k keys, k positions and a count
+    lists = 8 * (64 + 16 + 4 + 1)
     assert n.value == lists * 2048 * 8 + lists * 4
 
 
