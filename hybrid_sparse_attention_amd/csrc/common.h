@@ -81,8 +81,10 @@ __device__ __forceinline__ void transpose8x8(const uint4 r[8], uint4 c[8]) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float sigmoidf_fast(float g) {
-  // 1 / (1 + e^-g) with e^-g = 2^(-g * log2 e)
-  return 1.0f / (1.0f + fast_exp2(-g * 1.4426950408889634f));
+  // 1 / (1 + e^-g) with e^-g = 2^(-g * log2 e); the hardware reciprocal (about 1 ulp) instead
+  // of a correctly rounded division: the factor multiplies a bfloat16 value.  1 + e^-g = inf
+  // gives 0, as it should.
+  return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-g * 1.4426950408889634f));
 }
 
 }  // namespace lgsa

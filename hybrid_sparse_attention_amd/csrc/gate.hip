@@ -7,7 +7,8 @@
 //   - gate_bf16_big_kernel (M and N >= 256, the prefill shapes): 256 x 256 tiles fed by LDS
 //     DMA, W read through the transposing LDS read, tiles ordered so that the workgroups
 //     resident on one XCD share their q_lat and W tiles in that XCD's L2; the epilogue stages
-//     the fp32 gate factors in LDS and streams o and out with 16-byte accesses.
+//     the fp32 gate factors in LDS and streams o and out with 16-byte non-temporal accesses,
+//     which pass through L2 without displacing those shared tiles.
 //   - gate_bf16_kernel (small M or N, e.g. decode): 128 x 128 tiles, the W tile transposed
 //     while it is staged in LDS through registers, four waves of 64 x 64, K staged 64 at a
 //     time in double-buffered LDS; the lane multiplies its four channels into o and stores
@@ -22,6 +23,20 @@ namespace lgsa {
 namespace {
 
 constexpr int GT_N = 128, GT_M = 128, GT_K = 64, GT_LD = GT_K + 8;  // LDS row: 72 bf16
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte global accesses with the non-temporal cache policy: a stream touched once (o and
+// out, 4 bytes per output element) then goes through L2 without evicting the operand tiles
+// that the workgroups of an XCD share.
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+  const u32x4_t t = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ void store16_nt(void* p, uint4 v) {
+  const u32x4_t t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, (u32x4_t*)p);
+}
 
 __global__ __launch_bounds__(256) void gate_bf16_kernel(const uint16_t* __restrict__ ql,
                                                         const uint16_t* __restrict__ w,
@@ -276,7 +291,7 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_big_kernel(const uint16_t* _
     for (int u = 0; u < 8; ++u) {
       int blk, rr, m, n;
       chunk_mn(hl, u, blk, rr, m, n);
-      ov[hl][u] = *(const uint4*)(o + (size_t)min(m, M - 1) * N + min(n, N - 8));
+      ov[hl][u] = load16_nt(o + (size_t)min(m, M - 1) * N + min(n, N - 8));
     }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -311,7 +326,7 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_big_kernel(const uint16_t* _
                         __uint_as_float(x.z & 0xFFFF0000u) * f1[1]);
       r.w = pack_bf16x2(__uint_as_float(x.w << 16) * f1[2],
                         __uint_as_float(x.w & 0xFFFF0000u) * f1[3]);
-      if (m < M && n < N) *(uint4*)(out + (size_t)m * N + n) = r;
+      if (m < M && n < N) store16_nt(out + (size_t)m * N + n, r);
     }
     lds_barrier();
   }
