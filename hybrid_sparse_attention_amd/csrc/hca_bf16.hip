@@ -74,15 +74,28 @@ struct Src {
   }
 };
 
-// The calling wave DMAs rows r0, r0 + step, ... of one tile (K or V).  The row address is
-// wave-uniform and the lane adds a 32-bit offset made opaque at the point of use, so no 64-bit
-// per-lane pointer is kept live across the key loop (the instruction takes the scalar base).
+// The calling wave DMAs rows KT / n_waves * wave .. of one tile (K or V), a run of consecutive
+// rows.  A full tile that does not wrap the window ring is consecutive in memory too: one
+// wave-uniform base then serves all the wave's rows through immediate offsets, and the lane
+// adds a 32-bit offset made opaque at the point of use, so no per-lane pointer stays live
+// across the key loop.  Other tiles (the last, partial one, or one that wraps the ring) form
+// each row's address separately.
 __device__ __forceinline__ void dma_rows(const Src& src, const Tile& t, bool is_v, char* dst,
-                                         int ld, int r0, int step, int lane) {
+                                         int ld, int wave, int n_waves, int lane) {
   const char* base = t.kind == 0 ? (is_v ? src.vc : src.kc) : (is_v ? src.vw : src.kw);
-  for (int j = r0; j < KT; j += step) {
-    const char* rowp = base + src.row(t, j) * ROWB;
-    lds_dma16(rowp + (uint32_t)opaque(16 * lane), dst + j * ld);
+  const int n = KT / n_waves;  // rows per wave
+  const int j0 = wave * n;
+  if (t.count == KT && (t.kind == 0 || t.row0 + KT <= src.win_len)) {
+    const char* rowp = base + (size_t)(t.row0 + j0) * ROWB;
+    const uint32_t lo = (uint32_t)opaque(16 * lane);
+#pragma unroll
+    for (int u = 0; u < n; ++u) lds_dma16(rowp + u * ROWB + lo, dst + (j0 + u) * ld);
+  } else {
+#pragma unroll
+    for (int u = 0; u < n; ++u) {
+      const char* rowp = base + src.row(t, j0 + u) * ROWB;
+      lds_dma16(rowp + (uint32_t)opaque(16 * lane), dst + (j0 + u) * ld);
+    }
   }
 }
 
