@@ -276,6 +276,57 @@ def run_c4(torch, lgsa, synth, to_dev, iters):
                 bytes=hbytes + ibytes + sbytes, index_bytes=ibytes)
 
 
+def run_append(torch, lgsa, synth, to_dev, iters):
+    """Decode-time cache appends at the decode workloads' shapes: the HCA append for 64
+    sequences (ring of 128 rows, 1024 entries, d 512, bf16) at a block's last token, which also
+    writes the block's entry, and mid-block; the DSA append for 8 sequences (indexer key 64 fp32,
+    latent row 256 bf16, 1M positions)."""
+    B, d, W, n_cap = 64, 512, 128, 1024
+    kw = to_dev(synth.normal(50, (B, W, d), 1.0, True))
+    vw = to_dev(synth.normal(51, (B, W, d), 1.0, True))
+    kc = torch.zeros((B, n_cap, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    kn = to_dev(synth.normal(52, (B, d), 1.0, True))
+    vn = to_dev(synth.normal(53, (B, d), 1.0, True))
+    Bd, S = 8, 1 << 20
+    ki = torch.zeros((Bd, S, 64), dtype=torch.float32, device="cuda")
+    kv = torch.zeros((Bd, S, 256), dtype=torch.bfloat16, device="cuda")
+    kin = to_dev(synth.normal(54, (Bd, 64)))
+    kvn = to_dev(synth.normal(55, (Bd, 256), 1.0, True))
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    tm = Timer(torch, torch.cuda.current_stream())
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(iters):
+            flush_cache(torch, flush)
+            a = tm.event()
+            fn()
+            b = tm.event()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return float(np.median(ms))
+
+    res = {}
+    for name, t in (("hca_block_end", 131071), ("hca_mid_block", 131070)):
+        pos = torch.full((B,), t, dtype=torch.int32, device="cuda")
+        ms = timed(lambda: lgsa.hca_cache_append(pos, kn, vn, kw, vw, kc, vc))
+        # new rows read + ring rows written; at a block's end also the block's other rows read
+        # and the entry written
+        nbytes = 2 * B * d * 2 * 2 + (2 * B * (W - 1) * d * 2 + 2 * B * d * 2 if t % 128 == 127
+                                      else 0)
+        res[name] = dict(us=round(ms * 1e3, 2), bytes=nbytes,
+                         GBps=round(nbytes / (ms * 1e-3) / 1e9, 1))
+    posd = torch.full((Bd,), S - 1, dtype=torch.int32, device="cuda")
+    ms = timed(lambda: lgsa.dsa_cache_append(posd, kin, ki, kvn, kv))
+    nbytes = 2 * Bd * (64 * 4 + 256 * 2)
+    res["dsa"] = dict(us=round(ms * 1e3, 2), bytes=nbytes,
+                      GBps=round(nbytes / (ms * 1e-3) / 1e9, 1))
+    return res
+
+
 # --------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(x, budget_s=15.0):
     """The fp64 oracle on a bounded, evenly spread sample of query rows of the C1 workload."""
@@ -382,6 +433,8 @@ def main():
                                           GBps=round(gbps, 1),
                                           hbm_frac=round(gbps / PEAK_HBM_GBPS, 4),
                                           bytes=r2["bytes"])
+    if 2 in cfgs or 4 in cfgs:
+        secondary["decode_cache_append"] = run_append(torch, lgsa, synth, to_dev, 50)
     if 3 in cfgs:
         r3 = run_c3(torch, lgsa, synth, to_dev, 3)
         sp_tf = r3["sparse_flops"] / (r3["sparse_ms"] * 1e-3) / 1e12

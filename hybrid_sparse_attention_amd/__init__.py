@@ -22,7 +22,8 @@ LGSA_F32, LGSA_BF16 = 0, 1
 
 EXPORTS = ["lgsa_last_error", "hca_compress", "latent_gate", "hca_attn_fwd",
            "hca_attn_fwd_workspace", "dsa_index_topk", "dsa_index_topk_workspace",
-           "sparse_attn_fwd", "sparse_attn_fwd_workspace"]
+           "sparse_attn_fwd", "sparse_attn_fwd_workspace", "hca_cache_append",
+           "dsa_cache_append"]
 
 
 class LibraryMissing(RuntimeError):
@@ -61,6 +62,18 @@ class SparseArgs(ctypes.Structure):
                 ("workspace", _P), ("workspace_bytes", _SZ)]
 
 
+class HcaAppendArgs(ctypes.Structure):
+    _fields_ = [("dt", _I), ("B", _I), ("d", _I), ("pos", _P), ("k_new", _P), ("v_new", _P),
+                ("k_win", _P), ("v_win", _P), ("win_len", _I), ("kc", _P), ("vc", _P),
+                ("n_cap", _I), ("block", _I)]
+
+
+class DsaAppendArgs(ctypes.Structure):
+    _fields_ = [("dt", _I), ("B", _I), ("S", _I), ("pos", _P), ("k_idx_new", _P),
+                ("k_idx", _P), ("di", _I), ("kv_new", _P), ("kv_lat", _P), ("row", _I),
+                ("kv_row_stride", _LL)]
+
+
 _lib = None
 
 
@@ -81,6 +94,8 @@ def load():
             getattr(lib, name).argtypes = [ctypes.POINTER(st), _P]
             getattr(lib, name + "_workspace").argtypes = [ctypes.POINTER(st),
                                                           ctypes.POINTER(_SZ)]
+        lib.hca_cache_append.argtypes = [ctypes.POINTER(HcaAppendArgs), _P]
+        lib.dsa_cache_append.argtypes = [ctypes.POINTER(DsaAppendArgs), _P]
         for name in EXPORTS[1:]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
@@ -292,3 +307,38 @@ def sparse_attn_fwd(q, k_lat, idx, v_lat=None, *, scale=None, q_lat=None, w_gate
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("sparse_attn_fwd", load().sparse_attn_fwd(ctypes.byref(a), _stream(stream)))
     return out
+
+
+def hca_cache_append(pos, k_new, v_new, k_win, v_win, kc=None, vc=None, *, block=128,
+                     stream=None):
+    """Decode-time HCA cache update for each sequence's new token at position pos[b]: ring rows
+    k_win / v_win [B,win_len,d] and, on a block's last token, the entry kc / vc [B,n_cap,d]
+    (updated in place); see include/lgsa.h."""
+    B, d = k_new.shape
+    a = HcaAppendArgs()
+    a.dt = _dt(k_new)
+    a.B, a.d = B, d
+    a.pos = _dev(pos, "pos")
+    a.k_new, a.v_new = _dev(k_new, "k_new"), _dev(v_new, "v_new")
+    a.k_win, a.v_win = _dev(k_win, "k_win"), _dev(v_win, "v_win")
+    a.win_len = k_win.shape[1]
+    a.kc, a.vc = _dev(kc, "kc"), _dev(vc, "vc")
+    a.n_cap = 0 if kc is None else kc.shape[1]
+    a.block = block
+    _check("hca_cache_append", load().hca_cache_append(ctypes.byref(a), _stream(stream)))
+
+
+def dsa_cache_append(pos, k_idx_new, k_idx, kv_new, kv_lat, stream=None):
+    """Decode-time DSA cache append: k_idx[b,pos[b]] = k_idx_new[b] ([B,S,di] fp32) and
+    kv_lat[b,pos[b],:row] = kv_new[b] (kv_lat [B,S,stride]), in place; see include/lgsa.h."""
+    B, di = k_idx_new.shape
+    a = DsaAppendArgs()
+    a.dt = _dt(kv_new)
+    a.B, a.S = B, k_idx.shape[1]
+    a.pos = _dev(pos, "pos")
+    a.k_idx_new, a.k_idx = _dev(k_idx_new, "k_idx_new"), _dev(k_idx, "k_idx")
+    a.di = di
+    a.kv_new, a.kv_lat = _dev(kv_new, "kv_new"), _dev(kv_lat, "kv_lat")
+    a.row = kv_new.shape[1]
+    a.kv_row_stride = kv_lat.shape[2]
+    _check("dsa_cache_append", load().dsa_cache_append(ctypes.byref(a), _stream(stream)))

@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblgsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "compress.hip", "gate.hip", "hca_bf16.hip", "hca_f32.hip",
+SOURCES = ["api.cpp", "cache.hip", "compress.hip", "gate.hip", "hca_bf16.hip", "hca_f32.hip",
            "indexer.hip", "sparse.hip"]
 
 # -packed-fp32-ops off: hand no packed fp32 math to the device code generator.

@@ -244,6 +244,54 @@ lgsa_status hca_compress(const void* k, const void* v, void* kc, void* vc, int B
                     "hca_compress");
 }
 
+lgsa_status hca_cache_append(const lgsa_hca_append_args* a, void* stream) {
+  REQUIRE(a != nullptr, LGSA_EINVAL, "hca_cache_append: args is NULL");
+  REQUIRE(a->dt == LGSA_F32 || a->dt == LGSA_BF16, LGSA_EINVAL,
+          "hca_cache_append: unknown dt %d", a->dt);
+  REQUIRE(a->B >= 0 && a->n_cap >= 0, LGSA_EINVAL, "hca_cache_append: B and n_cap must be >= 0");
+  REQUIRE(a->d >= 1 && a->win_len >= 1 && a->block >= 1, LGSA_EINVAL,
+          "hca_cache_append: d, win_len and block must be >= 1");
+  REQUIRE(a->pos && a->k_new && a->v_new && a->k_win && a->v_win, LGSA_EINVAL,
+          "hca_cache_append: pos, k_new, v_new, k_win and v_win must be non-NULL");
+  REQUIRE(a->n_cap == 0 || (a->kc && a->vc), LGSA_EINVAL,
+          "hca_cache_append: kc and vc must be non-NULL when n_cap > 0");
+  REQUIRE(a->n_cap == 0 || a->win_len >= a->block, LGSA_EINVAL,
+          "hca_cache_append: the ring (win_len %d) must hold a whole block (%d) when n_cap > 0",
+          a->win_len, a->block);
+  REQUIRE(a->d % (a->dt == LGSA_BF16 ? 8 : 4) == 0, LGSA_EUNSUPPORTED,
+          "hca_cache_append: d must be a multiple of %d for this dtype",
+          a->dt == LGSA_BF16 ? 8 : 4);
+  REQUIRE(aligned(a->k_new, 16) && aligned(a->v_new, 16) && aligned(a->k_win, 16) &&
+              aligned(a->v_win, 16) && aligned(a->kc, 16) && aligned(a->vc, 16),
+          LGSA_EINVAL, "hca_cache_append: tensors must be 16-byte aligned");
+  return hip_status(lgsa::launch_hca_append(a->pos, a->k_new, a->v_new, a->k_win, a->v_win,
+                                            a->kc, a->vc, a->B, a->d, a->win_len, a->n_cap,
+                                            a->block, a->dt, (hipStream_t)stream),
+                    "hca_cache_append");
+}
+
+lgsa_status dsa_cache_append(const lgsa_dsa_append_args* a, void* stream) {
+  REQUIRE(a != nullptr, LGSA_EINVAL, "dsa_cache_append: args is NULL");
+  REQUIRE(a->dt == LGSA_F32 || a->dt == LGSA_BF16, LGSA_EINVAL,
+          "dsa_cache_append: unknown dt %d", a->dt);
+  REQUIRE(a->B >= 0 && a->S >= 1 && a->di >= 1 && a->row >= 1, LGSA_EINVAL,
+          "dsa_cache_append: B must be >= 0 and S, di, row >= 1");
+  REQUIRE(a->kv_row_stride >= a->row, LGSA_EINVAL,
+          "dsa_cache_append: kv_row_stride (%lld) must be >= row (%d)", a->kv_row_stride, a->row);
+  REQUIRE(a->pos && a->k_idx_new && a->k_idx && a->kv_new && a->kv_lat, LGSA_EINVAL,
+          "dsa_cache_append: pos, k_idx_new, k_idx, kv_new and kv_lat must be non-NULL");
+  const int vec = a->dt == LGSA_BF16 ? 8 : 4;
+  REQUIRE(a->di % 4 == 0 && a->row % vec == 0 && a->kv_row_stride % vec == 0, LGSA_EUNSUPPORTED,
+          "dsa_cache_append: di must be a multiple of 4 and row, kv_row_stride of %d", vec);
+  REQUIRE(aligned(a->k_idx_new, 16) && aligned(a->k_idx, 16) && aligned(a->kv_new, 16) &&
+              aligned(a->kv_lat, 16),
+          LGSA_EINVAL, "dsa_cache_append: tensors must be 16-byte aligned");
+  return hip_status(lgsa::launch_dsa_append(a->pos, a->B, a->S, a->k_idx_new, a->k_idx, a->di,
+                                            a->kv_new, a->kv_lat, a->row, a->kv_row_stride,
+                                            a->dt, (hipStream_t)stream),
+                    "dsa_cache_append");
+}
+
 lgsa_status latent_gate(const void* q_lat, const void* w_gate, const void* o, void* out, int M,
                         int d_lat, int N, int dt, void* stream) {
   REQUIRE(dt == LGSA_F32 || dt == LGSA_BF16, LGSA_EINVAL, "latent_gate: unknown dt %d", dt);

@@ -13,6 +13,14 @@ enum { DT_F32 = 0, DT_BF16 = 1 };
 hipError_t launch_compress(const void* k, const void* v, void* kc, void* vc, int B, int T,
                            int d, int block, int dt, hipStream_t stream);
 
+// Decode-time cache appends (cache.hip).
+hipError_t launch_hca_append(const int32_t* pos, const void* k_new, const void* v_new,
+                             void* k_win, void* v_win, void* kc, void* vc, int B, int d,
+                             int win_len, int n_cap, int block, int dt, hipStream_t stream);
+hipError_t launch_dsa_append(const int32_t* pos, int B, int S, const float* k_idx_new,
+                             float* k_idx, int di, const void* kv_new, void* kv_lat, int row,
+                             long long stride, int dt, hipStream_t stream);
+
 // out[m, n] = o[m, n] * sigmoid(q_lat[m, :] . w[:, n]); out may equal o.
 hipError_t launch_gate(const void* q_lat, const void* w, const void* o, void* out, int M,
                        int d_lat, int N, int dt, hipStream_t stream);

@@ -189,6 +189,65 @@ typedef struct {
 lgsa_status sparse_attn_fwd(const lgsa_sparse_args* a, void* stream);
 lgsa_status sparse_attn_fwd_workspace(const lgsa_sparse_args* a, size_t* bytes);
 
+/* ---------------------------------------------------------------------------------------
+ * hca_cache_append -- decode-time maintenance of an HCA layer's cache (release blog,
+ * section 2.1: one compressed entry per completed block of 128 tokens plus a window of recent
+ * raw tokens; window size from the xenospectrum.com article, long-context section).  For
+ * every sequence b whose new token sits at position t = pos[b] >= 0:
+ *   - k_new[b] and v_new[b] are written to row t % win_len of the rings k_win and v_win;
+ *   - when t completes its block (t % block == block - 1) and e = t / block < n_cap, the
+ *     entry kc[b, e] = (1/block) * (sum of the block's keys) is written, and vc[b, e] from the
+ *     values.  The block's first block - 1 rows are read from the ring (row p % win_len for
+ *     position p) and its last row from k_new / v_new.  The sum runs in fp32 in the order
+ *     hca_compress uses, so an entry completed here is bit-identical to the one hca_compress
+ *     makes from the same rows.
+ * Sequences with pos[b] < 0 are left untouched.  This runs before the decode attention of the
+ * same token, which sees the token itself and, at a block's last token, the new entry.
+ * --------------------------------------------------------------------------------------- */
+typedef struct {
+  int dt;              /* LGSA_F32 or LGSA_BF16: every tensor of the call */
+  int B, d;            /* sequences, row width */
+  const int32_t* pos;  /* device [B]: position of each sequence's new token */
+  const void* k_new;   /* [B, d] key of the new token */
+  const void* v_new;   /* [B, d] value of the new token */
+  void* k_win;         /* [B, win_len, d] ring of raw keys: position p in row p % win_len */
+  void* v_win;         /* [B, win_len, d] ring of raw values, same rows */
+  int win_len;         /* rows of each ring (>= 1) */
+  void* kc;            /* [B, n_cap, d] compressed keys (may be NULL when n_cap == 0) */
+  void* vc;            /* [B, n_cap, d] compressed values */
+  int n_cap;           /* entries held in kc / vc (>= 0); entries e >= n_cap are not written */
+  int block;           /* tokens per compressed entry (128 for ERNIE 5.5 Flash), >= 1 */
+} lgsa_hca_append_args;
+/* Validation: B >= 0, d >= 1, win_len >= 1, block >= 1, n_cap >= 0; when n_cap > 0, kc and vc
+ * non-NULL and win_len >= block (the ring must hold a whole block).  Supported: LGSA_F32 with
+ * d % 4 == 0 or LGSA_BF16 with d % 8 == 0; every tensor 16-byte aligned.  Ring rows are always
+ * in range; the caller keeps the block's earlier rows in the ring (they were appended by the
+ * previous block - 1 calls or by a prefill). */
+lgsa_status hca_cache_append(const lgsa_hca_append_args* a, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * dsa_cache_append -- decode-time append to a DSA layer's caches (release blog, section 2.1:
+ * the indexer scores every past position and sparse attention gathers the latent rows of the
+ * selected ones).  For every sequence b with 0 <= t = pos[b] < S:
+ *   k_idx[b, t, :] = k_idx_new[b, :]   and   kv_lat[b*S*stride + t*stride + 0 .. row) = kv_new[b, :]
+ * Other sequences are left untouched.
+ * --------------------------------------------------------------------------------------- */
+typedef struct {
+  int dt;                  /* LGSA_F32 or LGSA_BF16: element type of kv_new and kv_lat */
+  int B, S;                /* sequences, positions held per sequence */
+  const int32_t* pos;      /* device [B]: position of each sequence's new token */
+  const float* k_idx_new;  /* [B, di] fp32 indexer key of the new token */
+  float* k_idx;            /* [B, S, di] fp32 indexer keys */
+  int di;                  /* indexer head dim */
+  const void* kv_new;      /* [B, row] latent row of the new token */
+  void* kv_lat;            /* [B, S, kv_row_stride] latent rows */
+  int row;                 /* elements of a latent row */
+  long long kv_row_stride; /* elements between consecutive positions (>= row) */
+} lgsa_dsa_append_args;
+/* Validation: B >= 0, S >= 1, di >= 1, row >= 1, kv_row_stride >= row.  Supported: di % 4 == 0;
+ * row and kv_row_stride multiples of 8 (bf16) or 4 (f32); every tensor 16-byte aligned. */
+lgsa_status dsa_cache_append(const lgsa_dsa_append_args* a, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -211,3 +211,58 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(lgsa, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(lgsa.LibraryMissing):
         lgsa.load()
+
+
+def _hca_append_args(**kw):
+    a = lgsa.HcaAppendArgs()
+    base = dict(dt=1, B=2, d=512, pos=FAKE, k_new=FAKE, v_new=FAKE, k_win=FAKE, v_win=FAKE,
+                win_len=128, kc=FAKE, vc=FAKE, n_cap=4, block=128)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(dt=5), lgsa.LGSA_EINVAL, "dt"),
+    (dict(B=-1), lgsa.LGSA_EINVAL, ">= 0"),
+    (dict(win_len=0), lgsa.LGSA_EINVAL, ">= 1"),
+    (dict(k_new=None), lgsa.LGSA_EINVAL, "non-NULL"),
+    (dict(kc=None), lgsa.LGSA_EINVAL, "kc and vc"),
+    (dict(win_len=64), lgsa.LGSA_EINVAL, "whole block"),
+    (dict(d=12), lgsa.LGSA_EUNSUPPORTED, "multiple of 8"),
+    (dict(v_win=FAKE_ODD), lgsa.LGSA_EINVAL, "aligned"),
+])
+def test_hca_append_validation(lib, kw, code, msg):
+    assert lib.hca_cache_append(ctypes.byref(_hca_append_args(**kw)), None) == code
+    assert msg in lgsa.last_error()
+
+
+def test_hca_append_without_entries_needs_no_cache(lib):
+    # n_cap == 0: kc / vc may be NULL and the ring may be shorter than a block; with B == 0
+    # nothing is enqueued, so this runs without a GPU
+    a = _hca_append_args(B=0, kc=None, vc=None, n_cap=0, win_len=16)
+    assert lib.hca_cache_append(ctypes.byref(a), None) == lgsa.LGSA_OK
+
+
+def _dsa_append_args(**kw):
+    a = lgsa.DsaAppendArgs()
+    base = dict(dt=1, B=2, S=1000, pos=FAKE, k_idx_new=FAKE, k_idx=FAKE, di=64, kv_new=FAKE,
+                kv_lat=FAKE, row=256, kv_row_stride=256)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(S=0), lgsa.LGSA_EINVAL, ">= 1"),
+    (dict(kv_row_stride=128), lgsa.LGSA_EINVAL, "kv_row_stride"),
+    (dict(kv_lat=None), lgsa.LGSA_EINVAL, "non-NULL"),
+    (dict(di=6), lgsa.LGSA_EUNSUPPORTED, "multiple"),
+    (dict(row=252, kv_row_stride=252), lgsa.LGSA_EUNSUPPORTED, "multiple"),
+    (dict(k_idx=FAKE_ODD), lgsa.LGSA_EINVAL, "aligned"),
+])
+def test_dsa_append_validation(lib, kw, code, msg):
+    assert lib.dsa_cache_append(ctypes.byref(_dsa_append_args(**kw)), None) == code
+    assert msg in lgsa.last_error()
