@@ -276,6 +276,28 @@ def run_c4(torch, lgsa, synth, to_dev, iters):
                 bytes=hbytes + ibytes + sbytes, index_bytes=ibytes)
 
 
+def run_vha(torch, lgsa, synth, to_dev, iters):
+    """The Virtual Head Attention mixing step at the prefill model shape: 32768 tokens x 64
+    heads x 512 channels (bf16), rank 16, in place; it reads and writes the output once."""
+    M, H, d, r = 32768, 64, 512, 16
+    o = torch.randn((M, H, d), device="cuda").to(torch.bfloat16)
+    u = to_dev(synth.normal(60, (H, r), 0.02, True))
+    v = to_dev(synth.normal(61, (H, r), 0.02, True))
+    tm = Timer(torch, torch.cuda.current_stream())
+    lgsa.vha_mix(o, u, v, out=o)
+    torch.cuda.synchronize()
+    a = tm.event()
+    for _ in range(iters):
+        lgsa.vha_mix(o, u, v, out=o)
+    b = tm.event()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / iters
+    nbytes = 2 * M * H * d * 2 + 2 * H * r * 2
+    flops = 2.0 * 2 * M * H * r * d
+    return dict(ms=round(ms, 4), bytes=nbytes, GBps=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                hbm_frac=round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), flops=flops)
+
+
 def run_append(torch, lgsa, synth, to_dev, iters):
     """Decode-time cache appends at the decode workloads' shapes: the HCA append for 64
     sequences (ring of 128 rows, 1024 entries, d 512, bf16) at a block's last token, which also
@@ -433,6 +455,7 @@ def main():
                                           GBps=round(gbps, 1),
                                           hbm_frac=round(gbps / PEAK_HBM_GBPS, 4),
                                           bytes=r2["bytes"])
+    secondary["vha_mix_prefill"] = run_vha(torch, lgsa, synth, to_dev, 10)
     if 2 in cfgs or 4 in cfgs:
         secondary["decode_cache_append"] = run_append(torch, lgsa, synth, to_dev, 50)
     if 3 in cfgs:

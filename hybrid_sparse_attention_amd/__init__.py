@@ -23,7 +23,7 @@ LGSA_F32, LGSA_BF16 = 0, 1
 EXPORTS = ["lgsa_last_error", "hca_compress", "latent_gate", "hca_attn_fwd",
            "hca_attn_fwd_workspace", "dsa_index_topk", "dsa_index_topk_workspace",
            "sparse_attn_fwd", "sparse_attn_fwd_workspace", "hca_cache_append",
-           "dsa_cache_append"]
+           "dsa_cache_append", "vha_mix"]
 
 
 class LibraryMissing(RuntimeError):
@@ -94,6 +94,7 @@ def load():
             getattr(lib, name).argtypes = [ctypes.POINTER(st), _P]
             getattr(lib, name + "_workspace").argtypes = [ctypes.POINTER(st),
                                                           ctypes.POINTER(_SZ)]
+        lib.vha_mix.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
         lib.hca_cache_append.argtypes = [ctypes.POINTER(HcaAppendArgs), _P]
         lib.dsa_cache_append.argtypes = [ctypes.POINTER(DsaAppendArgs), _P]
         for name in EXPORTS[1:]:
@@ -342,3 +343,18 @@ def dsa_cache_append(pos, k_idx_new, k_idx, kv_new, kv_lat, stream=None):
     a.row = kv_new.shape[1]
     a.kv_row_stride = kv_lat.shape[2]
     _check("dsa_cache_append", load().dsa_cache_append(ctypes.byref(a), _stream(stream)))
+
+
+def vha_mix(o, u, v, out=None, stream=None):
+    """Virtual Head Attention mixing step: out = o + U V^T o over the heads of each token, with
+    o [M,H,d] (or [B,T,H,d]) and u, v [H,r]; out may be o; see include/lgsa.h."""
+    torch = _torch()
+    H, d = o.shape[-2], o.shape[-1]
+    M = o.numel() // (H * d)
+    r = u.shape[1]
+    if out is None:
+        out = torch.empty_like(o)
+    rc = load().vha_mix(_dev(o, "o"), _dev(u, "u"), _dev(v, "v"), _dev(out, "out"), M, H, d, r,
+                        _dt(o), _stream(stream))
+    _check("vha_mix", rc)
+    return out

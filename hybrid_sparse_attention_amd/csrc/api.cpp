@@ -244,6 +244,23 @@ lgsa_status hca_compress(const void* k, const void* v, void* kc, void* vc, int B
                     "hca_compress");
 }
 
+lgsa_status vha_mix(const void* o, const void* u, const void* v, void* out, int M, int H, int d,
+                    int r, int dt, void* stream) {
+  REQUIRE(dt == LGSA_F32 || dt == LGSA_BF16, LGSA_EINVAL, "vha_mix: unknown dt %d", dt);
+  REQUIRE(M >= 0 && H >= 1 && d >= 1 && r >= 1, LGSA_EINVAL,
+          "vha_mix: M must be >= 0 and H, d, r >= 1");
+  REQUIRE(o && u && v && out, LGSA_EINVAL, "vha_mix: o, u, v and out must be non-NULL");
+  REQUIRE(r <= 16, LGSA_EUNSUPPORTED, "vha_mix: rank r must be <= 16 (got %d)", r);
+  if (dt == LGSA_BF16) {
+    REQUIRE(H == 64 && d % 256 == 0, LGSA_EUNSUPPORTED,
+            "vha_mix: bf16 needs H == 64 and d %% 256 == 0 (got %d, %d)", H, d);
+    REQUIRE(aligned(o, 16) && aligned(out, 16), LGSA_EINVAL,
+            "vha_mix: o and out must be 16-byte aligned");
+  }
+  return hip_status(lgsa::launch_vha(o, u, v, out, M, H, d, r, dt, (hipStream_t)stream),
+                    "vha_mix");
+}
+
 lgsa_status hca_cache_append(const lgsa_hca_append_args* a, void* stream) {
   REQUIRE(a != nullptr, LGSA_EINVAL, "hca_cache_append: args is NULL");
   REQUIRE(a->dt == LGSA_F32 || a->dt == LGSA_BF16, LGSA_EINVAL,

@@ -21,6 +21,11 @@ hipError_t launch_dsa_append(const int32_t* pos, int B, int S, const float* k_id
                              float* k_idx, int di, const void* kv_new, void* kv_lat, int row,
                              long long stride, int dt, hipStream_t stream);
 
+// Virtual Head Attention mixing step (vha.hip): out = o + U V^T o over the heads of each
+// token; out may equal o.
+hipError_t launch_vha(const void* o, const void* u, const void* v, void* out, int M, int H,
+                      int d, int r, int dt, hipStream_t stream);
+
 // out[m, n] = o[m, n] * sigmoid(q_lat[m, :] . w[:, n]); out may equal o.
 hipError_t launch_gate(const void* q_lat, const void* w, const void* o, void* out, int M,
                        int d_lat, int N, int dt, hipStream_t stream);

@@ -190,6 +190,22 @@ lgsa_status sparse_attn_fwd(const lgsa_sparse_args* a, void* stream);
 lgsa_status sparse_attn_fwd_workspace(const lgsa_sparse_args* a, size_t* bytes);
 
 /* ---------------------------------------------------------------------------------------
+ * vha_mix -- Virtual Head Attention (release blog, section 2.1: after attention, a light
+ * low-rank mixing step across heads with an identity skip connection, so that heads share
+ * information).  Read as, per token m and channel c of the head dimension,
+ *     out[m, h, c] = o[m, h, c] + sum_{h'} (U V^T)[h, h'] * o[m, h', c]
+ * with U = u, V = v of shape [H, r] (the pages give neither the rank nor the weights), applied
+ * to the gated attention output.  Computed as z = V^T o[m] (rank r) and out = o[m] + U z,
+ * accumulating in fp32; on the bfloat16 path z is rounded to bfloat16 before the second
+ * product.
+ *   o, out [M, H, d] (dt); out may equal o.   u, v [H, r] (dt)
+ * Supported: LGSA_BF16 with H == 64, d % 256 == 0, 1 <= r <= 16 (o, out 16-byte aligned);
+ * LGSA_F32 with H >= 1, d >= 1, 1 <= r <= 16.  M == 0 enqueues nothing.
+ * ------------------------------------------------------------------------------------- */
+lgsa_status vha_mix(const void* o, const void* u, const void* v, void* out, int M, int H, int d,
+                    int r, int dt, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * hca_cache_append -- decode-time maintenance of an HCA layer's cache (release blog,
  * section 2.1: one compressed entry per completed block of 128 tokens plus a window of recent
  * raw tokens; window size from the xenospectrum.com article, long-context section).  For

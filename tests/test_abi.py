@@ -266,3 +266,17 @@ def _dsa_append_args(**kw):
 def test_dsa_append_validation(lib, kw, code, msg):
     assert lib.dsa_cache_append(ctypes.byref(_dsa_append_args(**kw)), None) == code
     assert msg in lgsa.last_error()
+
+
+def test_vha_validation(lib):
+    f = lib.vha_mix
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 64, 512, 16, 7, None) == lgsa.LGSA_EINVAL
+    assert f(None, FAKE, FAKE, FAKE, 4, 64, 512, 16, 1, None) == lgsa.LGSA_EINVAL
+    assert "non-NULL" in lgsa.last_error()
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 64, 512, 0, 1, None) == lgsa.LGSA_EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 64, 512, 17, 1, None) == lgsa.LGSA_EUNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 32, 512, 16, 1, None) == lgsa.LGSA_EUNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 64, 320, 16, 1, None) == lgsa.LGSA_EUNSUPPORTED
+    assert f(FAKE_ODD, FAKE, FAKE, FAKE, 4, 64, 512, 16, 1, None) == lgsa.LGSA_EINVAL
+    assert "aligned" in lgsa.last_error()
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, 64, 512, 16, 1, None) == lgsa.LGSA_OK  # M == 0: no work
