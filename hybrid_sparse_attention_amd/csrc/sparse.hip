@@ -5,9 +5,11 @@
 // irrelevant, and one latent row may serve as both key and value.
 //
 // Workgroup: one query row (its H heads share the index list), 64 heads, and a range of the
-// list.  Four waves take 16 heads each over the whole 256-wide head: Q in 32 registers, O in
-// 64.  Keys come in tiles of 32 gathered rows, brought to LDS by LDS DMA (one instruction
-// fetches two 512-byte rows) and double buffered.  When the value rows are the key rows the
+// list.  Two waves take 32 heads each over the whole 256-wide head, as two blocks of 16 MFMA
+// columns: Q in 64 registers, O in 128.  Every K or V fragment read from LDS feeds both blocks,
+// which halves the LDS read traffic of 16 heads per wave; four workgroups fit a CU.  Keys come
+// in tiles of 32 gathered rows, brought to LDS by LDS DMA (one instruction fetches two 512-byte
+// rows) and double buffered.  When the value rows are the key rows the
 // single tile serves both products: S^T = K Q^T reads it row-wise, O^T = V^T P^T reads it
 // through the transposing LDS read, so each gathered row crosses the memory system once.
 // The 16-byte chunks of a row are XOR-swizzled (chunk c of row r sits at position c ^ sw(r))
@@ -30,23 +32,25 @@ constexpr int TILE = KT * TROW;         // 16 KiB
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LAZY = 8.0f;            // rescale O only when the max grows by more (log2)
 constexpr float NEG_BIG = -1.0e30f;     // masked logit (finite: no inf - inf)
+constexpr int NW = 2;                   // waves per workgroup
+constexpr int NHB = 64 / (16 * NW);     // 16-head blocks per wave
 
 // chunk swizzle of row r: rows 0..7 -> 0, 2, .., 14; rows 8..15 -> 1, 3, .., 15 (period 16)
 __device__ __forceinline__ int sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 struct WaveState {
-  f32x4_t o[16];  // o[cb][r] = O[head l16][16cb + 4g + r]
-  float m;        // reference max (log2 domain)
-  float l;        // running partial sum of this lane's keys
+  f32x4_t o[NHB][16];  // o[hb][cb][r] = O[head 16hb + l16][16cb + 4g + r]
+  float m[NHB];        // reference max (log2 domain)
+  float l[NHB];        // running partial sum of this lane's keys
 };
 
 // Gather one tile: DMA instruction i (of 16) loads tile rows 2i (lanes 0..31) and 2i + 1
-// (lanes 32..63); the wave issues i = w, w + n_waves, ...  `ix` holds, in lane j < 32, the
-// position of tile row j (-1 when skipped: the row is then read from position 0 and masked).
+// (lanes 32..63); wave w issues i = w, w + NW, ...  `ix` holds, in lane j < 32, the position
+// of tile row j (-1 when skipped: the row is then read from position 0 and masked).
 __device__ __forceinline__ void gather_tile(const uint16_t* rows, long long stride, int ix,
-                                            char* tile, int w, int n_waves, int lane) {
+                                            char* tile, int w, int lane) {
   const int hi = lane >> 5;
-  for (int i = w; i < KT / 2; i += n_waves) {
+  for (int i = w; i < KT / 2; i += NW) {
     const int sa = __builtin_amdgcn_readlane(ix, 2 * i);
     const int sb = __builtin_amdgcn_readlane(ix, 2 * i + 1);
     const int s = max(hi ? sb : sa, 0);
@@ -67,9 +71,10 @@ __device__ __forceinline__ int load_ix(const int32_t* idx, int j0, int j_end, in
 // the entry as a position, or -1 when it is skipped (negative or beyond the rows held)
 __device__ __forceinline__ int valid_ix(int s, int S) { return (s >= 0 && s < S) ? s : -1; }
 
-__device__ __forceinline__ void scores(f32x4_t (&s)[2], const Frag8 (&qf)[8], const char* kt,
-                                       const int (&kb)[4]) {
-  s[0] = s[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ void scores(f32x4_t (&s)[NHB][2], const Frag8 (&qf)[NHB][8],
+                                       const char* kt, const int (&kb)[4]) {
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) s[hb][0] = s[hb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
     Frag8 ka[2];
@@ -78,47 +83,53 @@ __device__ __forceinline__ void scores(f32x4_t (&s)[2], const Frag8 (&qf)[8], co
     for (int mb = 0; mb < 2; ++mb)
       ka[mb].u = *(const uint4*)(kt + kb[kk & 3] + 256 * (kk >> 2) + 16 * TROW * mb);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) s[mb] = mfma_16x16x32(ka[mb], qf[kk], s[mb]);
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) s[hb][mb] = mfma_16x16x32(ka[mb], qf[hb][kk], s[hb][mb]);
   }
 }
 
-__device__ __forceinline__ void softmax_pv(WaveState& st, const f32x4_t (&s)[2],
+__device__ __forceinline__ void softmax_pv(WaveState& st, const f32x4_t (&s)[NHB][2],
                                            const char* vt, uint32_t valid, float scale_log2,
                                            int vrow, int vsw, int vh, int lane) {
   const int g = lane >> 4;
-  float x[2][4];  // [mb][r]: key 16mb + 4g + r
+  Frag8 pf[NHB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int hb = 0; hb < NHB; ++hb) {
+    float x[2][4];  // [mb][r]: key 16mb + 4g + r
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      x[mb][r] = ((valid >> (16 * mb + 4 * g + r)) & 1u) ? s[mb][r] * scale_log2 : NEG_BIG;
-  float mx = x[0][0];
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+      for (int r = 0; r < 4; ++r)
+        x[mb][r] = ((valid >> (16 * mb + 4 * g + r)) & 1u) ? s[hb][mb][r] * scale_log2 : NEG_BIG;
+    float mx = x[0][0];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[mb][r]);
-  const float m_new = fmaxf(st.m, wave_max16(mx));
-  if (__any(m_new > st.m + LAZY)) {
-    const float alpha = fast_exp2(st.m - m_new);
-    st.m = m_new;
-    st.l *= alpha;
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb) st.o[cb] *= alpha;
-  }
-  float pr[2][4];
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[mb][r]);
+    const float m_new = fmaxf(st.m[hb], wave_max16(mx));
+    if (__any(m_new > st.m[hb] + LAZY)) {
+      const float alpha = fast_exp2(st.m[hb] - m_new);
+      st.m[hb] = m_new;
+      st.l[hb] *= alpha;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pr[mb][r] = fast_exp2(x[mb][r] - st.m);
-      st.l += pr[mb][r];
+      for (int cb = 0; cb < 16; ++cb) st.o[hb][cb] *= alpha;
     }
-  Frag8 pf;
-  pf.u = make_uint4(pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
-                    pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3]));
+    float pr[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[mb][r] = fast_exp2(x[mb][r] - st.m[hb]);
+        st.l[hb] += pr[mb][r];
+      }
+    pf[hb].u = make_uint4(pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
+                          pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3]));
+  }
   // V^T fragment of column block cb: transposed reads of rows vrow (slots 8g..8g+3) and
   // vrow + 16 (slots 8g+4..8g+7), columns 16cb + 4(l16 % 4) .. +3 = chunk 2cb + vh, half
-  // l16 & 1 of it, the chunk found at its swizzled position
+  // l16 & 1 of it, the chunk found at its swizzled position; each fragment serves all the
+  // wave's head blocks
   const int vh_t = opaque(vh);  // formed per tile, so the 16 positions are not kept live
 #pragma unroll
   for (int cb = 0; cb < 16; ++cb) {
@@ -128,7 +139,8 @@ __device__ __forceinline__ void softmax_pv(WaveState& st, const f32x4_t (&s)[2],
     const uint2 lo = lds_read_tr16(a);
     const uint2 hi = lds_read_tr16(a + 16 * TROW);
     va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    st.o[cb] = mfma_16x16x32(va, pf, st.o[cb]);
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) st.o[hb][cb] = mfma_16x16x32(va, pf[hb], st.o[hb][cb]);
   }
 }
 
@@ -142,9 +154,10 @@ __device__ __forceinline__ void store4(uint16_t* dst, const f32x4_t& v) {
 // grid: (row r = b*Tq + i) x (head group of 64) x (split); n_split == 1 writes out directly.
 // ALIAS: the value rows are the key rows (one gathered tile per step); otherwise a second tile
 // of value rows is gathered beside it.
+// Two waves per SIMD (four workgroups per CU): the register budget is 256 per lane.
 template <bool ALIAS>
-__global__ __launch_bounds__(256, 2) void sparse_kernel(SparseParams p, int n_split, int chunk,
-                                                        float* part_o, float* part_ml) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+sparse_kernel(SparseParams p, int n_split, int chunk, float* part_o, float* part_ml) {
   __shared__ __attribute__((aligned(1024))) char kt0[TILE];
   __shared__ __attribute__((aligned(1024))) char kt1[TILE];
   __shared__ __attribute__((aligned(1024))) char vt0[ALIAS ? 16 : TILE];
@@ -159,19 +172,23 @@ __global__ __launch_bounds__(256, 2) void sparse_kernel(SparseParams p, int n_sp
   const int b = r / p.Tq;
   const int j_begin = sp * chunk, j_end = min(p.k, j_begin + chunk);
   const int n_tiles = max(0, (j_end - j_begin + KT - 1) / KT);
-  const int h = hg * 64 + 16 * wave + l16;  // this lane's head (MFMA column)
+  const int h0 = hg * 64 + 16 * NHB * wave + l16;  // this lane's head in block 0 (MFMA column)
 
-  Frag8 qf[8];
-  {
-    const uint16_t* qr = (const uint16_t*)p.q + ((size_t)r * p.H + h) * D;
+  Frag8 qf[NHB][8];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[kk].u = *(const uint4*)(qr + 32 * kk + 8 * g);
+  for (int hb = 0; hb < NHB; ++hb) {
+    const uint16_t* qr = (const uint16_t*)p.q + ((size_t)r * p.H + h0 + 16 * hb) * D;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qf[hb][kk].u = *(const uint4*)(qr + 32 * kk + 8 * g);
   }
   WaveState st;
 #pragma unroll
-  for (int cb = 0; cb < 16; ++cb) st.o[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  st.m = NEG_BIG;
-  st.l = 0.f;
+  for (int hb = 0; hb < NHB; ++hb) {
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) st.o[hb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    st.m[hb] = NEG_BIG;
+    st.l[hb] = 0.f;
+  }
   const float scale_log2 = p.scale * LOG2E;
 
   // lane-constant LDS offsets: key reads (row l16 / l16 + 16, chunk 4kk + g) and transposed
@@ -193,8 +210,8 @@ __global__ __launch_bounds__(256, 2) void sparse_kernel(SparseParams p, int n_sp
   const int ix_cur = valid_ix(load_ix(idx, j_begin, j_end, lane), p.S);
   uint32_t valid_cur = (uint32_t)__ballot(ix_cur >= 0);
   if (n_tiles > 0) {
-    gather_tile(kl, p.k_stride, ix_cur, kt0, wave, 4, lane);
-    if (!ALIAS) gather_tile(vl, p.v_stride, ix_cur, vt0, wave, 4, lane);
+    gather_tile(kl, p.k_stride, ix_cur, kt0, wave, lane);
+    if (!ALIAS) gather_tile(vl, p.v_stride, ix_cur, vt0, wave, lane);
   }
   int ix_nxt = load_ix(idx, j_begin + KT, j_end, lane);
   wait_all();
@@ -205,11 +222,11 @@ __global__ __launch_bounds__(256, 2) void sparse_kernel(SparseParams p, int n_sp
     if (ti + 1 < n_tiles) {
       const int ixv = valid_ix(ix_nxt, p.S);
       valid_nxt = (uint32_t)__ballot(ixv >= 0);
-      gather_tile(kl, p.k_stride, ixv, kn, wave, 4, lane);
-      if (!ALIAS) gather_tile(vl, p.v_stride, ixv, vn, wave, 4, lane);
+      gather_tile(kl, p.k_stride, ixv, kn, wave, lane);
+      if (!ALIAS) gather_tile(vl, p.v_stride, ixv, vn, wave, lane);
     }
     const int ix_after = load_ix(idx, j_begin + KT * (ti + 2), j_end, lane);
-    f32x4_t s[2];
+    f32x4_t s[NHB][2];
     scores(s, qf, kc, kb);
     softmax_pv(st, s, ALIAS ? kc : vc, valid_cur, scale_log2, vrow, vsw, vh, lane);
     wait_all();  // this wave's gathers of tile ti + 1 and the positions of tile ti + 2
@@ -222,24 +239,28 @@ __global__ __launch_bounds__(256, 2) void sparse_kernel(SparseParams p, int n_sp
     if (ti + 1 < n_tiles) body(ti + 1, kt1, vt1, kt0, vt0);
   }
 
-  const float lt = wave_sum16(st.l);
-  const bool seen = st.m > 0.5f * NEG_BIG;
-  if (n_split == 1) {
-    const float inv = (seen && lt > 0.f) ? 1.f / lt : 0.f;
-    uint16_t* orow = (uint16_t*)p.out + ((size_t)r * p.H + h) * D;
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb) store4(orow + 16 * cb + 4 * g, st.o[cb] * inv);
-    return;
-  }
-  const size_t pr = ((size_t)r * n_split + sp) * p.H + h;
-  float* po = part_o + pr * D;
-  // a split that saw no valid key contributes nothing: max -inf, sum 0, O 0
-  const float keep = seen ? 1.f : 0.f;
+  for (int hb = 0; hb < NHB; ++hb) {
+    const int h = h0 + 16 * hb;
+    const float lt = wave_sum16(st.l[hb]);
+    const bool seen = st.m[hb] > 0.5f * NEG_BIG;
+    if (n_split == 1) {
+      const float inv = (seen && lt > 0.f) ? 1.f / lt : 0.f;
+      uint16_t* orow = (uint16_t*)p.out + ((size_t)r * p.H + h) * D;
 #pragma unroll
-  for (int cb = 0; cb < 16; ++cb) *(f32x4_t*)(po + 16 * cb + 4 * g) = st.o[cb] * keep;
-  if (g == 0) {
-    part_ml[pr * 2 + 0] = seen ? st.m : -INFINITY;
-    part_ml[pr * 2 + 1] = seen ? lt : 0.f;
+      for (int cb = 0; cb < 16; ++cb) store4(orow + 16 * cb + 4 * g, st.o[hb][cb] * inv);
+      continue;
+    }
+    const size_t pr = ((size_t)r * n_split + sp) * p.H + h;
+    float* po = part_o + pr * D;
+    // a split that saw no valid key contributes nothing: max -inf, sum 0, O 0
+    const float keep = seen ? 1.f : 0.f;
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) *(f32x4_t*)(po + 16 * cb + 4 * g) = st.o[hb][cb] * keep;
+    if (g == 0) {
+      part_ml[pr * 2 + 0] = seen ? st.m[hb] : -INFINITY;
+      part_ml[pr * 2 + 1] = seen ? lt : 0.f;
+    }
   }
 }
 
@@ -305,10 +326,10 @@ hipError_t launch_sparse(const SparseParams& p, hipStream_t stream) {
   const long long grid = rows * (p.H / 64) * n_split;
   const bool alias = p.v_lat == p.k_lat && p.v_stride == p.k_stride;
   if (alias)
-    hipLaunchKernelGGL(sparse_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, p,
+    hipLaunchKernelGGL(sparse_kernel<true>, dim3((unsigned)grid), dim3(64 * NW), 0, stream, p,
                        n_split, chunk, part_o, part_ml);
   else
-    hipLaunchKernelGGL(sparse_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, p,
+    hipLaunchKernelGGL(sparse_kernel<false>, dim3((unsigned)grid), dim3(64 * NW), 0, stream, p,
                        n_split, chunk, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
