@@ -69,29 +69,14 @@ __device__ __forceinline__ void block_scan2(int a, int b, int& a_ex, int& b_ex, 
   __syncthreads();
 }
 
-// Histogram of one radix digit, one private copy per wave (hist: NT / 64 x 256 counters), and
-// the selection of the digit that holds the kr-th largest key: thread t < 256 takes digit
-// 255 - t, the counts are scanned in that (descending) order across the first four waves, and
-// the one thread whose inclusive count first reaches kr writes sh[0] = digit and
-// sh[1] = kr - (keys in larger digits).
-template <int NT, class Get>
-__device__ void radix_digit(const Get& get, int n, uint32_t prefix, uint32_t hi_mask, int shift,
-                            int kr, uint32_t* hist, int* sh, int* wsum) {
+// Selection of the digit that holds the kr-th largest key from a digit histogram (one private
+// copy per wave, hist: NT / 64 x 256 counters): thread t < 256 takes digit 255 - t, the counts
+// are scanned in that (descending) order across the first four waves, and the one thread whose
+// inclusive count first reaches kr writes sh[0] = digit, sh[1] = kr - (keys in larger digits)
+// and sh[2] = keys in the digit.
+template <int NT>
+__device__ void pick_digit(int kr, const uint32_t* hist, int* sh, int* wsum) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int x = tid; x < (NT / 64) * 256; x += NT) hist[x] = 0u;
-  __syncthreads();
-  uint32_t* mine = hist + wave * 256;
-  constexpr int PER = 8;  // loads in flight per thread; consecutive threads read consecutive keys
-  for (int c0 = tid; c0 < n; c0 += NT * PER) {
-    uint32_t u[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) u[j] = c0 + j * NT < n ? get(c0 + j * NT) : 0u;
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if (c0 + j * NT < n && (u[j] & hi_mask) == prefix)
-        atomicAdd(&mine[(u[j] >> shift) & 255u], 1u);
-  }
-  __syncthreads();
   int c = 0, incl = 0;
   if (tid < 256) {
 #pragma unroll
@@ -113,9 +98,33 @@ __device__ void radix_digit(const Get& get, int n, uint32_t prefix, uint32_t hi_
     if (incl >= kr && excl < kr) {
       sh[0] = 255 - tid;
       sh[1] = kr - excl;
+      sh[2] = c;
     }
   }
   __syncthreads();
+}
+
+// Histogram of one radix digit (bits shift .. shift + 7) over the keys whose bits above the
+// digit equal `prefix`, then pick_digit.
+template <int NT, class Get>
+__device__ void radix_digit(const Get& get, int n, uint32_t prefix, uint32_t hi_mask, int shift,
+                            int kr, uint32_t* hist, int* sh, int* wsum) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  for (int x = tid; x < (NT / 64) * 256; x += NT) hist[x] = 0u;
+  __syncthreads();
+  uint32_t* mine = hist + wave * 256;
+  constexpr int PER = 8;  // loads in flight per thread; consecutive threads read consecutive keys
+  for (int c0 = tid; c0 < n; c0 += NT * PER) {
+    uint32_t u[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) u[j] = c0 + j * NT < n ? get(c0 + j * NT) : 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (c0 + j * NT < n && (u[j] & hi_mask) == prefix)
+        atomicAdd(&mine[(u[j] >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  pick_digit<NT>(kr, hist, sh, wsum);
 }
 
 // Finds the k-th largest key K* among get(0..n-1) (1 <= k <= n) and the number of keys equal
@@ -271,30 +280,194 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexParams p, int b,
 }
 
 constexpr int SEL_NT = 1024;
+constexpr int SEL_N16 = 65536;  // rows of up to this many keys keep 16-bit key images in LDS
+constexpr int SEL_CAP = 2048;   // keys of the threshold's 16-bit bin held in full
 
+// One workgroup per query row.  Rows of at most SEL_N16 keys: one pass over the row in global
+// memory stores the upper 16 bits of every key in LDS and counts its upper 12 bits in one
+// shared 4096-bin histogram (scores crowd into a few exponents: 8-bit digits would send most
+// of a wave's atomic adds to the same counter); the next 4 bits are counted from LDS; the keys whose upper 16 bits equal the threshold's (the bin the
+// k-th largest key falls in) are then read in full, in position order, into LDS, where the
+// last two digits are resolved; the selection is emitted from LDS.  The row is read from
+// global memory once, plus the threshold bin's keys.  Longer rows, and rows whose threshold
+// bin holds more than SEL_CAP keys, take all four digits and the emission over global memory.
 __global__ __launch_bounds__(SEL_NT) void index_select_rows_kernel(IndexParams p, int b,
                                                                    int i_begin,
                                                                    const uint32_t* ws,
                                                                    int s_ld) {
+  __shared__ __attribute__((aligned(16))) uint16_t k16[SEL_N16];
   __shared__ uint32_t hist[(SEL_NT / 64) * 256];
-  __shared__ int sh[2];
+  __shared__ uint32_t cand[SEL_CAP];
+  __shared__ int sh[3];
   __shared__ int wsum[2 * SEL_NT / 64];
-  __shared__ uint32_t stage[SEL_NT * EMIT_PER];
+  const int tid = threadIdx.x;
   const int i = i_begin + blockIdx.x;
   const int t = min(p.pos0[b] + i, min(p.S, p.max_pos + 1) - 1);
   const int n = t >= 0 ? t + 1 : 0;
   int32_t* out = p.idx_out + ((size_t)b * p.Tq + i) * p.k;
   if (n <= p.k) {
-    for (int j = threadIdx.x; j < p.k; j += SEL_NT) out[j] = j < n ? j : -1;
+    for (int j = tid; j < p.k; j += SEL_NT) out[j] = j < n ? j : -1;
     return;
   }
   const uint32_t* row = ws + (size_t)blockIdx.x * s_ld;
   auto get = [&](int x) { return row[x]; };
-  uint32_t kstar;
-  int need_eq;
-  radix_threshold<SEL_NT>(get, n, p.k, hist, sh, wsum, kstar, need_eq);
-  emit_topk<SEL_NT>(get, n, kstar, need_eq, wsum, stage,
-                    [&](int slot, int x, uint32_t) { out[slot] = x; });
+  auto emit_global = [&](uint32_t prefix, uint32_t hi_mask, int shift, int kr) {
+    // remaining digits and the emission over global memory (k16 serves as the staging buffer)
+    for (; shift >= 0; shift -= 8) {
+      radix_digit<SEL_NT>(get, n, prefix, hi_mask, shift, kr, hist, sh, wsum);
+      prefix |= (uint32_t)sh[0] << shift;
+      kr = sh[1];
+      hi_mask = 0xFFFFFFFFu << shift;
+      __syncthreads();
+    }
+    emit_topk<SEL_NT>(get, n, prefix, kr, wsum, (uint32_t*)k16,
+                      [&](int slot, int x, uint32_t) { out[slot] = x; });
+  };
+  if (n > SEL_N16) {
+    emit_global(0u, 0u, 24, p.k);
+    return;
+  }
+
+  // bits 31..20 (one shared histogram of 4096 counters in the space of the per-wave ones),
+  // with the 16-bit images stored on the way
+  constexpr int NB = 4096, BPT = NB / SEL_NT;
+  static_assert(NB <= (SEL_NT / 64) * 256, "the 12-bit histogram reuses the digit histograms");
+  for (int x = tid; x < NB; x += SEL_NT) hist[x] = 0u;
+  __syncthreads();
+  {
+    constexpr int PER = 8;
+    for (int c0 = tid; c0 < n; c0 += SEL_NT * PER) {
+      uint32_t u[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) u[j] = c0 + j * SEL_NT < n ? row[c0 + j * SEL_NT] : 0u;
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (c0 + j * SEL_NT < n) {
+          k16[c0 + j * SEL_NT] = (uint16_t)(u[j] >> 16);
+          atomicAdd(&hist[u[j] >> 20], 1u);
+        }
+    }
+  }
+  __syncthreads();
+  {
+    // thread t covers bins NB - 1 - BPT t - j (j < BPT), the bins in descending order
+    int cnt[BPT], tot = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      cnt[j] = (int)hist[NB - 1 - BPT * tid - j];
+      tot += cnt[j];
+    }
+    int ex, z_ex, all, z_tot;
+    block_scan2<SEL_NT>(tot, 0, ex, z_ex, all, z_tot, wsum);
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      if (ex < p.k && ex + cnt[j] >= p.k) {
+        sh[0] = NB - 1 - BPT * tid - j;
+        sh[1] = p.k - ex;
+      }
+      ex += cnt[j];
+    }
+  }
+  __syncthreads();
+  const uint32_t d1 = (uint32_t)sh[0];  // upper 12 bits of the k-th largest key
+  const int kr1 = sh[1];
+  __syncthreads();
+  // bits 19..16 from LDS (an 8-bit digit of the images whose upper 4 bits the prefix fixes)
+  auto get16 = [&](int x) { return (uint32_t)k16[x]; };
+  radix_digit<SEL_NT>(get16, n, d1 << 4, 0xFFF0u, 0, kr1, hist, sh, wsum);
+  const uint32_t p16 = (d1 << 4) | ((uint32_t)sh[0] & 15u);  // upper 16 bits of the k-th key
+  const int kr2 = sh[1];                              // keys needed from that bin
+  const int c16 = sh[2];                              // keys in that bin
+  __syncthreads();
+  if (c16 > SEL_CAP) {
+    emit_global(p16 << 16, 0xFFFF0000u, 8, kr2);
+    return;
+  }
+
+  // the bin's keys in full, in position order: thread t of a chunk takes positions
+  // c0 + 8t .. c0 + 8t + 7
+  constexpr int PER = EMIT_PER;
+  static_assert(PER == 8, "one 16-byte LDS read per thread and chunk");
+  int cbase = 0;
+  for (int c0 = 0; c0 < n; c0 += SEL_NT * PER) {
+    const int i0 = c0 + tid * PER;
+    const uint4 w4 = *(const uint4*)(k16 + min(i0, SEL_N16 - PER));
+    const uint32_t wv[4] = {w4.x, w4.y, w4.z, w4.w};
+    int nc = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const uint32_t h = (wv[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      nc += (i0 + j < n && h == p16) ? 1 : 0;
+    }
+    int c_ex, z_ex, c_tot, z_tot;
+    block_scan2<SEL_NT>(nc, 0, c_ex, z_ex, c_tot, z_tot, wsum);
+    int slot = cbase + c_ex;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const uint32_t h = (wv[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      if (i0 + j < n && h == p16) cand[slot++] = row[i0 + j];
+    }
+    cbase += c_tot;
+  }
+  __syncthreads();
+  // digits 3 and 4 over the bin's keys
+  auto getc = [&](int x) { return cand[x]; };
+  uint32_t kstar = p16 << 16;
+  int kr = kr2;
+  for (int shift = 8; shift >= 0; shift -= 8) {
+    radix_digit<SEL_NT>(getc, c16, kstar, 0xFFFFFFFFu << (shift + 8), shift, kr, hist, sh, wsum);
+    kstar |= (uint32_t)sh[0] << shift;
+    kr = sh[1];
+    __syncthreads();
+  }
+  const int need_eq = kr;
+
+  // emission from LDS: keys above the bin are kept, keys below it dropped; a key of the bin
+  // (its full value the next in `cand`) is kept if above K*, or equal to K* and among the
+  // first need_eq such
+  int base = 0, eq_seen = 0;
+  cbase = 0;
+  for (int c0 = 0; c0 < n; c0 += SEL_NT * PER) {
+    const int i0 = c0 + tid * PER;
+    const uint4 w4 = *(const uint4*)(k16 + min(i0, SEL_N16 - PER));
+    const uint32_t wv[4] = {w4.x, w4.y, w4.z, w4.w};
+    uint32_t h[PER];
+    int nc = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      h[j] = i0 + j < n ? (wv[j >> 1] >> (16 * (j & 1))) & 0xFFFFu : 0u;
+      nc += (i0 + j < n && h[j] == p16) ? 1 : 0;
+    }
+    int c_ex, z_ex, c_tot, z_tot;
+    block_scan2<SEL_NT>(nc, 0, c_ex, z_ex, c_tot, z_tot, wsum);
+    // full keys: above the bin -> above K*, below it -> below K*, in it -> from cand
+    uint32_t u[PER];
+    int ci = cbase + c_ex, n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      u[j] = h[j] > p16 ? 0xFFFFFFFFu : (h[j] == p16 && i0 + j < n ? cand[ci++] : 0u);
+      n_gt += (i0 + j < n && u[j] > kstar) ? 1 : 0;
+      n_eq += (i0 + j < n && u[j] == kstar) ? 1 : 0;
+    }
+    cbase += c_tot;
+    int gt_ex, eq_ex, gt_tot, eq_tot;
+    block_scan2<SEL_NT>(n_gt, n_eq, gt_ex, eq_ex, gt_tot, eq_tot, wsum);
+    const int eq_keep_before = min(max(need_eq - eq_seen, 0), eq_ex);
+    int slot = base + gt_ex + eq_keep_before;
+    int eq_rank = eq_seen + eq_ex;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (i0 + j >= n) continue;
+      bool sel = u[j] > kstar;
+      if (u[j] == kstar) {
+        sel = eq_rank < need_eq;
+        ++eq_rank;
+      }
+      if (sel) out[slot++] = i0 + j;
+    }
+    base += gt_tot + min(max(need_eq - eq_seen, 0), eq_tot);
+    eq_seen += eq_tot;
+  }
 }
 
 // ------------------------------------------------------------------------------ decode
@@ -313,7 +486,7 @@ __global__ __launch_bounds__(DEC_NT) void index_segment_kernel(IndexParams p, in
   __shared__ uint32_t skey[SEG];
   __shared__ __attribute__((aligned(16))) float sq[4 * 64 + 4];
   __shared__ uint32_t hist[(DEC_NT / 64) * 256];
-  __shared__ int sh[2];
+  __shared__ int sh[3];
   __shared__ int wsum[2 * DEC_NT / 64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -412,7 +585,7 @@ __global__ __launch_bounds__(RED_NT) void index_reduce_kernel(IndexParams p, int
   __shared__ uint32_t rkey[RED_CAP];
   __shared__ int32_t rpos[RED_CAP];
   __shared__ uint32_t hist[(RED_NT / 64) * 256];
-  __shared__ int sh[2];
+  __shared__ int sh[3];
   __shared__ int wsum[2 * RED_NT / 64];
   const int G = red_g(p.k);
   const int n_out = (n_in + G - 1) / G;

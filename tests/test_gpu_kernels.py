@@ -215,6 +215,41 @@ def test_index_ties_and_zero_scores(torch, orc):
     assert kth[rows.index(2499)] == 0.0
 
 
+def test_index_prefill_long_rows(torch, orc):
+    """Rows of more than 65536 positions on the many-query path: their selection runs over the
+    scores in global memory rather than from on-chip 16-bit images."""
+    S, k, Tq = 70000, 2048, 8
+    x = synth.dsa_index(269, B=1, Tq=Tq, S=S, pos0=[S - Tq])
+    idx = lgsa.dsa_index_topk(to_dev(x["q_idx"]), to_dev(x["w_idx"]), to_dev(x["k_idx"]),
+                              to_dev(x["pos0"]), k, max_pos=S - 1)
+    torch.cuda.synchronize()
+    same = _check_index(orc, x, idx.cpu().numpy(), k, [0, 3, 7])
+    assert same >= 2
+
+
+def test_index_prefill_tie_group_in_threshold_bin(torch, orc):
+    """1500 identical key rows score identically for every query; where the k-th score falls
+    among them, the kept members must be the lowest-positioned ones (a prefix of the group)."""
+    T, k = 6000, 2048
+    x = synth.dsa_index(270, B=1, Tq=T, S=T)
+    g0, g1 = 1000, 2500
+    x["k_idx"][0, g0:g1] = x["k_idx"][0, g0]
+    idx = lgsa.dsa_index_topk(to_dev(x["q_idx"]), to_dev(x["w_idx"]), to_dev(x["k_idx"]),
+                              to_dev(x["pos0"]), k, max_pos=T - 1)
+    torch.cuda.synchronize()
+    g = idx.cpu().numpy()
+    rows = [2600, 3000, 4000, 5000, 5999] + list(range(2048, 6000, 97))
+    same = _check_index(orc, x, g, k, rows)
+    assert same >= len(rows) - 2
+    straddled = 0
+    for r in rows:
+        sel = g[0, r][g[0, r] >= 0]
+        grp = sel[(sel >= g0) & (sel < g1)]
+        assert grp.tolist() == list(range(g0, g0 + len(grp))), r
+        straddled += 0 < len(grp) < g1 - g0
+    assert straddled > 0  # some row's k-th score lies in the group
+
+
 @pytest.mark.parametrize("pos0", [[39999, 20000, 1500], [16383, 16384, 2047]])
 def test_index_decode(torch, orc, pos0):
     S, k = 40000, 2048
