@@ -8,10 +8,10 @@
 // above K* and the lowest-positioned keys equal to K*, which writes the kept positions in
 // ascending order.  Block-wide ranks come from wavefront ballots.
 //
-// Prefill (many queries per sequence): scores come from fp32 MFMA (v_mfma_f32_16x16x4f32,
+// Prefill (many queries per sequence): scores come from fp32 MFMA (v_mfma_f32_32x32x2f32,
 // rows = (query, indexer head), columns = keys, contraction = the 64 indexer dims), so each
-// key tile in LDS serves 64 queries; they are written as keys to the workspace, a chunk of
-// queries at a time, and a 1024-thread workgroup per query selects.
+// key tile in LDS serves 64 queries; they are written as keys to the workspace, a chunk of up
+// to 2048 queries at a time, and a 1024-thread workgroup per query selects.
 // Decode (few queries, long context): one workgroup per (query, 16384-position segment)
 // streams its key rows once, scores them with fp32 FMA, selects the segment's top-k in LDS and
 // writes them as a candidate list in ascending position; 4-way reductions of candidate lists
@@ -202,13 +202,21 @@ constexpr int SC_KT = 64;    // keys per LDS tile
 constexpr int SC_CH = 512;   // keys per workgroup
 constexpr int SK_LD = 64 + 4;
 
+typedef float f32x16v __attribute__((ext_vector_type(16)));
+
 // Scores of queries [i_begin, i_begin + nq) of sequence b against keys, written as ordered
-// keys to ws[(i - i_begin) * s_ld + s].
+// keys to ws[(i - i_begin) * s_ld + s].  Products on v_mfma_f32_32x32x2f32: a wave's rows are
+// (query, indexer head) pairs, 8 queries x 4 heads per 32-row block, two blocks per wave; the
+// columns are 32 keys of the tile; the contraction runs over the 64 indexer dims, 2 per step.
+// A lane's accumulator then holds the four heads of one (query, key) pair in consecutive
+// registers, so the weighted head sum is lane-local.  Key tiles are double buffered through
+// registers: the next tile's loads are in flight while the current one is used.
 __global__ __launch_bounds__(256) void index_scores_kernel(IndexParams p, int b, int i_begin,
                                                            int nq, uint32_t* ws, int s_ld) {
-  __shared__ __attribute__((aligned(16))) float sk[SC_KT * SK_LD];
+  __shared__ __attribute__((aligned(16))) float sk[2][SC_KT * SK_LD];
+  __shared__ __attribute__((aligned(16))) float sw[SC_Q * 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
+  const int l32 = lane & 31, hi = lane >> 5;
   const int i0 = i_begin + blockIdx.x * SC_Q;
   const int i_stop = i_begin + nq;
   const int pos = p.pos0[b];
@@ -217,65 +225,86 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexParams p, int b,
   if (s_begin > t_hi) return;
   const int s_end = min(t_hi + 1, s_begin + SC_CH);
 
-  // A fragments: row (query 4mb + l16/4, head l16%4), contraction index 4ks + g
-  float a[4][16];
-  float wv[4][4];
-  const int hq = l16 & 3;
+  {  // head weights of the workgroup's queries: sw[4q + h]
+    const int i = i0 + (tid >> 2), h = tid & 3;
+    sw[tid] = (i < i_stop && h < p.Hi) ? p.w_idx[((size_t)b * p.Tq + i) * p.Hi + h] : 0.f;
+  }
+  // A operands: row l32 of block mb is (query 16 wave + 8 mb + l32 / 4, head l32 % 4); step ks
+  // takes dim 2 ks + hi
+  float a[2][32];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const int i = i0 + 16 * wave + 4 * mb + (l16 >> 2);
+  for (int mb = 0; mb < 2; ++mb) {
+    const int i = i0 + 16 * wave + 8 * mb + (l32 >> 2), hq = l32 & 3;
     const bool ok = i < i_stop && hq < p.Hi;
-    const float* qr = p.q_idx + (((size_t)b * p.Tq + i) * p.Hi + hq) * 64;
+    const float* qr = p.q_idx + (((size_t)b * p.Tq + (ok ? i : 0)) * p.Hi + (ok ? hq : 0)) * 64;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) a[mb][ks] = ok ? qr[4 * ks + g] : 0.f;
-    const int io = i0 + 16 * wave + 4 * mb + g;  // the query of output rows 4g..4g+3
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      wv[mb][r] = (io < i_stop && r < p.Hi) ? p.w_idx[((size_t)b * p.Tq + io) * p.Hi + r] : 0.f;
+    for (int ks = 0; ks < 32; ++ks) a[mb][ks] = ok ? qr[2 * ks + hi] : 0.f;
   }
   const float* kb = p.k_idx + (size_t)b * p.S * 64;
-  for (int s0 = s_begin; s0 < s_end; s0 += SC_KT) {
-    __syncthreads();
+  float4 kv[4];
+  auto load_tile = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = tid + 256 * u;  // float4 index in the 64 x 64 tile
       const int key = c >> 4, dim = (c & 15) * 4;
-      const float4 v = s0 + key < s_end ? *(const float4*)(kb + (size_t)(s0 + key) * 64 + dim)
-                                        : make_float4(0.f, 0.f, 0.f, 0.f);
-      *(float4*)(&sk[key * SK_LD + dim]) = v;
+      kv[u] = s0 + key < s_end ? *(const float4*)(kb + (size_t)(s0 + key) * 64 + dim)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    __syncthreads();
-    f32x4v acc[4][4];
+  };
+  auto store_tile = [&](float* dst) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      float bv[4];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) bv[nb] = sk[(16 * nb + l16) * SK_LD + 4 * ks + g];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mb][ks], bv[nb], acc[mb][nb], 0, 0, 0);
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + 256 * u;
+      *(float4*)(&dst[(c >> 4) * SK_LD + (c & 15) * 4]) = kv[u];
     }
-    // lane: query 4mb + g (of this wave), key s0 + 16nb + l16, heads r = 0..3
+  };
+  load_tile(s_begin);
+  store_tile(sk[0]);
+  __syncthreads();
+  int buf = 0;
+  for (int s0 = s_begin; s0 < s_end; s0 += SC_KT) {
+    const bool more = s0 + SC_KT < s_end;
+    if (more) load_tile(s0 + SC_KT);
+    const float* skc = sk[buf];
+    f32x16v acc[2][2];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int i = i0 + 16 * wave + 4 * mb + g;
-      if (i >= i_stop) continue;
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int s = s0 + 16 * nb + l16;
-        if (s >= s_end) continue;
-        float sc = 0.f;
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16v{};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc = fmaf(wv[mb][r], fmaxf(acc[mb][nb][r], 0.f), sc);
-        ws[(size_t)(i - i_begin) * s_ld + s] = order_key(sc);
+    for (int ks = 0; ks < 32; ++ks) {
+      float bv[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) bv[nb] = skc[(32 * nb + l32) * SK_LD + 2 * ks + hi];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mb][ks], bv[nb], acc[mb][nb],
+                                                             0, 0, 0);
+    }
+    // acc[mb][nb][4j + h]: query 16 wave + 8 mb + 2j + hi, head h, key s0 + 32 nb + l32
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ql = 16 * wave + 8 * mb + 2 * j + hi;
+        const int i = i0 + ql;
+        const float4 w4 = *(const float4*)(sw + 4 * ql);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int s = s0 + 32 * nb + l32;
+          float sc = 0.f;
+          sc = fmaf(w4.x, fmaxf(acc[mb][nb][4 * j + 0], 0.f), sc);
+          sc = fmaf(w4.y, fmaxf(acc[mb][nb][4 * j + 1], 0.f), sc);
+          sc = fmaf(w4.z, fmaxf(acc[mb][nb][4 * j + 2], 0.f), sc);
+          sc = fmaf(w4.w, fmaxf(acc[mb][nb][4 * j + 3], 0.f), sc);
+          if (i < i_stop && s < s_end) ws[(size_t)(i - i_begin) * s_ld + s] = order_key(sc);
+        }
       }
-    }
+    if (more) store_tile(sk[buf ^ 1]);
+    __syncthreads();
+    buf ^= 1;
   }
 }
 
@@ -674,7 +703,7 @@ size_t index_workspace(const IndexParams& p) {
     const size_t lists = rows * level_lists(n_segments(p), p.k);
     return lists * p.k * (sizeof(uint32_t) + sizeof(int32_t)) + lists * sizeof(int);
   }
-  const size_t q_chunk = std::min(p.Tq, 1024);
+  const size_t q_chunk = std::min(p.Tq, 2048);
   return q_chunk * (size_t)key_bound(p) * sizeof(uint32_t);
 }
 
