@@ -51,7 +51,7 @@ def _load():
                                      P, P, I, L, P, L, P]
         lib.orc_latent_gate.argtypes = [P, I, P, I, P, I, L, L, L, P, L, P]
         lib.orc_dsa_scores.argtypes = [P, P, P, L, L, L, L, L, L, L, L, L, P]
-        lib.orc_dsa_topk.argtypes = [P, P, P, L, L, L, L, L, L, P, P, L, P, P]
+        lib.orc_dsa_topk.argtypes = [P, P, P, L, L, L, L, L, L, L, P, P, L, P, P]
         lib.orc_sparse_attn.argtypes = [P, I, L, L, L, L, L, P, L, P, L, I, L, P, L, D, P, P,
                                         I, L, P, L, P]
         for f in (lib.orc_hca_compress, lib.orc_hca_attn, lib.orc_latent_gate,
@@ -189,8 +189,10 @@ def dsa_scores(q_idx, w_idx, k_idx, b, i, s0, s1):
     return out
 
 
-def dsa_topk(q_idx, w_idx, k_idx, pos0, k, rows=None):
-    """Top-k positions per query row (ascending, -1 padded) and the k-th highest score."""
+def dsa_topk(q_idx, w_idx, k_idx, pos0, k, rows=None, block=1):
+    """Top-k keys per query row (ascending, -1 padded) and the k-th highest score.  block > 1:
+    key s is the compressed entry of positions block*s .. block*s + block - 1, visible to the
+    query at t once complete (s < (t + 1) // block)."""
     q_idx = np.ascontiguousarray(q_idx, dtype=np.float32)
     w_idx = np.ascontiguousarray(w_idx, dtype=np.float32)
     k_idx = np.ascontiguousarray(k_idx, dtype=np.float32)
@@ -201,7 +203,8 @@ def dsa_topk(q_idx, w_idx, k_idx, pos0, k, rows=None):
     idx = np.zeros((len(rows), k), dtype=np.int32)
     kth = np.zeros(len(rows), dtype=np.float64)
     _check(_load().orc_dsa_topk(_ptr(q_idx), _ptr(w_idx), _ptr(k_idx), B, Tq, S, Hi, di, k,
-                                _ptr(pos0), _ptr(rows), len(rows), _ptr(idx), _ptr(kth)),
+                                int(block), _ptr(pos0), _ptr(rows), len(rows), _ptr(idx),
+                                _ptr(kth)),
            "dsa_topk")
     return idx, kth
 
@@ -241,3 +244,31 @@ def sparse_attn(q, k_lat, idx, v_lat=None, *, dqk=None, dv=None, scale=None, q_l
                                  _ptr(out))
     _check(rc, "sparse_attn")
     return out
+
+
+def csa_attn(q, pos0, k, v, q_idx, w_idx, k_idx, k_top, *, block=4, scale=None, q_lat=None,
+             w_gate=None, rows=None):
+    """Compressed sparse attention (the variant of [blog 2.1] that compresses history, then
+    attends to a sparse part of it), in the steps the pages name, taken as the other layers
+    take them: K, V and the indexer keys are mean-pooled over complete blocks of `block`
+    tokens (hca_compress); the indexer scores the compressed entries a query can see (its
+    block complete) and keeps the top k_top (dsa_topk with block); softmax attention runs over
+    the kept entries (sparse_attn, values distinct from keys), gated when q_lat is given.
+
+    q [B,T,H,d]; k, v [B,T,d] (the layer's keys and values of every position; rows beyond the
+    last complete block are ignored); q_idx [B,T,Hi,64]; w_idx [B,T,Hi]; k_idx [B,T,64].
+    Returns (float64 out [n_rows,H,d], idx [n_rows,k_top], kth [n_rows], compressed keys,
+    compressed values, compressed indexer keys as float32).
+    """
+    kc = hca_compress(k, block)
+    vc = hca_compress(v, block)
+    kic = hca_compress(k_idx, block).astype(np.float32)
+    B, T = np.asarray(q_idx).shape[:2]
+    rows = _rows(rows, B * T)
+    idx, kth = dsa_topk(q_idx, w_idx, kic, pos0, k_top, rows=rows, block=block)
+    full = np.full((B, T, k_top), -1, np.int32)
+    for j, r in enumerate(rows):
+        full[r // T, r % T] = idx[j]
+    out = sparse_attn(q, kc, full, v_lat=vc, scale=scale, q_lat=q_lat, w_gate=w_gate,
+                      rows=rows)
+    return out, idx, kth, kc, vc, kic

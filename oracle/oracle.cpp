@@ -229,17 +229,22 @@ int orc_dsa_scores(const float* q_idx, const float* w_idx, const float* k_idx, l
   return 0;
 }
 
-// Per-query top-k of [blog 2.1]: among the causal positions s <= t (t = pos0[b] + i, and
-// t < S is required), keep the k highest scores, the lower position winning a tie; when
-// t + 1 <= k every position is kept.  The kept positions are written in ascending order
-// and the remaining slots hold -1.  kth_score[r] receives the k-th highest score (the
-// selection threshold), or -inf when every position is kept.
-// idx_out is [n_rows, k] int32.
+// Per-query top-k of [blog 2.1]: among the keys visible to the query at t = pos0[b] + i,
+// keep the k highest scores, the lower key winning a tie; when at most k keys are visible
+// every one is kept.  With block == 1 the keys are token positions and key s is visible
+// when s <= t (DSA).  With block > 1 key s is the compressed entry of positions
+// block*s .. block*s + block - 1 (the compressed sparse variant of [blog 2.1]: history
+// compressed, then a sparse part of it attended), visible once its block is complete,
+// block*s + block - 1 <= t; there are (t + 1) / block of them, and that many keys must
+// exist (at most S).  The kept keys are written in ascending order and the remaining slots
+// hold -1.  kth_score[r] receives the k-th highest score (the selection threshold), or -inf
+// when every visible key is kept.  idx_out is [n_rows, k] int32.
 int orc_dsa_topk(const float* q_idx, const float* w_idx, const float* k_idx, long long B,
                  long long Tq, long long S, long long Hi, long long di, long long k,
-                 const int* pos0, const long long* rows, long long n_rows, int* idx_out,
-                 double* kth_score) {
-  if (!q_idx || !w_idx || !k_idx || !pos0 || !rows || !idx_out || k <= 0) return -1;
+                 long long block, const int* pos0, const long long* rows, long long n_rows,
+                 int* idx_out, double* kth_score) {
+  if (!q_idx || !w_idx || !k_idx || !pos0 || !rows || !idx_out || k <= 0 || block <= 0)
+    return -1;
   for (long long r = 0; r < n_rows; ++r)
     if (rows[r] < 0 || rows[r] >= B * Tq) return -2;
   int err = 0;
@@ -248,12 +253,12 @@ int orc_dsa_topk(const float* q_idx, const float* w_idx, const float* k_idx, lon
     const long long b = rows[r] / Tq, i = rows[r] % Tq;
     const long long t = (long long)pos0[b] + i;
     int* dst = idx_out + r * k;
-    if (t < 0 || t >= S) {
+    const long long n = t < 0 ? 0 : (t + 1) / block;  // visible keys
+    if (t < 0 || n > S) {
 #pragma omp atomic write
       err = -3;
       continue;
     }
-    const long long n = t + 1;
     std::vector<long long> keep;
     double kth = -std::numeric_limits<double>::infinity();
     if (n <= k) {
