@@ -51,7 +51,7 @@ class HcaArgs(ctypes.Structure):
 class IndexArgs(ctypes.Structure):
     _fields_ = [("B", _I), ("Tq", _I), ("S", _I), ("Hi", _I), ("di", _I), ("k", _I),
                 ("q_idx", _P), ("w_idx", _P), ("k_idx", _P), ("pos0", _P), ("max_pos", _I),
-                ("idx_out", _P), ("workspace", _P), ("workspace_bytes", _SZ)]
+                ("idx_out", _P), ("workspace", _P), ("workspace_bytes", _SZ), ("block", _I)]
 
 
 class SparseArgs(ctypes.Structure):
@@ -228,9 +228,10 @@ def hca_attn_fwd_workspace(a) -> int:
     return n.value
 
 
-def index_args(q_idx, w_idx, k_idx, pos0, k, *, max_pos, idx_out=None):
+def index_args(q_idx, w_idx, k_idx, pos0, k, *, max_pos, idx_out=None, block=1):
     B, Tq, Hi, di = q_idx.shape
     a = IndexArgs()
+    a.block = int(block)
     a.B, a.Tq, a.S, a.Hi, a.di, a.k = B, Tq, k_idx.shape[1], Hi, di, k
     a.q_idx, a.w_idx, a.k_idx = _dev(q_idx, "q_idx"), _dev(w_idx, "w_idx"), _dev(k_idx, "k_idx")
     a.pos0 = _dev(pos0, "pos0")
@@ -247,13 +248,14 @@ def dsa_index_topk_workspace(a) -> int:
 
 
 def dsa_index_topk(q_idx, w_idx, k_idx, pos0, k, *, max_pos, idx_out=None, workspace=None,
-                   stream=None):
-    """Indexer scores + per-query top-k positions (ascending, -1 padded); see lgsa.h."""
+                   stream=None, block=1):
+    """Indexer scores + per-query top-k keys (ascending, -1 padded); see lgsa.h.  block > 1:
+    key s is the compressed entry of positions block*s .. block*s + block - 1."""
     torch = _torch()
     B, Tq = q_idx.shape[:2]
     if idx_out is None:
         idx_out = torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device)
-    a = index_args(q_idx, w_idx, k_idx, pos0, k, max_pos=max_pos, idx_out=idx_out)
+    a = index_args(q_idx, w_idx, k_idx, pos0, k, max_pos=max_pos, idx_out=idx_out, block=block)
     if workspace is None:
         workspace, _ = _workspace(dsa_index_topk_workspace(a), q_idx.device)
     a.workspace = None if workspace is None else workspace.data_ptr()
@@ -308,6 +310,27 @@ def sparse_attn_fwd(q, k_lat, idx, v_lat=None, *, scale=None, q_lat=None, w_gate
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("sparse_attn_fwd", load().sparse_attn_fwd(ctypes.byref(a), _stream(stream)))
     return out
+
+
+def csa_attn_fwd(q, pos0, k, v, q_idx, w_idx, k_idx, k_top, *, max_pos, block=4, q_lat=None,
+                 w_gate=None, out=None, stream=None):
+    """Compressed sparse attention, the variant of the release blog's section 2.1 that
+    compresses history `block`x and attends to a sparse part of it, composed from three library
+    calls: hca_compress pools K, V (bf16, [B,T,256]) and the indexer keys (fp32, [B,T,64]) over
+    complete blocks; dsa_index_topk with `block` scores the entries each query can see (its
+    block complete) and keeps the top k_top; sparse_attn_fwd attends to the kept entries (values
+    distinct from keys), gated when q_lat is given.  q [B,Tq,H,256] sits at positions pos0[b] +
+    i; every T >= block.  Returns (out [B,Tq,H,256], idx [B,Tq,k_top])."""
+    if k.shape[1] < block:
+        raise ValueError("csa_attn_fwd: the sequence (%d) holds no complete block of %d"
+                         % (k.shape[1], block))
+    kc, vc = hca_compress(k, v, block=block, stream=stream)
+    kic, _ = hca_compress(k_idx, k_idx, block=block, stream=stream)
+    idx = dsa_index_topk(q_idx, w_idx, kic, pos0, k_top, max_pos=max_pos, block=block,
+                         stream=stream)
+    out = sparse_attn_fwd(q, kc, idx, v_lat=vc, q_lat=q_lat, w_gate=w_gate, out=out,
+                          stream=stream)
+    return out, idx
 
 
 def hca_cache_append(pos, k_new, v_new, k_win, v_win, kc=None, vc=None, *, block=128,

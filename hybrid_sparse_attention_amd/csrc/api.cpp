@@ -134,6 +134,7 @@ lgsa::IndexParams to_params(const lgsa_index_args* a) {
   p.idx_out = a->idx_out;
   p.ws = a->workspace;
   p.ws_bytes = a->workspace_bytes;
+  p.block = a->block == 0 ? 1 : a->block;
   return p;
 }
 
@@ -147,9 +148,10 @@ lgsa_status check_index(const lgsa_index_args* a) {
           "dsa_index_topk: q_idx, w_idx, k_idx, pos0 and idx_out must be non-NULL");
   REQUIRE(a->max_pos >= a->Tq - 1, LGSA_EINVAL,
           "dsa_index_topk: max_pos (%d) is below Tq - 1 (%d)", a->max_pos, a->Tq - 1);
-  REQUIRE(a->max_pos < a->S, LGSA_EINVAL,
-          "dsa_index_topk: max_pos (%d) must be below S (%d): keys s <= t must exist",
-          a->max_pos, a->S);
+  REQUIRE(a->block >= 0, LGSA_EINVAL, "dsa_index_topk: block must be >= 0 (got %d)", a->block);
+  REQUIRE(((long long)a->max_pos + 1) / (a->block == 0 ? 1 : a->block) <= a->S, LGSA_EINVAL,
+          "dsa_index_topk: max_pos (%d) needs (max_pos + 1) / block keys but S is %d: every "
+          "visible key must exist", a->max_pos, a->S);
   REQUIRE(a->di == 64, LGSA_EUNSUPPORTED, "dsa_index_topk: di must be 64 (got %d)", a->di);
   REQUIRE(a->Hi <= 4, LGSA_EUNSUPPORTED, "dsa_index_topk: Hi must be <= 4 (got %d)", a->Hi);
   REQUIRE(a->k <= 4096, LGSA_EUNSUPPORTED, "dsa_index_topk: k must be <= 4096 (got %d)", a->k);

@@ -27,6 +27,12 @@ namespace {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
+// Number of keys visible to the query at position t: keys s < (t + 1) / block, at most
+// `bound` (the keys that exist and the rows' promised range); none for t < 0.
+__device__ __forceinline__ int visible_keys(int t, int block, int bound) {
+  return t >= 0 ? min((t + 1) / block, bound) : 0;
+}
+
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0u;  // -0.0 counts as +0.0
@@ -220,10 +226,13 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexParams p, int b,
   const int i0 = i_begin + blockIdx.x * SC_Q;
   const int i_stop = i_begin + nq;
   const int pos = p.pos0[b];
-  const int t_hi = min(min(p.S, p.max_pos + 1) - 1, pos + min(i_stop, i0 + SC_Q) - 1);
+  const int kbound = min(p.S, (p.max_pos + 1) / p.block);
+  // keys visible to the workgroup's last query bound the keys scored (earlier queries' rows
+  // get scores past their own visible range, which their selection never reads)
+  const int n_hi = visible_keys(pos + min(i_stop, i0 + SC_Q) - 1, p.block, kbound);
   const int s_begin = blockIdx.y * SC_CH;
-  if (s_begin > t_hi) return;
-  const int s_end = min(t_hi + 1, s_begin + SC_CH);
+  if (s_begin >= n_hi) return;
+  const int s_end = min(n_hi, s_begin + SC_CH);
 
   {  // head weights of the workgroup's queries: sw[4q + h]
     const int i = i0 + (tid >> 2), h = tid & 3;
@@ -331,8 +340,7 @@ __global__ __launch_bounds__(SEL_NT) void index_select_rows_kernel(IndexParams p
   __shared__ int wsum[2 * SEL_NT / 64];
   const int tid = threadIdx.x;
   const int i = i_begin + blockIdx.x;
-  const int t = min(p.pos0[b] + i, min(p.S, p.max_pos + 1) - 1);
-  const int n = t >= 0 ? t + 1 : 0;
+  const int n = visible_keys(p.pos0[b] + i, p.block, min(p.S, (p.max_pos + 1) / p.block));
   int32_t* out = p.idx_out + ((size_t)b * p.Tq + i) * p.k;
   if (n <= p.k) {
     for (int j = tid; j < p.k; j += SEL_NT) out[j] = j < n ? j : -1;
@@ -521,8 +529,7 @@ __global__ __launch_bounds__(DEC_NT) void index_segment_kernel(IndexParams p, in
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = blockIdx.x / n_seg, seg = blockIdx.x % n_seg;  // r = b * Tq + i
   const int b = r / p.Tq;
-  const int t = min(p.pos0[b] + r % p.Tq, min(p.S, p.max_pos + 1) - 1);
-  const int n = t >= 0 ? t + 1 : 0;
+  const int n = visible_keys(p.pos0[b] + r % p.Tq, p.block, min(p.S, (p.max_pos + 1) / p.block));
   const int seg_start = seg * SEG;
   if (n <= p.k) return;  // short rows are finished by the last reduction
   if (seg_start >= n) {  // a segment past the row's last position contributes nothing
@@ -621,8 +628,7 @@ __global__ __launch_bounds__(RED_NT) void index_reduce_kernel(IndexParams p, int
   const bool last = n_out == 1;
   const int r = blockIdx.x / n_out, grp = blockIdx.x % n_out;
   const int b = r / p.Tq, i = r % p.Tq;
-  const int t = min(p.pos0[b] + i, min(p.S, p.max_pos + 1) - 1);
-  const int n = t >= 0 ? t + 1 : 0;
+  const int n = visible_keys(p.pos0[b] + i, p.block, min(p.S, (p.max_pos + 1) / p.block));
   const int k = p.k;
   int32_t* out = p.idx_out + (size_t)r * k;
   if (n <= k) {
@@ -676,7 +682,7 @@ __global__ __launch_bounds__(RED_NT) void index_reduce_kernel(IndexParams p, int
 bool use_decode_path(const IndexParams& p) { return p.Tq <= 4; }
 
 long long key_bound(const IndexParams& p) {
-  return std::min<long long>(p.S, (long long)p.max_pos + 1);
+  return std::max<long long>(1, std::min<long long>(p.S, ((long long)p.max_pos + 1) / p.block));
 }
 
 int n_segments(const IndexParams& p) {

@@ -67,6 +67,7 @@ struct IndexParams {
   int32_t* idx_out;
   void* ws;
   size_t ws_bytes;
+  int block;  // positions per key (>= 1): key s visible to position t iff s < (t + 1) / block
 };
 
 size_t index_workspace(const IndexParams& p);      // recommended size

@@ -150,6 +150,15 @@ def dsa_sparse(config: int, B: int, Tq: int, S: int, H: int, d: int = D_MLA,
     return x
 
 
+def csa(config: int, B: int, T: int, H: int, d: int = D_MLA, gated: bool = True):
+    """Compressed sparse attention inputs for T positions per sequence: the sparse-attention
+    draws with distinct values (q, kv_lat as the keys, v_lat as the values, the gate) and the
+    indexer draws (q_idx, w_idx, k_idx per position), pos0 = 0."""
+    x = dsa_sparse(config, B, T, T, H, d, distinct_v=True, gated=gated)
+    x.update(dsa_index(config, B, Tq=T, S=T))
+    return x
+
+
 def random_topk(config: int, B: int, Tq: int, S: int, k: int, pos0):
     """A seeded index list per query: k distinct causal positions (all when t+1 <= k),
     ascending, -1 padded.  Stands in for an indexer output when sparse attention is tested

@@ -133,10 +133,14 @@ lgsa_status hca_attn_fwd_workspace(const lgsa_hca_args* a, size_t* bytes);
  * 2.1: the indexer scores the past positions of each query and core attention runs only on
  * the k highest-scoring ones).  The indexer form taken here is
  *     score(t, s) = sum_{h<Hi} w_idx[b,i,h] * max(0, <q_idx[b,i,h,:], k_idx[b,s,:]>)
- * computed in fp32 for every causal position s <= t, t = pos0[b] + i.  The k highest
- * scores are kept (all positions when t + 1 <= k); a tie is won by the lower position;
- * -0.0 counts as +0.0.  idx_out[b,i,:] lists the kept positions in ascending order and
- * holds -1 in the remaining slots.
+ * computed in fp32 for every visible key s of the query at position t = pos0[b] + i.  With
+ * block == 1 key s is token position s and is visible when s <= t.  With block > 1 (the
+ * compressed sparse attention variant, release blog section 2.1: history compressed 4x, then
+ * a sparse part of it attended) key s is the entry summarising positions block*s ..
+ * block*s + block - 1 and is visible once that block is complete: block*s + block - 1 <= t,
+ * i.e. s < (t + 1) / block.  The k highest scores are kept (every visible key when there are
+ * at most k); a tie is won by the lower key index; -0.0 counts as +0.0.  idx_out[b,i,:]
+ * lists the kept keys in ascending order and holds -1 in the remaining slots.
  * --------------------------------------------------------------------------------------- */
 typedef struct {
   int B, Tq, S;          /* sequences, query rows per sequence, key positions held */
@@ -149,9 +153,12 @@ typedef struct {
   int32_t* idx_out;      /* [B, Tq, k] int32 */
   void* workspace;       /* scratch, dsa_index_topk_workspace() bytes */
   size_t workspace_bytes;
+  int block;             /* positions per key (see above); 0 is read as 1 */
 } lgsa_index_args;
-/* Supported: di == 64, 1 <= Hi <= 4, 1 <= k <= 4096, S >= 1; q_idx and k_idx 16-byte aligned.  A position t >= S (caller
- * broke the max_pos promise) is clamped to S - 1 for reading; it never reads out of bounds. */
+/* Supported: di == 64, 1 <= Hi <= 4, 1 <= k <= 4096, S >= 1, block >= 0; (max_pos + 1) / block
+ * <= S (the visible keys of every row exist); q_idx and k_idx 16-byte aligned.  A position
+ * beyond max_pos (caller broke the promise) is clamped for reading; it never reads out of
+ * bounds. */
 lgsa_status dsa_index_topk(const lgsa_index_args* a, void* stream);
 lgsa_status dsa_index_topk_workspace(const lgsa_index_args* a, size_t* bytes);
 

@@ -141,7 +141,9 @@ def _idx(**kw):
 @pytest.mark.parametrize("kw,code,msg", [
     (dict(S=0), lgsa.LGSA_EINVAL, ">= 1"),
     (dict(k=0), lgsa.LGSA_EINVAL, ">= 1"),
-    (dict(max_pos=4096), lgsa.LGSA_EINVAL, "below S"),
+    (dict(max_pos=4096), lgsa.LGSA_EINVAL, "every visible key must exist"),
+    (dict(max_pos=4096 * 4 + 3, block=4), lgsa.LGSA_EINVAL, "every visible key must exist"),
+    (dict(block=-1), lgsa.LGSA_EINVAL, "block must be >= 0"),
     (dict(max_pos=100), lgsa.LGSA_EINVAL, "max_pos"),
     (dict(idx_out=None), lgsa.LGSA_EINVAL, "non-NULL"),
     (dict(di=128), lgsa.LGSA_EUNSUPPORTED, "di"),
@@ -153,6 +155,19 @@ def test_index_validation(lib, kw, code, msg):
     a = _idx(**kw)
     assert _call(lib, "dsa_index_topk", a) == code
     assert msg in lgsa.last_error()
+
+
+def test_index_block_bounds_the_keys(lib):
+    """With block 4, (max_pos + 1) / 4 keys must exist: S = 1024 serves max_pos up to 4098
+    (the call then only lacks its workspace), and the recommended workspace holds the scores of
+    that many keys per query chunk."""
+    n4, n1 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    a4 = _idx(S=1024, max_pos=4098, block=4)
+    assert _call(lib, "dsa_index_topk", a4) == lgsa.LGSA_EWORKSPACE
+    assert lib.dsa_index_topk_workspace(ctypes.byref(a4), ctypes.byref(n4)) == lgsa.LGSA_OK
+    a1 = _idx(S=4096, max_pos=4095)
+    assert lib.dsa_index_topk_workspace(ctypes.byref(a1), ctypes.byref(n1)) == lgsa.LGSA_OK
+    assert n4.value * 4 == n1.value
 
 
 def test_index_workspace(lib):
