@@ -229,6 +229,38 @@ def run_c3(torch, lgsa, synth, to_dev, iters):
                 sparse_flops=sp_flops, index_flops=float(ind_flops))
 
 
+def run_csa(torch, lgsa, synth, to_dev, iters):
+    """The compressed sparse attention variant at the DSA prefill shape: 65536 positions, 64
+    heads, d 256 (bf16), keys and values pooled 4x (16384 entries), the indexer (4 heads x 64,
+    fp32) over the entries each query can see, top-2048, gated.  One step = the three library
+    calls of csa_attn_fwd."""
+    T, H, d, k, block = 65536, 64, 256, 2048, 4
+    log("[bench] CSA: generating inputs (seq %d, block %d, top-%d)" % (T, block, k))
+    x = synth.csa(5, B=1, T=T, H=H)
+    dx = {k_: to_dev(v) for k_, v in x.items()}
+    tm = Timer(torch, torch.cuda.current_stream())
+
+    def step():
+        return lgsa.csa_attn_fwd(dx["q"], dx["pos0"], dx["kv_lat"], dx["v_lat"], dx["q_idx"],
+                                 dx["w_idx"], dx["k_idx"], k, max_pos=T - 1, block=block,
+                                 q_lat=dx["q_lat"], w_gate=dx["w_gate"])
+
+    step()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(iters):
+        a = tm.event()
+        step()
+        b = tm.event()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    ne = [(t + 1) // block for t in range(T)]
+    att_pairs = float(sum(min(k, n) for n in ne))
+    ind_pairs = float(sum(ne))
+    flops = 4.0 * d * att_pairs * H + 2.0 * T * 1024 * H * d + ind_pairs * (4 * 2 * 64 + 8)
+    return dict(ms=float(np.median(ms)), flops=flops)
+
+
 def run_c4(torch, lgsa, synth, to_dev, iters):
     B, ctx, H = 8, 1 << 20, 64
     log("[bench] C4: generating inputs (batch %d, context %d)" % (B, ctx))
@@ -467,6 +499,10 @@ def main():
             sparse_mfma_frac=round(sp_tf / PEAK_BF16_TFLOPS, 4),
             indexer_ms=round(r3["index_ms"], 3), indexer_TFLOPs=round(ix_tf, 1),
             indexer_fp32_frac=round(ix_tf / PEAK_FP32_TFLOPS, 4))
+    if 3 in cfgs:
+        rc = run_csa(torch, lgsa, synth, to_dev, 3)
+        tf = rc["flops"] / (rc["ms"] * 1e-3) / 1e12
+        secondary["csa_prefill"] = dict(ms=round(rc["ms"], 3), TFLOPs=round(tf, 1))
     if 4 in cfgs:
         r4 = run_c4(torch, lgsa, synth, to_dev, 30)
         gbps = r4["bytes"] / (r4["ms"] * 1e-3) / 1e9

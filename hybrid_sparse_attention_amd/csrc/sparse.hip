@@ -32,12 +32,15 @@ constexpr int TILE = KT * TROW;         // 16 KiB
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LAZY = 8.0f;            // rescale O only when the max grows by more (log2)
 constexpr float NEG_BIG = -1.0e30f;     // masked logit (finite: no inf - inf)
-constexpr int NW = 2;                   // waves per workgroup
-constexpr int NHB = 64 / (16 * NW);     // 16-head blocks per wave
+// Waves per workgroup: two of 32 heads when one gathered tile serves as keys and values, four
+// of 16 heads when a second (value) tile is gathered beside it (its LDS then allows two
+// workgroups per CU, and four waves keep eight waves on the CU).
+template <bool ALIAS> constexpr int waves_of() { return ALIAS ? 2 : 4; }
 
 // chunk swizzle of row r: rows 0..7 -> 0, 2, .., 14; rows 8..15 -> 1, 3, .., 15 (period 16)
 __device__ __forceinline__ int sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
+template <int NHB>
 struct WaveState {
   f32x4_t o[NHB][16];  // o[hb][cb][r] = O[head 16hb + l16][16cb + 4g + r]
   float m[NHB];        // reference max (log2 domain)
@@ -47,6 +50,7 @@ struct WaveState {
 // Gather one tile: DMA instruction i (of 16) loads tile rows 2i (lanes 0..31) and 2i + 1
 // (lanes 32..63); wave w issues i = w, w + NW, ...  `ix` holds, in lane j < 32, the position
 // of tile row j (-1 when skipped: the row is then read from position 0 and masked).
+template <int NW>
 __device__ __forceinline__ void gather_tile(const uint16_t* rows, long long stride, int ix,
                                             char* tile, int w, int lane) {
   const int hi = lane >> 5;
@@ -71,6 +75,7 @@ __device__ __forceinline__ int load_ix(const int32_t* idx, int j0, int j_end, in
 // the entry as a position, or -1 when it is skipped (negative or beyond the rows held)
 __device__ __forceinline__ int valid_ix(int s, int S) { return (s >= 0 && s < S) ? s : -1; }
 
+template <int NHB>
 __device__ __forceinline__ void scores(f32x4_t (&s)[NHB][2], const Frag8 (&qf)[NHB][8],
                                        const char* kt, const int (&kb)[4]) {
 #pragma unroll
@@ -89,7 +94,8 @@ __device__ __forceinline__ void scores(f32x4_t (&s)[NHB][2], const Frag8 (&qf)[N
   }
 }
 
-__device__ __forceinline__ void softmax_pv(WaveState& st, const f32x4_t (&s)[NHB][2],
+template <int NHB>
+__device__ __forceinline__ void softmax_pv(WaveState<NHB>& st, const f32x4_t (&s)[NHB][2],
                                            const char* vt, uint32_t valid, float scale_log2,
                                            int vrow, int vsw, int vh, int lane) {
   const int g = lane >> 4;
@@ -154,10 +160,12 @@ __device__ __forceinline__ void store4(uint16_t* dst, const f32x4_t& v) {
 // grid: (row r = b*Tq + i) x (head group of 64) x (split); n_split == 1 writes out directly.
 // ALIAS: the value rows are the key rows (one gathered tile per step); otherwise a second tile
 // of value rows is gathered beside it.
-// Two waves per SIMD (four workgroups per CU): the register budget is 256 per lane.
+// Two waves per SIMD: the register budget is 256 per lane.
 template <bool ALIAS>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void
-sparse_kernel(SparseParams p, int n_split, int chunk, float* part_o, float* part_ml) {
+__global__ __launch_bounds__(64 * waves_of<ALIAS>()) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void sparse_kernel(SparseParams p, int n_split, int chunk, float* part_o, float* part_ml) {
+  constexpr int NW = waves_of<ALIAS>();
+  constexpr int NHB = 64 / (16 * NW);  // 16-head blocks per wave
   __shared__ __attribute__((aligned(1024))) char kt0[TILE];
   __shared__ __attribute__((aligned(1024))) char kt1[TILE];
   __shared__ __attribute__((aligned(1024))) char vt0[ALIAS ? 16 : TILE];
@@ -181,7 +189,7 @@ sparse_kernel(SparseParams p, int n_split, int chunk, float* part_o, float* part
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) qf[hb][kk].u = *(const uint4*)(qr + 32 * kk + 8 * g);
   }
-  WaveState st;
+  WaveState<NHB> st;
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
 #pragma unroll
@@ -210,8 +218,8 @@ sparse_kernel(SparseParams p, int n_split, int chunk, float* part_o, float* part
   const int ix_cur = valid_ix(load_ix(idx, j_begin, j_end, lane), p.S);
   uint32_t valid_cur = (uint32_t)__ballot(ix_cur >= 0);
   if (n_tiles > 0) {
-    gather_tile(kl, p.k_stride, ix_cur, kt0, wave, lane);
-    if (!ALIAS) gather_tile(vl, p.v_stride, ix_cur, vt0, wave, lane);
+    gather_tile<NW>(kl, p.k_stride, ix_cur, kt0, wave, lane);
+    if (!ALIAS) gather_tile<NW>(vl, p.v_stride, ix_cur, vt0, wave, lane);
   }
   int ix_nxt = load_ix(idx, j_begin + KT, j_end, lane);
   wait_all();
@@ -222,8 +230,8 @@ sparse_kernel(SparseParams p, int n_split, int chunk, float* part_o, float* part
     if (ti + 1 < n_tiles) {
       const int ixv = valid_ix(ix_nxt, p.S);
       valid_nxt = (uint32_t)__ballot(ixv >= 0);
-      gather_tile(kl, p.k_stride, ixv, kn, wave, lane);
-      if (!ALIAS) gather_tile(vl, p.v_stride, ixv, vn, wave, lane);
+      gather_tile<NW>(kl, p.k_stride, ixv, kn, wave, lane);
+      if (!ALIAS) gather_tile<NW>(vl, p.v_stride, ixv, vn, wave, lane);
     }
     const int ix_after = load_ix(idx, j_begin + KT * (ti + 2), j_end, lane);
     f32x4_t s[NHB][2];
@@ -326,11 +334,11 @@ hipError_t launch_sparse(const SparseParams& p, hipStream_t stream) {
   const long long grid = rows * (p.H / 64) * n_split;
   const bool alias = p.v_lat == p.k_lat && p.v_stride == p.k_stride;
   if (alias)
-    hipLaunchKernelGGL(sparse_kernel<true>, dim3((unsigned)grid), dim3(64 * NW), 0, stream, p,
-                       n_split, chunk, part_o, part_ml);
+    hipLaunchKernelGGL(sparse_kernel<true>, dim3((unsigned)grid), dim3(64 * waves_of<true>()), 0,
+                       stream, p, n_split, chunk, part_o, part_ml);
   else
-    hipLaunchKernelGGL(sparse_kernel<false>, dim3((unsigned)grid), dim3(64 * NW), 0, stream, p,
-                       n_split, chunk, part_o, part_ml);
+    hipLaunchKernelGGL(sparse_kernel<false>, dim3((unsigned)grid), dim3(64 * waves_of<false>()), 0,
+                       stream, p, n_split, chunk, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (n_split > 1) {
