@@ -261,6 +261,35 @@ def run_csa(torch, lgsa, synth, to_dev, iters):
     return dict(ms=float(np.median(ms)), flops=flops)
 
 
+def run_gate_bwd(torch, lgsa, iters):
+    """Backward of the gate at the HCA prefill model shape (32768 rows x 32768 channels, d_lat
+    1024, bf16): the recomputed gate with the elementwise gradients, then dq_lat = dG W^T and
+    dW = q_lat^T dG.  Inputs are device-side N(0,1) draws from a seeded generator (W scaled by
+    0.02), the shapes of the forward's."""
+    M, N, d_lat = 32768, 32768, 1024
+    g = torch.Generator(device="cuda").manual_seed(7)
+    bf = torch.bfloat16
+    ql = torch.randn(M, d_lat, device="cuda", generator=g).to(bf)
+    w = (torch.randn(d_lat, N, device="cuda", generator=g) * 0.02).to(bf)
+    o = torch.randn(M, N, device="cuda", generator=g).to(bf)
+    dout = torch.randn(M, N, device="cuda", generator=g).to(bf)
+    d_o, dq, dw = torch.empty_like(o), torch.empty_like(ql), torch.empty_like(w)
+    ws = torch.empty(M * N * 2, dtype=torch.uint8, device="cuda")
+    tm = Timer(torch, torch.cuda.current_stream())
+    lgsa.latent_gate_bwd(ql, w, o, dout, d_o, dq, dw, workspace=ws)
+    torch.cuda.synchronize()
+    a = tm.event()
+    for _ in range(iters):
+        lgsa.latent_gate_bwd(ql, w, o, dout, d_o, dq, dw, workspace=ws)
+    b = tm.event()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / iters
+    flops = 3 * 2.0 * M * N * d_lat
+    del ql, w, o, dout, d_o, dq, dw, ws
+    return dict(ms=round(ms, 3), TFLOPs=round(flops / (ms * 1e-3) / 1e12, 1),
+                mfma_frac=round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+
+
 def run_c4(torch, lgsa, synth, to_dev, iters):
     B, ctx, H = 8, 1 << 20, 64
     log("[bench] C4: generating inputs (batch %d, context %d)" % (B, ctx))
@@ -488,6 +517,7 @@ def main():
                                           hbm_frac=round(gbps / PEAK_HBM_GBPS, 4),
                                           bytes=r2["bytes"])
     secondary["vha_mix_prefill"] = run_vha(torch, lgsa, synth, to_dev, 10)
+    secondary["gate_bwd_prefill"] = run_gate_bwd(torch, lgsa, 3)
     if 2 in cfgs or 4 in cfgs:
         secondary["decode_cache_append"] = run_append(torch, lgsa, synth, to_dev, 50)
     if 3 in cfgs:

@@ -23,7 +23,7 @@ LGSA_F32, LGSA_BF16 = 0, 1
 EXPORTS = ["lgsa_last_error", "hca_compress", "latent_gate", "hca_attn_fwd",
            "hca_attn_fwd_workspace", "dsa_index_topk", "dsa_index_topk_workspace",
            "sparse_attn_fwd", "sparse_attn_fwd_workspace", "hca_cache_append",
-           "dsa_cache_append", "vha_mix"]
+           "dsa_cache_append", "vha_mix", "latent_gate_bwd", "latent_gate_bwd_workspace"]
 
 
 class LibraryMissing(RuntimeError):
@@ -95,6 +95,9 @@ def load():
             getattr(lib, name + "_workspace").argtypes = [ctypes.POINTER(st),
                                                           ctypes.POINTER(_SZ)]
         lib.vha_mix.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
+        lib.latent_gate_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _SZ,
+                                        _P]
+        lib.latent_gate_bwd_workspace.argtypes = [_I, _I, _I, _I, ctypes.POINTER(_SZ)]
         lib.hca_cache_append.argtypes = [ctypes.POINTER(HcaAppendArgs), _P]
         lib.dsa_cache_append.argtypes = [ctypes.POINTER(DsaAppendArgs), _P]
         for name in EXPORTS[1:]:
@@ -310,6 +313,34 @@ def sparse_attn_fwd(q, k_lat, idx, v_lat=None, *, scale=None, q_lat=None, w_gate
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("sparse_attn_fwd", load().sparse_attn_fwd(ctypes.byref(a), _stream(stream)))
     return out
+
+
+def latent_gate_bwd(q_lat, w_gate, o, dout, d_o=None, dq_lat=None, dw_gate=None, *,
+                    workspace=None, stream=None):
+    """Backward of latent_gate: (d_o, dq_lat, dw_gate) for the loss gradient dout with respect
+    to out = o * sigmoid(q_lat @ w_gate); see include/lgsa.h."""
+    torch = _torch()
+    M, d_lat = q_lat.shape
+    N = w_gate.shape[1]
+    if d_o is None:
+        d_o = torch.empty_like(o)
+    if dq_lat is None:
+        dq_lat = torch.empty_like(q_lat)
+    if dw_gate is None:
+        dw_gate = torch.empty_like(w_gate)
+    n = _SZ(0)
+    _check("latent_gate_bwd_workspace",
+           load().latent_gate_bwd_workspace(M, d_lat, N, _dt(o), ctypes.byref(n)))
+    if workspace is None:
+        workspace, _ = _workspace(n.value, o.device)
+    rc = load().latent_gate_bwd(_dev(q_lat, "q_lat"), _dev(w_gate, "w_gate"), _dev(o, "o"),
+                                _dev(dout, "dout"), _dev(d_o, "d_o"), _dev(dq_lat, "dq_lat"),
+                                _dev(dw_gate, "dw_gate"), M, d_lat, N, _dt(o),
+                                None if workspace is None else workspace.data_ptr(),
+                                0 if workspace is None else
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("latent_gate_bwd", rc)
+    return d_o, dq_lat, dw_gate
 
 
 def csa_attn_fwd(q, pos0, k, v, q_idx, w_idx, k_idx, k_top, *, max_pos, block=4, q_lat=None,

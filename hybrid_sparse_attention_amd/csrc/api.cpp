@@ -329,6 +329,48 @@ lgsa_status latent_gate(const void* q_lat, const void* w_gate, const void* o, vo
                     "latent_gate");
 }
 
+lgsa_status latent_gate_bwd_workspace(int M, int d_lat, int N, int dt, size_t* bytes) {
+  REQUIRE(bytes != nullptr, LGSA_EINVAL, "latent_gate_bwd_workspace: bytes is NULL");
+  REQUIRE(dt == LGSA_F32 || dt == LGSA_BF16, LGSA_EINVAL, "latent_gate_bwd: unknown dt %d", dt);
+  REQUIRE(M >= 0 && d_lat >= 1 && N >= 1, LGSA_EINVAL,
+          "latent_gate_bwd: M must be >= 0 and d_lat, N >= 1");
+  *bytes = (size_t)M * (size_t)N * (dt == LGSA_BF16 ? 2 : 4);
+  return ok();
+}
+
+lgsa_status latent_gate_bwd(const void* q_lat, const void* w_gate, const void* o,
+                            const void* dout, void* d_o, void* dq_lat, void* dw_gate, int M,
+                            int d_lat, int N, int dt, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  size_t need = 0;
+  const lgsa_status s = latent_gate_bwd_workspace(M, d_lat, N, dt, &need);
+  if (s != LGSA_OK) return s;
+  REQUIRE(q_lat && w_gate && o && dout && d_o && dq_lat && dw_gate, LGSA_EINVAL,
+          "latent_gate_bwd: q_lat, w_gate, o, dout, d_o, dq_lat, dw_gate must be non-NULL");
+  if (dt == LGSA_BF16) {
+    REQUIRE(d_lat % 64 == 0 && N % 16 == 0, LGSA_EUNSUPPORTED,
+            "latent_gate_bwd: bf16 needs d_lat %% 64 == 0 and N %% 16 == 0 (got %d, %d)", d_lat,
+            N);
+  }
+  REQUIRE(aligned(q_lat, 16) && aligned(w_gate, 16) && aligned(o, 16) && aligned(dout, 16) &&
+              aligned(d_o, 16) && aligned(dq_lat, 16) && aligned(dw_gate, 16),
+          LGSA_EINVAL, "latent_gate_bwd: every tensor must be 16-byte aligned");
+  const lgsa_status w = check_workspace("latent_gate_bwd", workspace, workspace_bytes, need);
+  if (w != LGSA_OK) return w;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = lgsa::launch_gate_bwd_elem(q_lat, w_gate, o, dout, d_o, workspace, M, d_lat,
+                                            N, dt, st);
+  // dq_lat [M, d_lat] = dG [M, N] (k-contiguous) x W^T (W rows are d_lat, k-contiguous)
+  if (e == hipSuccess)
+    e = lgsa::launch_gemm(workspace, N, false, w_gate, N, false, dq_lat, d_lat, M, d_lat, N, dt,
+                          st);
+  // dw_gate [d_lat, N] = q_lat^T (k-major, k = rows of q_lat) x dG (k-major)
+  if (e == hipSuccess)
+    e = lgsa::launch_gemm(q_lat, d_lat, true, workspace, N, true, dw_gate, N, d_lat, N, M, dt,
+                          st);
+  return hip_status(e, "latent_gate_bwd");
+}
+
 lgsa_status hca_attn_fwd_workspace(const lgsa_hca_args* a, size_t* bytes) {
   REQUIRE(bytes != nullptr, LGSA_EINVAL, "hca_attn_fwd_workspace: bytes is NULL");
   const lgsa_status s = check_hca(a);

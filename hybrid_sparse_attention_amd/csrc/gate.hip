@@ -38,10 +38,14 @@ __device__ __forceinline__ void store16_nt(void* p, uint4 v) {
   __builtin_nontemporal_store(t, (u32x4_t*)p);
 }
 
+// BWD: the backward's first step on the same recomputed G: with s = sigmoid(G), out receives
+// dout * s (the gradient of o) and dg receives dout * o * s * (1 - s) (the gradient of G).
+template <bool BWD>
 __global__ __launch_bounds__(256) void gate_bf16_kernel(const uint16_t* __restrict__ ql,
                                                         const uint16_t* __restrict__ w,
                                                         const uint16_t* o, uint16_t* out,
-                                                        int M, int d_lat, int N) {
+                                                        int M, int d_lat, int N,
+                                                        const uint16_t* dout, uint16_t* dg) {
   __shared__ __attribute__((aligned(16))) uint16_t sW[2][GT_N * GT_LD];
   __shared__ __attribute__((aligned(16))) uint16_t sQ[2][GT_M * GT_LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -134,6 +138,22 @@ __global__ __launch_bounds__(256) void gate_bf16_kernel(const uint16_t* __restri
       const uint2 ov = *(const uint2*)(o + off);
       const float o0 = __uint_as_float(ov.x << 16), o1 = __uint_as_float(ov.x & 0xFFFF0000u);
       const float o2 = __uint_as_float(ov.y << 16), o3 = __uint_as_float(ov.y & 0xFFFF0000u);
+      if constexpr (BWD) {
+        const uint2 dv = *(const uint2*)(dout + off);
+        const float d[4] = {__uint_as_float(dv.x << 16), __uint_as_float(dv.x & 0xFFFF0000u),
+                            __uint_as_float(dv.y << 16), __uint_as_float(dv.y & 0xFFFF0000u)};
+        const float ox[4] = {o0, o1, o2, o3};
+        float s4[4], g4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s4[r] = sigmoidf_fast(acc[i][j][r]);
+          g4[r] = d[r] * ox[r] * s4[r] * (1.f - s4[r]);
+          s4[r] *= d[r];
+        }
+        *(uint2*)(out + off) = make_uint2(pack_bf16x2(s4[0], s4[1]), pack_bf16x2(s4[2], s4[3]));
+        *(uint2*)(dg + off) = make_uint2(pack_bf16x2(g4[0], g4[1]), pack_bf16x2(g4[2], g4[3]));
+        continue;
+      }
       uint2 r;
       r.x = pack_bf16x2(o0 * sigmoidf_fast(acc[i][j][0]), o1 * sigmoidf_fast(acc[i][j][1]));
       r.y = pack_bf16x2(o2 * sigmoidf_fast(acc[i][j][2]), o3 * sigmoidf_fast(acc[i][j][3]));
@@ -459,10 +479,12 @@ __global__ __launch_bounds__(256) void gate_bf16_skinny_kernel(const uint16_t* _
 }
 
 // fp32: 64x64 output tile, each of 256 threads computes a 4x4 block.
+template <bool BWD>  // as gate_bf16_kernel
 __global__ __launch_bounds__(256) void gate_f32_kernel(const float* __restrict__ ql,
                                                        const float* __restrict__ w,
                                                        const float* o, float* out, int M,
-                                                       int d_lat, int N) {
+                                                       int d_lat, int N, const float* dout,
+                                                       float* dg) {
   __shared__ float sQ[16][64 + 1];
   __shared__ float sW[16][64];
   const int tid = threadIdx.x;
@@ -502,7 +524,13 @@ __global__ __launch_bounds__(256) void gate_f32_kernel(const float* __restrict__
       const int n = n0 + tn + j;
       if (n >= N) continue;
       const size_t off = (size_t)m * N + n;
-      out[off] = o[off] / (1.0f + expf(-acc[i][j]));
+      if constexpr (BWD) {
+        const float sg = 1.0f / (1.0f + expf(-acc[i][j]));
+        dg[off] = dout[off] * o[off] * sg * (1.0f - sg);
+        out[off] = dout[off] * sg;
+      } else {
+        out[off] = o[off] / (1.0f + expf(-acc[i][j]));
+      }
     }
   }
 }
@@ -523,13 +551,34 @@ hipError_t launch_gate(const void* q_lat, const void* w, const void* o, void* ou
                        (uint16_t*)out, M, N);
   } else if (dt == DT_BF16) {
     const int grid = ((N + GT_N - 1) / GT_N) * ((M + GT_M - 1) / GT_M);
-    hipLaunchKernelGGL(gate_bf16_kernel, dim3(grid), dim3(256), 0, stream,
+    hipLaunchKernelGGL(gate_bf16_kernel<false>, dim3(grid), dim3(256), 0, stream,
                        (const uint16_t*)q_lat, (const uint16_t*)w, (const uint16_t*)o,
-                       (uint16_t*)out, M, d_lat, N);
+                       (uint16_t*)out, M, d_lat, N, nullptr, nullptr);
   } else {
     const int grid = ((N + 63) / 64) * ((M + 63) / 64);
-    hipLaunchKernelGGL(gate_f32_kernel, dim3(grid), dim3(256), 0, stream, (const float*)q_lat,
-                       (const float*)w, (const float*)o, (float*)out, M, d_lat, N);
+    hipLaunchKernelGGL(gate_f32_kernel<false>, dim3(grid), dim3(256), 0, stream,
+                       (const float*)q_lat, (const float*)w, (const float*)o, (float*)out, M,
+                       d_lat, N, nullptr, nullptr);
+  }
+  return hipGetLastError();
+}
+
+// Backward, first step: G recomputed as in the forward, then do = dout * s into d_o and
+// dG = dout * o * s * (1 - s) into dg (same dtype as the operands).
+hipError_t launch_gate_bwd_elem(const void* q_lat, const void* w, const void* o,
+                                const void* dout, void* d_o, void* dg, int M, int d_lat, int N,
+                                int dt, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  if (dt == DT_BF16) {
+    const int grid = ((N + GT_N - 1) / GT_N) * ((M + GT_M - 1) / GT_M);
+    hipLaunchKernelGGL(gate_bf16_kernel<true>, dim3(grid), dim3(256), 0, stream,
+                       (const uint16_t*)q_lat, (const uint16_t*)w, (const uint16_t*)o,
+                       (uint16_t*)d_o, M, d_lat, N, (const uint16_t*)dout, (uint16_t*)dg);
+  } else {
+    const int grid = ((N + 63) / 64) * ((M + 63) / 64);
+    hipLaunchKernelGGL(gate_f32_kernel<true>, dim3(grid), dim3(256), 0, stream,
+                       (const float*)q_lat, (const float*)w, (const float*)o, (float*)d_o, M,
+                       d_lat, N, (const float*)dout, (float*)dg);
   }
   return hipGetLastError();
 }

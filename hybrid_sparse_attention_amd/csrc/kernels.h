@@ -27,6 +27,14 @@ hipError_t launch_vha(const void* o, const void* u, const void* v, void* out, in
                       int d, int r, int dt, hipStream_t stream);
 
 // out[m, n] = o[m, n] * sigmoid(q_lat[m, :] . w[:, n]); out may equal o.
+// Backward, first step of the gate: do = dout * s into d_o, dG = dout * o * s * (1 - s) into dg.
+hipError_t launch_gate_bwd_elem(const void* q_lat, const void* w, const void* o,
+                                const void* dout, void* d_o, void* dg, int M, int d_lat, int N,
+                                int dt, hipStream_t stream);
+// C[m][n] = sum_k A(m, k) B(k, n) (see gemm.hip for the two operand layouts).
+hipError_t launch_gemm(const void* a, long long lda, bool a_kmajor, const void* b,
+                       long long ldb, bool b_kmajor, void* c, long long ldc, int M, int N, int K,
+                       int dt, hipStream_t stream);
 hipError_t launch_gate(const void* q_lat, const void* w, const void* o, void* out, int M,
                        int d_lat, int N, int dt, hipStream_t stream);
 

@@ -83,6 +83,26 @@ lgsa_status latent_gate(const void* q_lat, const void* w_gate, const void* o, vo
                         int d_lat, int N, int dt, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * latent_gate_bwd -- backward of latent_gate (the chain rule of its definition): with
+ * G = q_lat w_gate and s = sigmoid(G), so that out = o * s, and dout the gradient of a loss
+ * with respect to out,
+ *     d_o = dout * s,   dG = dout * o * s * (1 - s),   dq_lat = dG w_gate^T,   dw_gate = q_lat^T dG.
+ *   q_lat [M, d_lat], w_gate [d_lat, N], o and dout [M, N] (dt, read);
+ *   d_o [M, N], dq_lat [M, d_lat], dw_gate [d_lat, N] (dt, written; d_o may equal dout).
+ * G is recomputed, not stored by the forward.  dG is kept in the workspace, in dt:
+ * latent_gate_bwd_workspace() bytes (M * N elements).  fp32 accumulation; the bf16 path rounds
+ * dG to bf16 before the two products.  Supported: as latent_gate (LGSA_BF16: d_lat % 64 == 0,
+ * N % 16 == 0, every pointer 16-byte aligned).  Errors: LGSA_EINVAL for NULL or misaligned
+ * pointers and bad sizes, LGSA_EWORKSPACE for a missing or short workspace; nothing is
+ * enqueued on error.  M == 0 writes zeros to dw_gate.
+ * --------------------------------------------------------------------------------------- */
+lgsa_status latent_gate_bwd(const void* q_lat, const void* w_gate, const void* o,
+                            const void* dout, void* d_o, void* dq_lat, void* dw_gate, int M,
+                            int d_lat, int N, int dt, void* workspace, size_t workspace_bytes,
+                            void* stream);
+lgsa_status latent_gate_bwd_workspace(int M, int d_lat, int N, int dt, size_t* bytes);
+
+/* ---------------------------------------------------------------------------------------
  * hca_attn_fwd -- Heavily Compressed Attention forward (release blog, section 2.1; window
  * size from the xenospectrum.com article).  Query row i of sequence b sits at position
  * t = pos0[b] + i and attends, with one shared key/value head for all H query heads, to

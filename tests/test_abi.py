@@ -295,3 +295,34 @@ def test_vha_validation(lib):
     assert f(FAKE_ODD, FAKE, FAKE, FAKE, 4, 64, 512, 16, 1, None) == lgsa.LGSA_EINVAL
     assert "aligned" in lgsa.last_error()
     assert f(FAKE, FAKE, FAKE, FAKE, 0, 64, 512, 16, 1, None) == lgsa.LGSA_OK  # M == 0: no work
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(dt=7), lgsa.LGSA_EINVAL, "unknown dt"),
+    (dict(M=-1), lgsa.LGSA_EINVAL, ">= 0"),
+    (dict(dq_lat=None), lgsa.LGSA_EINVAL, "non-NULL"),
+    (dict(d_lat=96), lgsa.LGSA_EUNSUPPORTED, "d_lat % 64"),
+    (dict(o=FAKE_ODD), lgsa.LGSA_EINVAL, "aligned"),
+    (dict(workspace=None), lgsa.LGSA_EWORKSPACE, "workspace"),
+    (dict(workspace_bytes=64 * 32 * 2 - 1), lgsa.LGSA_EWORKSPACE, "below"),
+])
+def test_gate_bwd_validation(lib, kw, code, msg):
+    """Invalid arguments are refused before anything is enqueued (the pointers are never
+    dereferenced: the calls fail on the host)."""
+    a = dict(q_lat=FAKE, w_gate=FAKE, o=FAKE, dout=FAKE, d_o=FAKE, dq_lat=FAKE, dw_gate=FAKE,
+             M=64, d_lat=64, N=32, dt=lgsa.LGSA_BF16, workspace=FAKE, workspace_bytes=64 * 32 * 2)
+    a.update(kw)
+    rc = lib.latent_gate_bwd(a["q_lat"], a["w_gate"], a["o"], a["dout"], a["d_o"], a["dq_lat"],
+                             a["dw_gate"], a["M"], a["d_lat"], a["N"], a["dt"], a["workspace"],
+                             a["workspace_bytes"], None)
+    assert rc == code
+    assert msg in lgsa.last_error()
+
+
+def test_gate_bwd_workspace_size(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.latent_gate_bwd_workspace(100, 64, 48, lgsa.LGSA_BF16, ctypes.byref(n)) == 0
+    assert n.value == 100 * 48 * 2
+    assert lib.latent_gate_bwd_workspace(100, 64, 48, lgsa.LGSA_F32, ctypes.byref(n)) == 0
+    assert n.value == 100 * 48 * 4
+
