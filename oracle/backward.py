@@ -70,7 +70,7 @@ def hca_attn_bwd(q, pos0, k, v, dout, *, window=128, block=128, scale=None):
     dv = np.zeros_like(V)
     for b in range(B):
         kc = K[b, :ne_all * block].reshape(ne_all, block, d).mean(axis=1)
-        vc = V[b, :ne_all * block].reshape(ne_all, block, -1).mean(axis=1)
+        vc = V[b, :ne_all * block].reshape(ne_all, block, V.shape[-1]).mean(axis=1)
         dkc = np.zeros_like(kc)
         dvc = np.zeros_like(vc)
         for i in range(Tq):

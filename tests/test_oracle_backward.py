@@ -72,6 +72,23 @@ def test_hca_backward_matches_finite_differences(orc):
     assert np.allclose(dv, _fd(loss, v), rtol=1e-5, atol=1e-7)
 
 
+def test_hca_backward_without_a_complete_block(orc):
+    """A sequence shorter than a block: only the window path, no entry at all."""
+    rng = np.random.default_rng(85)
+    B, T, H, d, block, window = 1, 3, 2, 4, 4, 2
+    q = rng.standard_normal((B, T, H, d))
+    k = rng.standard_normal((B, T, d))
+    v = rng.standard_normal((B, T, d))
+    dout = rng.standard_normal((B, T, H, d))
+    pos0 = np.zeros(B, np.int32)
+    loss = lambda: float(np.sum(dout.reshape(B * T, H, d) *
+                                orc.hca_attn(q, pos0, k, v, window=window, block=block)))
+    dq, dk, dv = backward.hca_attn_bwd(q, pos0, k, v, dout, window=window, block=block)
+    assert np.allclose(dq, _fd(loss, q), rtol=1e-5, atol=1e-7)
+    assert np.allclose(dk, _fd(loss, k), rtol=1e-5, atol=1e-7)
+    assert np.allclose(dv, _fd(loss, v), rtol=1e-5, atol=1e-7)
+
+
 def test_sparse_backward_matches_finite_differences(orc):
     """Latent rows serving as both keys and values (V = K), with a repeated and a skipped entry
     in the lists; then distinct value rows."""
