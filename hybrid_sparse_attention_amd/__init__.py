@@ -23,7 +23,8 @@ LGSA_F32, LGSA_BF16 = 0, 1
 EXPORTS = ["lgsa_last_error", "hca_compress", "latent_gate", "hca_attn_fwd",
            "hca_attn_fwd_workspace", "dsa_index_topk", "dsa_index_topk_workspace",
            "sparse_attn_fwd", "sparse_attn_fwd_workspace", "hca_cache_append",
-           "dsa_cache_append", "vha_mix", "latent_gate_bwd", "latent_gate_bwd_workspace"]
+           "dsa_cache_append", "vha_mix", "latent_gate_bwd", "latent_gate_bwd_workspace",
+           "hca_attn_bwd", "hca_attn_bwd_workspace"]
 
 
 class LibraryMissing(RuntimeError):
@@ -45,7 +46,14 @@ class HcaArgs(ctypes.Structure):
                 ("pos0", _P), ("max_pos", _I), ("k_win", _P), ("v_win", _P),
                 ("win_len", _I), ("window", _I), ("kc", _P), ("vc", _P), ("n_cap", _I),
                 ("block", _I), ("scale", _F), ("q_lat", _P), ("w_gate", _P), ("d_lat", _I),
-                ("out", _P), ("workspace", _P), ("workspace_bytes", _SZ)]
+                ("out", _P), ("workspace", _P), ("workspace_bytes", _SZ), ("lse", _P)]
+
+
+class HcaBwdArgs(ctypes.Structure):
+    _fields_ = [("dt", _I), ("B", _I), ("T", _I), ("H", _I), ("d", _I), ("q", _P), ("k", _P),
+                ("v", _P), ("kc", _P), ("vc", _P), ("out", _P), ("lse", _P), ("dout", _P),
+                ("window", _I), ("block", _I), ("scale", _F), ("dq", _P), ("dk", _P),
+                ("dv", _P), ("workspace", _P), ("workspace_bytes", _SZ)]
 
 
 class IndexArgs(ctypes.Structure):
@@ -90,7 +98,7 @@ def load():
         lib.hca_compress.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
         lib.latent_gate.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P]
         for name, st in (("hca_attn_fwd", HcaArgs), ("dsa_index_topk", IndexArgs),
-                         ("sparse_attn_fwd", SparseArgs)):
+                         ("sparse_attn_fwd", SparseArgs), ("hca_attn_bwd", HcaBwdArgs)):
             getattr(lib, name).argtypes = [ctypes.POINTER(st), _P]
             getattr(lib, name + "_workspace").argtypes = [ctypes.POINTER(st),
                                                           ctypes.POINTER(_SZ)]
@@ -208,13 +216,16 @@ def hca_args(q, pos0, k_win, v_win, kc=None, vc=None, *, max_pos, window=128, bl
 
 
 def hca_attn_fwd(q, pos0, k_win, v_win, kc=None, vc=None, *, max_pos, window=128, block=128,
-                 scale=None, q_lat=None, w_gate=None, out=None, workspace=None, stream=None):
-    """Heavily Compressed Attention forward (optionally gated); see include/lgsa.h."""
+                 scale=None, q_lat=None, w_gate=None, out=None, workspace=None, stream=None,
+                 lse=None):
+    """Heavily Compressed Attention forward (optionally gated); see include/lgsa.h.  lse: an
+    optional [B, Tq, H] fp32 tensor receiving each row's log-sum-exp (for hca_attn_bwd)."""
     torch = _torch()
     if out is None:
         out = torch.empty_like(q)
     a = hca_args(q, pos0, k_win, v_win, kc, vc, max_pos=max_pos, window=window, block=block,
                  scale=scale, q_lat=q_lat, w_gate=w_gate, out=out)
+    a.lse = _dev(lse, "lse")
     need = hca_attn_fwd_workspace(a)
     if workspace is None:
         workspace, _ = _workspace(need, q.device)
@@ -313,6 +324,36 @@ def sparse_attn_fwd(q, k_lat, idx, v_lat=None, *, scale=None, q_lat=None, w_gate
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("sparse_attn_fwd", load().sparse_attn_fwd(ctypes.byref(a), _stream(stream)))
     return out
+
+
+def hca_attn_bwd(q, k, v, kc, vc, out, lse, dout, *, window=128, block=128, scale=None,
+                 dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward of hca_attn_fwd in prefill (sequences from position 0, window rows = k, v):
+    returns (dq [B,T,H,d], dk [B,T,d], dv [B,T,d]); see include/lgsa.h.  out and lse are the
+    forward's (ungated) output and log-sum-exp."""
+    torch = _torch()
+    B, T, H, d = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    a = HcaBwdArgs()
+    a.dt = _dt(q)
+    a.B, a.T, a.H, a.d = B, T, H, d
+    a.q, a.k, a.v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    a.kc, a.vc = _dev(kc, "kc"), _dev(vc, "vc")
+    a.out, a.lse, a.dout = _dev(out, "out"), _dev(lse, "lse"), _dev(dout, "dout")
+    a.window, a.block = window, block
+    a.scale = 1.0 / math.sqrt(d) if scale is None else scale
+    a.dq, a.dk, a.dv = _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv")
+    n = _SZ(0)
+    _check("hca_attn_bwd_workspace", load().hca_attn_bwd_workspace(ctypes.byref(a),
+                                                                   ctypes.byref(n)))
+    if workspace is None:
+        workspace, _ = _workspace(n.value, q.device)
+    a.workspace = None if workspace is None else workspace.data_ptr()
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("hca_attn_bwd", load().hca_attn_bwd(ctypes.byref(a), _stream(stream)))
+    return dq, dk, dv
 
 
 def latent_gate_bwd(q_lat, w_gate, o, dout, d_o=None, dq_lat=None, dw_gate=None, *,

@@ -63,6 +63,7 @@ lgsa::HcaParams to_params(const lgsa_hca_args* a) {
   p.w_gate = a->w_gate;
   p.d_lat = a->d_lat;
   p.out = a->out;
+  p.lse = a->lse;
   p.ws = a->workspace;
   p.ws_bytes = a->workspace_bytes;
   return p;
@@ -85,6 +86,8 @@ lgsa_status check_hca(const lgsa_hca_args* a) {
           "hca_attn_fwd: window (%d) exceeds the rows held in k_win/v_win (%d)", a->window,
           a->win_len);
   REQUIRE(a->block >= 1, LGSA_EINVAL, "hca_attn_fwd: block must be >= 1");
+  REQUIRE(a->lse == nullptr || (a->dt == LGSA_BF16 && a->Tq > 1), LGSA_EUNSUPPORTED,
+          "hca_attn_fwd: lse is written by the bf16 path with Tq > 1 only");
   REQUIRE(a->n_cap >= 0, LGSA_EINVAL, "hca_attn_fwd: n_cap must be >= 0");
   REQUIRE(a->n_cap == 0 || (a->kc && a->vc), LGSA_EINVAL,
           "hca_attn_fwd: kc and vc must be non-NULL when n_cap > 0");
@@ -221,6 +224,51 @@ lgsa_status check_workspace(const char* name, const void* ws, size_t have, size_
   REQUIRE(need == 0 || ws != nullptr, LGSA_EWORKSPACE, "%s: workspace is NULL", name);
   REQUIRE(need == 0 || aligned(ws, 16), LGSA_EWORKSPACE, "%s: workspace must be 16-byte aligned",
           name);
+  return LGSA_OK;
+}
+
+lgsa::HcaBwdParams to_params(const lgsa_hca_bwd_args* a) {
+  lgsa::HcaBwdParams p;
+  p.B = a->B;
+  p.T = a->T;
+  p.H = a->H;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.kc = a->kc;
+  p.vc = a->vc;
+  p.out = a->out;
+  p.lse = a->lse;
+  p.dout = a->dout;
+  p.window = a->window;
+  p.block = a->block;
+  p.ne = a->block >= 1 ? a->T / a->block : 0;
+  p.scale = a->scale;
+  p.dq = a->dq;
+  p.dk = a->dk;
+  p.dv = a->dv;
+  p.ws = a->workspace;
+  p.ws_bytes = a->workspace_bytes;
+  return p;
+}
+
+lgsa_status check_hca_bwd(const lgsa_hca_bwd_args* a) {
+  REQUIRE(a != nullptr, LGSA_EINVAL, "hca_attn_bwd: args is NULL");
+  REQUIRE(a->dt == LGSA_BF16, LGSA_EUNSUPPORTED, "hca_attn_bwd: only LGSA_BF16 is supported");
+  REQUIRE(a->B >= 1 && a->T >= 1 && a->H >= 1 && a->d >= 1, LGSA_EINVAL,
+          "hca_attn_bwd: B, T, H, d must be >= 1");
+  REQUIRE(a->d == 512, LGSA_EUNSUPPORTED, "hca_attn_bwd: d must be 512 (got %d)", a->d);
+  REQUIRE(a->H % 4 == 0, LGSA_EUNSUPPORTED, "hca_attn_bwd: H must be a multiple of 4");
+  REQUIRE(a->window >= 1 && a->window <= 512 && a->block >= 1, LGSA_EINVAL,
+          "hca_attn_bwd: window must be in [1, 512] and block >= 1");
+  REQUIRE(std::isfinite(a->scale), LGSA_EINVAL, "hca_attn_bwd: scale is not finite");
+  REQUIRE(a->q && a->k && a->v && a->out && a->lse && a->dout && a->dq && a->dk && a->dv,
+          LGSA_EINVAL, "hca_attn_bwd: q, k, v, out, lse, dout, dq, dk, dv must be non-NULL");
+  REQUIRE(a->T < a->block || (a->kc && a->vc), LGSA_EINVAL,
+          "hca_attn_bwd: kc and vc must be non-NULL when a block is complete");
+  for (const void* p : {a->q, a->k, a->v, a->kc, a->vc, a->out, (const void*)a->lse, a->dout,
+                        (const void*)a->dq, (const void*)a->dk, (const void*)a->dv})
+    REQUIRE(aligned(p, 16), LGSA_EINVAL, "hca_attn_bwd: tensors must be 16-byte aligned");
   return LGSA_OK;
 }
 
@@ -369,6 +417,24 @@ lgsa_status latent_gate_bwd(const void* q_lat, const void* w_gate, const void* o
     e = lgsa::launch_gemm(q_lat, d_lat, true, workspace, N, true, dw_gate, N, d_lat, N, M, dt,
                           st);
   return hip_status(e, "latent_gate_bwd");
+}
+
+lgsa_status hca_attn_bwd_workspace(const lgsa_hca_bwd_args* a, size_t* bytes) {
+  REQUIRE(bytes != nullptr, LGSA_EINVAL, "hca_attn_bwd_workspace: bytes is NULL");
+  const lgsa_status s = check_hca_bwd(a);
+  if (s != LGSA_OK) return s;
+  *bytes = lgsa::hca_bwd_workspace(to_params(a));
+  return ok();
+}
+
+lgsa_status hca_attn_bwd(const lgsa_hca_bwd_args* a, void* stream) {
+  const lgsa_status s = check_hca_bwd(a);
+  if (s != LGSA_OK) return s;
+  const lgsa::HcaBwdParams p = to_params(a);
+  const lgsa_status w = check_workspace("hca_attn_bwd", a->workspace, a->workspace_bytes,
+                                        lgsa::hca_bwd_workspace(p));
+  if (w != LGSA_OK) return w;
+  return hip_status(lgsa::launch_hca_bwd(p, (hipStream_t)stream), "hca_attn_bwd");
 }
 
 lgsa_status hca_attn_fwd_workspace(const lgsa_hca_args* a, size_t* bytes) {

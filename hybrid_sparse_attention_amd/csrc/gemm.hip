@@ -56,12 +56,15 @@ __device__ __forceinline__ void gemm_store(uint16_t* s, int t, const uint4 (&st)
   }
 }
 
-template <bool AK, bool BK>
+// OUT_F32: C is fp32 and blockIdx.y selects a range of `kchunk` contraction indices whose
+// partial product goes to C + blockIdx.y * M * ldc (split K; the partials are summed after).
+template <bool AK, bool BK, bool OUT_F32>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restrict__ a,
                                                         long long lda,
                                                         const uint16_t* __restrict__ b,
-                                                        long long ldb, uint16_t* __restrict__ c,
-                                                        long long ldc, int M, int N, int K) {
+                                                        long long ldb, void* __restrict__ cv,
+                                                        long long ldc, int M, int N, int K,
+                                                        int kchunk) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][GM_T * GM_LD];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][GM_T * GM_LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -79,25 +82,28 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   uint4 st[8];
-  auto load = [&](int k0) {
-    if (is_a)
-      gemm_load<AK>(a, lda, m0, M, k0, K, t, st);
-    else
-      gemm_load<BK>(b, ldb, n0, N, k0, K, t, st);
-  };
   auto store = [&](int buf) {
     if (is_a)
       gemm_store<AK>(sA[buf], t, st);
     else
       gemm_store<BK>(sB[buf], t, st);
   };
-  const int nk = (K + GM_K - 1) / GM_K;
-  load(0);
+  // contraction range of this workgroup (all of K unless split)
+  const int kb = OUT_F32 ? (int)blockIdx.y * kchunk : 0;
+  const int ke = OUT_F32 ? min(K, kb + kchunk) : K;
+  const int nk = ke > kb ? (ke - kb + GM_K - 1) / GM_K : 0;
+  auto load_k = [&](int k0) {
+    if (is_a)
+      gemm_load<AK>(a, lda, m0, M, k0, ke, t, st);
+    else
+      gemm_load<BK>(b, ldb, n0, N, k0, ke, t, st);
+  };
+  load_k(kb);
   store(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * GM_K);
+    if (kt + 1 < nk) load_k(kb + (kt + 1) * GM_K);
 #pragma unroll
     for (int ks = 0; ks < GM_K / 32; ++ks) {
       Frag8 fa[4], fb[4];
@@ -125,9 +131,15 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
     for (int i = 0; i < 4; ++i) {
       const int n = n0 + wn + 16 * i + 4 * g;
       if (n >= N) continue;
-      *(uint2*)(c + (size_t)m * ldc + n) =
-          make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]),
-                     pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+      if constexpr (OUT_F32) {
+        float* c = (float*)cv + (size_t)blockIdx.y * M * ldc;
+        *(f32x4_t*)(c + (size_t)m * ldc + n) = acc[i][j];
+      } else {
+        uint16_t* c = (uint16_t*)cv;
+        *(uint2*)(c + (size_t)m * ldc + n) =
+            make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]),
+                       pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+      }
     }
   }
 }
@@ -174,9 +186,8 @@ hipError_t gemm_launch(const void* a, long long lda, const void* b, long long ld
                        long long ldc, int M, int N, int K, int dt, hipStream_t stream) {
   if (dt == DT_BF16) {
     const int grid = ((N + GM_T - 1) / GM_T) * ((M + GM_T - 1) / GM_T);
-    hipLaunchKernelGGL((gemm_bf16_kernel<AK, BK>), dim3(grid), dim3(256), 0, stream,
-                       (const uint16_t*)a, lda, (const uint16_t*)b, ldb, (uint16_t*)c, ldc, M,
-                       N, K);
+    hipLaunchKernelGGL((gemm_bf16_kernel<AK, BK, false>), dim3(grid), dim3(256), 0, stream,
+                       (const uint16_t*)a, lda, (const uint16_t*)b, ldb, c, ldc, M, N, K, K);
   } else {
     const int grid = ((N + 63) / 64) * ((M + 63) / 64);
     hipLaunchKernelGGL((gemm_f32_kernel<AK, BK>), dim3(grid), dim3(256), 0, stream,
@@ -185,7 +196,47 @@ hipError_t gemm_launch(const void* a, long long lda, const void* b, long long ld
   return hipGetLastError();
 }
 
+// Sum of `splits` fp32 partials of M x N (row stride ldc) into out (fp32, row stride ldc).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            float* __restrict__ out, int splits,
+                                                            long long n) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int k = 0; k < splits; ++k) s += part[(size_t)k * n + i];
+  out[i] = s;
+}
+
 }  // namespace
+
+hipError_t launch_gemm_splitk_f32(const void* a, long long lda, bool a_kmajor, const void* b,
+                                  long long ldb, bool b_kmajor, float* c, int M, int N, int K,
+                                  int splits, float* part, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const int kchunk = ((K + splits - 1) / splits + GM_K - 1) / GM_K * GM_K;
+  splits = K > 0 ? (K + kchunk - 1) / kchunk : 1;
+  const dim3 grid(((N + GM_T - 1) / GM_T) * ((M + GM_T - 1) / GM_T), splits);
+  const uint16_t* pa = (const uint16_t*)a;
+  const uint16_t* pb = (const uint16_t*)b;
+  if (a_kmajor && b_kmajor)
+    hipLaunchKernelGGL((gemm_bf16_kernel<true, true, true>), grid, dim3(256), 0, stream, pa, lda,
+                       pb, ldb, (void*)part, (long long)N, M, N, K, kchunk);
+  else if (a_kmajor)
+    hipLaunchKernelGGL((gemm_bf16_kernel<true, false, true>), grid, dim3(256), 0, stream, pa, lda,
+                       pb, ldb, (void*)part, (long long)N, M, N, K, kchunk);
+  else if (b_kmajor)
+    hipLaunchKernelGGL((gemm_bf16_kernel<false, true, true>), grid, dim3(256), 0, stream, pa, lda,
+                       pb, ldb, (void*)part, (long long)N, M, N, K, kchunk);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, true>), grid, dim3(256), 0, stream, pa,
+                       lda, pb, ldb, (void*)part, (long long)N, M, N, K, kchunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long n = (long long)M * N;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     stream, part, c, splits, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const void* a, long long lda, bool a_kmajor, const void* b,
                        long long ldb, bool b_kmajor, void* c, long long ldc, int M, int N, int K,

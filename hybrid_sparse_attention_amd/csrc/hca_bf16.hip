@@ -234,11 +234,10 @@ __device__ __forceinline__ void row_softmax_pv(RowState& st, const f32x4_t (&s)[
 // buffer: tile ti is read from (k0, v0) or (k1, v1) while tile ti + 1 streams into the other
 // pair by LDS DMA.  The four buffers are separate LDS objects: the compiler can then prove that
 // reading one pair does not touch the transfers into the other and does not wait for them.
-template <class TileOf>
-__device__ __forceinline__ void row_key_loop(RowState& st, const Frag8 (&qf)[16],
-                                             const RowPos& rp, const Src& src,
-                                             const TileOf& tile_of, int n_tiles, int wave,
-                                             int n_waves, int lane, float scale_log2) {
+template <class TileOf, class Consume>
+__device__ __forceinline__ void tile_key_loop(const Src& src, const TileOf& tile_of, int n_tiles,
+                                              int wave, int n_waves, int lane,
+                                              const Consume& consume) {
   if (n_tiles > 0) {
     const Tile t0 = tile_of(0);
     dma_rows(src, t0, false, pf_k0, KLD, wave, n_waves, lane);
@@ -253,9 +252,7 @@ __device__ __forceinline__ void row_key_loop(RowState& st, const Frag8 (&qf)[16]
       dma_rows(src, tn, false, knxt, KLD, wave, n_waves, lane);
       dma_rows(src, tn, true, vnxt, VLD, wave, n_waves, lane);
     }
-    f32x4_t s[2];
-    row_scores(s, qf, kcur, lane);
-    row_softmax_pv(st, s, vcur, t, rp, scale_log2, lane);
+    consume(t, kcur, vcur);
     wait_all();  // this wave's transfers of tile ti + 1 have landed
     __syncthreads();
   };
@@ -263,6 +260,19 @@ __device__ __forceinline__ void row_key_loop(RowState& st, const Frag8 (&qf)[16]
     body(ti, pf_k0, pf_v0, pf_k1, pf_v1);
     if (ti + 1 < n_tiles) body(ti + 1, pf_k1, pf_v1, pf_k0, pf_v0);
   }
+}
+
+template <class TileOf>
+__device__ __forceinline__ void row_key_loop(RowState& st, const Frag8 (&qf)[16],
+                                             const RowPos& rp, const Src& src,
+                                             const TileOf& tile_of, int n_tiles, int wave,
+                                             int n_waves, int lane, float scale_log2) {
+  tile_key_loop(src, tile_of, n_tiles, wave, n_waves, lane,
+                [&](const Tile& t, const char* kcur, const char* vcur) {
+                  f32x4_t s[2];
+                  row_scores(s, qf, kcur, lane);
+                  row_softmax_pv(st, s, vcur, t, rp, scale_log2, lane);
+                });
 }
 
 __device__ __forceinline__ void init_row_state(RowState& st) {
@@ -350,11 +360,16 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_kernel(HcaParams p) {
   row_key_loop(st, qf, rp, src, tile_of, n_tiles, wave, 8, lane, p.scale * LOG2E);
 
   const int i = r_first + l16;
-  const float inv = final_scale(st.m, wave_sum16(st.l));
+  const float lt = wave_sum16(st.l);
+  const float inv = final_scale(st.m, lt);
   if (i < i_end && h_ok) {
     uint16_t* orow = (uint16_t*)p.out + (((size_t)b * p.Tq + i) * p.H + h) * D;
 #pragma unroll
     for (int cb = 0; cb < 32; ++cb) store4(orow + 16 * cb + 4 * g, st.o[cb] * inv);
+    // ln sum_j exp(scale s_j) = (m + log2 l) ln 2 in the log2 domain of the key loop
+    if (p.lse != nullptr && g == 0)
+      p.lse[((size_t)b * p.Tq + i) * p.H + h] =
+          inv > 0.f ? (st.m + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
   }
 }
 
@@ -483,7 +498,370 @@ void decode_plan(const HcaParams& p, int& n_split, int& chunk) {
 // prefill kernel takes groups of 4 heads and any number of rows
 bool use_decode(const HcaParams& p) { return p.Tq == 1 && p.H % 64 == 0; }
 
+// ------------------------------------------------------------------------------ backward
+// Prefill backward (every sequence from position 0).  With P = softmax of the scaled logits
+// (rebuilt from the forward's log-sum-exp), dP = dO V^T and D = rowsum(dO * O):
+//   dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO
+// over the keys of each row.  A compressed entry's gradient reaches each position of its
+// block divided by block.  Three stages:
+//   hca_bwd_dq_kernel   per (32 query tokens, 4 heads), as the forward: recomputes S and dP
+//                       tile by tile, accumulates dQ (two passes of 256 columns: Q, dO and
+//                       half of dQ fill the registers), and in its first pass writes P and
+//                       scale * dS of every (row, key) pair: for the entries to [rows][ne_pad],
+//                       for the window to [rows][window] at column t - s;
+//   entry gradients     dKc = dSc^T Q and dVc = Pc^T dO as split-K GEMMs over all rows;
+//   hca_bwd_dkv_kernel  per 32 keys: the window gradients as banded products over the query
+//                       tokens s .. s + window - 1 of every head, plus dKc / block and
+//                       dVc / block of the key's block, written as dK and dV.
+__global__ __launch_bounds__(256) void hca_bwd_delta_kernel(const uint16_t* __restrict__ dout,
+                                                            const uint16_t* __restrict__ out,
+                                                            float* __restrict__ delta,
+                                                            long long rows) {
+  const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const uint4 a = *(const uint4*)(dout + r * D + 8 * lane);
+  const uint4 o = *(const uint4*)(out + r * D + 8 * lane);
+  const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, ow[4] = {o.x, o.y, o.z, o.w};
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sum = fmaf(__uint_as_float(aw[j] << 16), __uint_as_float(ow[j] << 16), sum);
+    sum = fmaf(__uint_as_float(aw[j] & 0xFFFF0000u), __uint_as_float(ow[j] & 0xFFFF0000u), sum);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  if (lane == 0) delta[r] = sum;
+}
+
+struct BwdWs {  // workspace regions of the backward
+  float* delta;
+  uint16_t* pc;
+  uint16_t* dsc;
+  uint16_t* pw;
+  uint16_t* dsw;
+  float* dkc;
+  float* dvc;
+  float* part;
+  int ne_pad, splits;
+};
+
+__global__ __launch_bounds__(512, 1) void hca_bwd_dq_kernel(HcaBwdParams bp, BwdWs ws) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int hw = wave & 3, rh = wave >> 2;
+  const int n_hg = bp.H / 4;
+  const int n_qt = (bp.T + 31) / 32;
+  const int unit = blockIdx.x / n_hg, hgi = blockIdx.x % n_hg;
+  const int b = unit / n_qt, qt = unit % n_qt;
+  const int h = hgi * 4 + hw;
+  const int T = bp.T, W = bp.window;
+  const int i_first = qt * 32, i_end = min(T, i_first + 32);
+  const int t_first = i_first, t_last = i_end - 1;
+  const bool all_rows = i_end - i_first == 32;
+  const int ne = min(bp.ne, (t_last + 1) / bp.block);
+  const int s_lo = max(0, t_first - W + 1);
+  const int nw = t_last - s_lo + 1;
+  const int tiles_c = (ne + KT - 1) / KT, tiles_w = (nw + KT - 1) / KT;
+  const int n_tiles = tiles_c + tiles_w;
+  auto tile_of = [&](int ti) {
+    Tile t;
+    if (ti < tiles_c) {
+      t.kind = 0;
+      t.start = KT * ti;
+      t.count = min(KT, ne - t.start);
+      t.row0 = t.start;
+    } else {
+      t.kind = 1;
+      t.start = s_lo + KT * (ti - tiles_c);
+      t.count = min(KT, t_last - t.start + 1);
+      t.row0 = t.start;
+    }
+    t.full = all_rows && tile_full(t, t_first, t_last, W, bp.block);
+    return t;
+  };
+  Src src;
+  src.kc = (const char*)bp.kc + (size_t)b * bp.ne * ROWB;
+  src.vc = (const char*)bp.vc + (size_t)b * bp.ne * ROWB;
+  src.kw = (const char*)bp.k + (size_t)b * T * ROWB;
+  src.vw = (const char*)bp.v + (size_t)b * T * ROWB;
+  src.win_len = T;
+
+  const int r_first = i_first + 16 * rh;
+  RowPos rp;
+  rp.t0 = r_first;
+  rp.n_rows = i_end - r_first;
+  rp.step = 1;
+  rp.window = W;
+  rp.block = bp.block;
+  const int i = r_first + l16;
+  const bool row_ok = i < i_end;
+  const int ic = min(i, i_end - 1);
+  const size_t row = ((size_t)b * T + ic) * bp.H + h;
+  Frag8 qf[16], of[16];
+  {
+    const uint16_t* qr = (const uint16_t*)bp.q + row * D;
+    const uint16_t* dr = (const uint16_t*)bp.dout + row * D;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      qf[kk].u = *(const uint4*)(qr + 32 * kk + 8 * g);
+      of[kk].u = *(const uint4*)(dr + 32 * kk + 8 * g);
+    }
+  }
+  const float lse2 = bp.lse[row] * LOG2E;
+  const float dlt = ws.delta[row];
+  const float scale_log2 = bp.scale * LOG2E;
+  uint16_t* pc = ws.pc + row * ws.ne_pad;
+  uint16_t* dsc = ws.dsc + row * ws.ne_pad;
+  uint16_t* pw = ws.pw + row * W;
+  uint16_t* dsw = ws.dsw + row * W;
+
+  for (int hf = 0; hf < 2; ++hf) {
+    f32x4_t dq[16];
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) dq[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    tile_key_loop(src, tile_of, n_tiles, wave, 8, lane,
+                  [&](const Tile& t, const char* kcur, const char* vcur) {
+      f32x4_t sc[2], dp[2];
+      row_scores(sc, qf, kcur, lane);
+      row_scores(dp, of, vcur, lane);
+      const int tr = row_t(rp, opaque(l16));
+      float pr[2][4], ds[2][4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool vis = t.full || visible(t, 16 * mb + 4 * g + r, tr, rp);
+          pr[mb][r] = vis ? fast_exp2(sc[mb][r] * scale_log2 - lse2) : 0.f;
+          ds[mb][r] = pr[mb][r] * (dp[mb][r] - dlt);
+        }
+      if (hf == 0 && row_ok) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const int j0 = t.start + 16 * mb + 4 * g;  // keys j0 .. j0 + 3
+          if (t.kind == 0) {
+            if (j0 < ws.ne_pad) {
+              *(uint2*)(pc + j0) = make_uint2(pack_bf16x2(pr[mb][0], pr[mb][1]),
+                                              pack_bf16x2(pr[mb][2], pr[mb][3]));
+              *(uint2*)(dsc + j0) =
+                  make_uint2(pack_bf16x2(ds[mb][0] * bp.scale, ds[mb][1] * bp.scale),
+                             pack_bf16x2(ds[mb][2] * bp.scale, ds[mb][3] * bp.scale));
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int jj = i - (j0 + r);  // column t - s of the window arrays
+              if (jj >= 0 && jj < W) {
+                pw[jj] = f32_to_bf16(pr[mb][r]);
+                dsw[jj] = f32_to_bf16(ds[mb][r] * bp.scale);
+              }
+            }
+          }
+        }
+      }
+      Frag8 pf;
+      pf.u = make_uint4(pack_bf16x2(ds[0][0], ds[0][1]), pack_bf16x2(ds[0][2], ds[0][3]),
+                        pack_bf16x2(ds[1][0], ds[1][1]), pack_bf16x2(ds[1][2], ds[1][3]));
+      // dQ^T += K^T dS^T over this half's 16 column blocks (K read as V is in the forward)
+      const char* k0 = kcur + (4 * g + (l16 >> 2)) * KLD + 8 * (l16 & 3) + 512 * hf;
+#pragma unroll
+      for (int cb = 0; cb < 16; ++cb) {
+        Frag8 ka;
+        const uint2 lo = lds_read_tr16(k0 + 32 * cb);
+        const uint2 hi = lds_read_tr16(k0 + 32 * cb + 16 * KLD);
+        ka.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        dq[cb] = mfma_16x16x32(ka, pf, dq[cb]);
+      }
+    });
+    if (row_ok) {
+      uint16_t* dr = (uint16_t*)bp.dq + row * D + 256 * hf;
+#pragma unroll
+      for (int cb = 0; cb < 16; ++cb) store4(dr + 16 * cb + 4 * g, dq[cb] * bp.scale);
+    }
+  }
+  // entries past the workgroup's last tile are invisible to its rows: zeros
+  if (row_ok)
+    for (int e = tiles_c * KT + 4 * g; e < ws.ne_pad; e += 16) {
+      *(uint2*)(pc + e) = make_uint2(0u, 0u);
+      *(uint2*)(dsc + e) = make_uint2(0u, 0u);
+    }
+}
+
+constexpr int BW_CLD = 32 + 8;  // LDS row of a coefficient tile (bf16)
+
+// Window gradients of 32 keys s0 .. s0 + 31 and the final dK, dV.  Wave w owns the dims
+// 64w .. 64w + 63.  For every query-token tile of 32 and head h: the coefficient tiles
+// C[s][t] = scale dS (or P) of (t, h) at key s when 0 <= t - s < window, and the 32 rows of Q
+// (or dO) of head h go to LDS; then dK[s][c] += sum_t C[s][t] Q[t][c] on the MFMA (A = C rows,
+// B = Q^T by the transposing read).
+__global__ __launch_bounds__(512, 1) void hca_bwd_dkv_kernel(HcaBwdParams bp, BwdWs ws) {
+  __shared__ __attribute__((aligned(16))) uint16_t ck[32 * BW_CLD];
+  __shared__ __attribute__((aligned(16))) uint16_t cv[32 * BW_CLD];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int T = bp.T, W = bp.window, H = bp.H;
+  const int n_kt = (T + 31) / 32;
+  const int b = blockIdx.x / n_kt, s0 = (blockIdx.x % n_kt) * 32;
+  char* sq = pf_k0;  // 32 rows of Q of one head
+  char* so = pf_v0;  // 32 rows of dO of the same head
+  f32x4_t ak[2][4], av[2][4];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) ak[sb][cb] = av[sb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int t_end = min(T, s0 + 31 + W);  // tokens that see one of the keys: s0 .. t_end - 1
+  for (int t0 = s0; t0 < t_end; t0 += 32) {
+    for (int h = 0; h < H; ++h) {
+      __syncthreads();
+      // rows t0 .. t0 + 31 of Q and dO for head h: 2 x 2048 chunks of 16 bytes
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = tid + 512 * u;  // 0..2047
+        const int rr = c >> 6, ch = c & 63;
+        const int t = t0 + rr;
+        const size_t src = (((size_t)b * T + min(t, T - 1)) * H + h) * D + 8 * ch;
+        const uint4 zq = make_uint4(0, 0, 0, 0);
+        *(uint4*)(sq + rr * KLD + 16 * ch) = t < T ? *(const uint4*)((const uint16_t*)bp.q + src) : zq;
+        *(uint4*)(so + rr * KLD + 16 * ch) = t < T ? *(const uint4*)((const uint16_t*)bp.dout + src) : zq;
+      }
+      // coefficients of keys s0 + sr and tokens t0 + tc
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = tid + 512 * u;  // 0..1023
+        const int sr = e >> 5, tc = e & 31;
+        const int s = s0 + sr, t = t0 + tc, jj = t - s;
+        uint16_t vk = 0, vv = 0;
+        if (t < T && s < T && jj >= 0 && jj < W) {
+          const size_t at = (((size_t)b * T + t) * H + h) * W + jj;
+          vk = ws.dsw[at];
+          vv = ws.pw[at];
+        }
+        ck[sr * BW_CLD + tc] = vk;
+        cv[sr * BW_CLD + tc] = vv;
+      }
+      __syncthreads();
+      // A = coefficient rows (keys 16sb + l16, tokens 8g .. 8g + 7); B = Q^T / dO^T columns
+      // 64 wave + 16cb + l16 of tokens 8g .. 8g + 7 (two transposed reads of 4 rows each)
+      Frag8 fk[2], fv[2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        fk[sb].u = *(const uint4*)(&ck[(16 * sb + l16) * BW_CLD + 8 * g]);
+        fv[sb].u = *(const uint4*)(&cv[(16 * sb + l16) * BW_CLD + 8 * g]);
+      }
+      const int rowa = (8 * g + (l16 >> 2)) * KLD + 2 * (64 * wave + 4 * (l16 & 3));
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        Frag8 bq, bo;
+        const uint2 q0 = lds_read_tr16(sq + rowa + 32 * cb);
+        const uint2 q1 = lds_read_tr16(sq + rowa + 32 * cb + 4 * KLD);
+        const uint2 o0 = lds_read_tr16(so + rowa + 32 * cb);
+        const uint2 o1 = lds_read_tr16(so + rowa + 32 * cb + 4 * KLD);
+        bq.u = make_uint4(q0.x, q0.y, q1.x, q1.y);
+        bo.u = make_uint4(o0.x, o0.y, o1.x, o1.y);
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          ak[sb][cb] = mfma_16x16x32(fk[sb], bq, ak[sb][cb]);
+          av[sb][cb] = mfma_16x16x32(fv[sb], bo, av[sb][cb]);
+        }
+      }
+    }
+  }
+  // lane holds dK, dV[s = s0 + 16sb + 4g + r][c = 64 wave + 16cb + l16]
+  const float inv_blk = 1.0f / (float)bp.block;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int s = s0 + 16 * sb + 4 * g + r;
+      if (s >= T) continue;
+      const int e = s / bp.block;
+      const bool pooled = e < bp.ne;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int c = 64 * wave + 16 * cb + l16;
+        float gk = ak[sb][cb][r], gv = av[sb][cb][r];
+        if (pooled) {
+          gk += ws.dkc[((size_t)b * ws.ne_pad + e) * D + c] * inv_blk;
+          gv += ws.dvc[((size_t)b * ws.ne_pad + e) * D + c] * inv_blk;
+        }
+        ((uint16_t*)bp.dk)[((size_t)b * T + s) * D + c] = f32_to_bf16(gk);
+        ((uint16_t*)bp.dv)[((size_t)b * T + s) * D + c] = f32_to_bf16(gv);
+      }
+    }
+}
+
+BwdWs bwd_layout(const HcaBwdParams& p, size_t* total) {
+  BwdWs w;
+  const size_t rows = (size_t)p.B * p.T * p.H;
+  w.ne_pad = (std::max(p.ne, 1) + 7) / 8 * 8;
+  w.splits = (int)std::max<size_t>(1, std::min<size_t>(64, rows / 4096));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) / 256 * 256;
+    return at;
+  };
+  const size_t o_delta = take(rows * 4);
+  const size_t o_pc = take(rows * w.ne_pad * 2), o_dsc = take(rows * w.ne_pad * 2);
+  const size_t o_pw = take(rows * p.window * 2), o_dsw = take(rows * p.window * 2);
+  const size_t o_dkc = take((size_t)p.B * w.ne_pad * D * 4);
+  const size_t o_dvc = take((size_t)p.B * w.ne_pad * D * 4);
+  const size_t o_part = take((size_t)w.splits * w.ne_pad * D * 4);
+  *total = off;
+  char* base = (char*)p.ws;
+  w.delta = (float*)(base + o_delta);
+  w.pc = (uint16_t*)(base + o_pc);
+  w.dsc = (uint16_t*)(base + o_dsc);
+  w.pw = (uint16_t*)(base + o_pw);
+  w.dsw = (uint16_t*)(base + o_dsw);
+  w.dkc = (float*)(base + o_dkc);
+  w.dvc = (float*)(base + o_dvc);
+  w.part = (float*)(base + o_part);
+  return w;
+}
+
 }  // namespace
+
+size_t hca_bwd_workspace(const HcaBwdParams& p) {
+  size_t total = 0;
+  bwd_layout(p, &total);
+  return total;
+}
+
+hipError_t launch_hca_bwd(const HcaBwdParams& p, hipStream_t stream) {
+  size_t total = 0;
+  const BwdWs w = bwd_layout(p, &total);
+  const long long rows = (long long)p.B * p.T * p.H;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(hca_bwd_delta_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                     stream, (const uint16_t*)p.dout, (const uint16_t*)p.out, w.delta, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long grid = (long long)p.B * ((p.T + 31) / 32) * (p.H / 4);
+  hipLaunchKernelGGL(hca_bwd_dq_kernel, dim3((unsigned)grid), dim3(512), 0, stream, p, w);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // entry gradients per sequence: dKc = dSc^T Q, dVc = Pc^T dO over its T * H rows
+  const long long rows_b = (long long)p.T * p.H;
+  for (int b = 0; b < p.B && p.ne > 0; ++b) {
+    const size_t ro = (size_t)b * rows_b;
+    e = launch_gemm_splitk_f32(w.dsc + ro * w.ne_pad, w.ne_pad, true,
+                               (const uint16_t*)p.q + ro * D, D, true,
+                               w.dkc + (size_t)b * w.ne_pad * D, w.ne_pad, D, (int)rows_b,
+                               w.splits, w.part, stream);
+    if (e != hipSuccess) return e;
+    e = launch_gemm_splitk_f32(w.pc + ro * w.ne_pad, w.ne_pad, true,
+                               (const uint16_t*)p.dout + ro * D, D, true,
+                               w.dvc + (size_t)b * w.ne_pad * D, w.ne_pad, D, (int)rows_b,
+                               w.splits, w.part, stream);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(hca_bwd_dkv_kernel, dim3((unsigned)(p.B * ((p.T + 31) / 32))), dim3(512),
+                     0, stream, p, w);
+  return hipGetLastError();
+}
 
 size_t hca_bf16_workspace(const HcaParams& p) {
   if (!use_decode(p)) return 0;

@@ -56,7 +56,34 @@ struct HcaParams {
   void* out;
   void* ws;
   size_t ws_bytes;
+  float* lse;  // optional per-row log-sum-exp of the scaled logits (prefill kernel only)
 };
+
+// Backward of HCA in prefill (every sequence from position 0, T query rows = T positions):
+// the window rows are the sequence's own keys and values, the entries their block means.
+struct HcaBwdParams {
+  int B, T, H;  // d == 512, bfloat16
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* kc;
+  const void* vc;
+  const void* out;
+  const float* lse;
+  const void* dout;
+  int window, block, ne;  // ne = T / block entries
+  float scale;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* ws;
+  size_t ws_bytes;
+};
+size_t hca_bwd_workspace(const HcaBwdParams& p);
+hipError_t launch_hca_bwd(const HcaBwdParams& p, hipStream_t stream);
+hipError_t launch_gemm_splitk_f32(const void* a, long long lda, bool a_kmajor, const void* b,
+                                  long long ldb, bool b_kmajor, float* c, int M, int N, int K,
+                                  int splits, float* part, hipStream_t stream);
 
 // bfloat16, d == 512
 size_t hca_bf16_workspace(const HcaParams& p);

@@ -137,6 +137,9 @@ typedef struct {
   void* out;           /* [B, Tq, H, d] */
   void* workspace;     /* scratch, hca_attn_fwd_workspace() bytes */
   size_t workspace_bytes;
+  float* lse;          /* NULL, or [B, Tq, H] fp32: ln sum_j exp(scale <q, key_j>) of every row
+                          (-inf for a row with no visible key), for hca_attn_bwd; bf16 with
+                          Tq > 1 only */
 } lgsa_hca_args;
 /* Validation: every size >= 1 (n_cap >= 0); window <= win_len unless max_pos < win_len (then
  * no window row wraps around the ring); max_pos >= Tq - 1; kc / vc non-NULL when n_cap > 0.
@@ -147,6 +150,44 @@ typedef struct {
  * position is negative has no visible key and produces zeros. */
 lgsa_status hca_attn_fwd(const lgsa_hca_args* a, void* stream);
 lgsa_status hca_attn_fwd_workspace(const lgsa_hca_args* a, size_t* bytes);
+
+/* ---------------------------------------------------------------------------------------
+ * hca_attn_bwd -- backward of hca_attn_fwd in prefill (the chain rule of its definition;
+ * training runs whole sequences): every sequence b holds T positions from position 0, query
+ * row i sits at position i, the window rows are the sequence's own k, v (win_len = T) and the
+ * entries kc, vc are their block means (hca_compress).  With P the softmax of each row's
+ * scaled logits over its keys (rebuilt from the forward's lse), dP = dO V^T and
+ * D = rowsum(dO * O):
+ *     dS = P (dP - D),   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO,
+ * and an entry's gradient reaches each position of its block divided by block, so dk, dv
+ * hold the gradients of the raw k, v (through the window and through the pooling).  A gated
+ * layer runs latent_gate_bwd first and passes its d_o here as dout (out is then the ungated O).
+ * --------------------------------------------------------------------------------------- */
+typedef struct {
+  int dt;              /* LGSA_BF16 */
+  int B, T, H, d;      /* sequences, positions (= query rows) per sequence, heads, head dim */
+  const void* q;       /* [B, T, H, d] */
+  const void* k;       /* [B, T, d] raw keys */
+  const void* v;       /* [B, T, d] raw values */
+  const void* kc;      /* [B, T / block, d] entries (block means of k); NULL when T < block */
+  const void* vc;      /* [B, T / block, d] */
+  const void* out;     /* [B, T, H, d] the forward's output O (ungated) */
+  const float* lse;    /* [B, T, H] the forward's log-sum-exp (hca_attn_fwd with lse) */
+  const void* dout;    /* [B, T, H, d] gradient of the loss with respect to O */
+  int window, block;   /* as in the forward */
+  float scale;         /* as in the forward */
+  void* dq;            /* [B, T, H, d] */
+  void* dk;            /* [B, T, d] */
+  void* dv;            /* [B, T, d] */
+  void* workspace;     /* scratch, hca_attn_bwd_workspace() bytes (P and dS of every row and
+                          key are kept there in bf16) */
+  size_t workspace_bytes;
+} lgsa_hca_bwd_args;
+/* Supported: LGSA_BF16, d == 512, H % 4 == 0, 1 <= window <= 512, block >= 1, every tensor
+ * 16-byte aligned.  Errors: LGSA_EINVAL (NULL, misaligned, bad sizes), LGSA_EUNSUPPORTED,
+ * LGSA_EWORKSPACE; nothing is enqueued on error.  Deterministic (no atomics). */
+lgsa_status hca_attn_bwd(const lgsa_hca_bwd_args* a, void* stream);
+lgsa_status hca_attn_bwd_workspace(const lgsa_hca_bwd_args* a, size_t* bytes);
 
 /* ---------------------------------------------------------------------------------------
  * dsa_index_topk -- the DSA lightweight indexer and per-query top-k (release blog, section
