@@ -290,6 +290,46 @@ def run_gate_bwd(torch, lgsa, iters):
                 mfma_frac=round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
 
 
+def run_hca_bwd(torch, lgsa, iters):
+    """Backward of HCA prefill at the model shape (seq 32768, 64 heads, d 512, bf16, block 128,
+    window 128), after an ungated forward that also writes the log-sum-exp.  Inputs are
+    device-side seeded N(0,1) draws scaled as the forward's (q, k, v / sqrt(512)); the output
+    gradient is N(0,1).  Algorithmic work: 10 d flops per visible (row, key) pair (S, dP, dQ,
+    dK, dV)."""
+    T, H, d, W, blk = 32768, 64, 512, 128, 128
+    g = torch.Generator(device="cuda").manual_seed(11)
+    bf = torch.bfloat16
+    sc = 1.0 / math.sqrt(d)
+    q = (torch.randn(1, T, H, d, device="cuda", generator=g) * sc).to(bf)
+    k = (torch.randn(1, T, d, device="cuda", generator=g) * sc).to(bf)
+    v = (torch.randn(1, T, d, device="cuda", generator=g) * sc).to(bf)
+    kc, vc = lgsa.hca_compress(k, v, block=blk)
+    lse = torch.empty(1, T, H, dtype=torch.float32, device="cuda")
+    pos0 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = lgsa.hca_attn_fwd(q, pos0, k, v, kc, vc, max_pos=T - 1, window=W, block=blk, lse=lse)
+    dout = torch.randn(1, T, H, d, device="cuda", generator=g).to(bf)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step():
+        lgsa.hca_attn_bwd(q, k, v, kc, vc, out, lse, dout, window=W, block=blk, dq=dq, dk=dk,
+                          dv=dv)
+
+    step()
+    torch.cuda.synchronize()
+    tm = Timer(torch, torch.cuda.current_stream())
+    a = tm.event()
+    for _ in range(iters):
+        step()
+    b = tm.event()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / iters
+    pairs = sum(min(T // blk, (t + 1) // blk) + min(W, t + 1) for t in range(T))
+    flops = 10.0 * d * pairs * H
+    del q, k, v, out, dout, dq, dk, dv, lse
+    return dict(ms=round(ms, 3), TFLOPs=round(flops / (ms * 1e-3) / 1e12, 1),
+                mfma_frac=round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+
+
 def run_c4(torch, lgsa, synth, to_dev, iters):
     B, ctx, H = 8, 1 << 20, 64
     log("[bench] C4: generating inputs (batch %d, context %d)" % (B, ctx))
@@ -518,6 +558,7 @@ def main():
                                           bytes=r2["bytes"])
     secondary["vha_mix_prefill"] = run_vha(torch, lgsa, synth, to_dev, 10)
     secondary["gate_bwd_prefill"] = run_gate_bwd(torch, lgsa, 3)
+    secondary["hca_bwd_prefill"] = run_hca_bwd(torch, lgsa, 3)
     if 2 in cfgs or 4 in cfgs:
         secondary["decode_cache_append"] = run_append(torch, lgsa, synth, to_dev, 50)
     if 3 in cfgs:

@@ -326,3 +326,41 @@ def test_gate_bwd_workspace_size(lib):
     assert lib.latent_gate_bwd_workspace(100, 64, 48, lgsa.LGSA_F32, ctypes.byref(n)) == 0
     assert n.value == 100 * 48 * 4
 
+
+def _hca_bwd(**kw):
+    a = lgsa.HcaBwdArgs()
+    vals = dict(dt=lgsa.LGSA_BF16, B=1, T=256, H=4, d=512, q=FAKE, k=FAKE, v=FAKE, kc=FAKE,
+                vc=FAKE, out=FAKE, lse=FAKE, dout=FAKE, window=128, block=128, scale=0.044,
+                dq=FAKE, dk=FAKE, dv=FAKE, workspace=None, workspace_bytes=0)
+    vals.update(kw)
+    for k, v in vals.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(dt=lgsa.LGSA_F32), lgsa.LGSA_EUNSUPPORTED, "LGSA_BF16"),
+    (dict(d=256), lgsa.LGSA_EUNSUPPORTED, "d must be 512"),
+    (dict(H=6), lgsa.LGSA_EUNSUPPORTED, "multiple of 4"),
+    (dict(window=0), lgsa.LGSA_EINVAL, "window"),
+    (dict(window=600), lgsa.LGSA_EINVAL, "window"),
+    (dict(lse=None), lgsa.LGSA_EINVAL, "non-NULL"),
+    (dict(kc=None), lgsa.LGSA_EINVAL, "kc and vc"),
+    (dict(dk=FAKE_ODD), lgsa.LGSA_EINVAL, "aligned"),
+    (dict(), lgsa.LGSA_EWORKSPACE, "workspace"),
+])
+def test_hca_bwd_validation(lib, kw, code, msg):
+    a = _hca_bwd(**kw)
+    assert _call(lib, "hca_attn_bwd", a) == code
+    assert msg in lgsa.last_error()
+
+
+def test_hca_bwd_short_sequence_needs_no_entries(lib):
+    """T below one block: kc and vc may be NULL; the workspace holds no entry gradients."""
+    n_short, n_long = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    a = _hca_bwd(T=100, kc=None, vc=None)
+    assert lib.hca_attn_bwd_workspace(ctypes.byref(a), ctypes.byref(n_short)) == lgsa.LGSA_OK
+    b = _hca_bwd(T=100)
+    assert lib.hca_attn_bwd_workspace(ctypes.byref(b), ctypes.byref(n_long)) == lgsa.LGSA_OK
+    assert n_short.value == n_long.value > 0
+
