@@ -24,7 +24,8 @@ EXPORTS = ["lgsa_last_error", "hca_compress", "latent_gate", "hca_attn_fwd",
            "hca_attn_fwd_workspace", "dsa_index_topk", "dsa_index_topk_workspace",
            "sparse_attn_fwd", "sparse_attn_fwd_workspace", "hca_cache_append",
            "dsa_cache_append", "vha_mix", "latent_gate_bwd", "latent_gate_bwd_workspace",
-           "hca_attn_bwd", "hca_attn_bwd_workspace"]
+           "hca_attn_bwd", "hca_attn_bwd_workspace",
+           "sparse_attn_bwd", "sparse_attn_bwd_workspace"]
 
 
 class LibraryMissing(RuntimeError):
@@ -67,6 +68,14 @@ class SparseArgs(ctypes.Structure):
                 ("S", _I), ("k", _I), ("q", _P), ("k_lat", _P), ("k_row_stride", _LL),
                 ("v_lat", _P), ("v_row_stride", _LL), ("idx", _P), ("scale", _F),
                 ("q_lat", _P), ("w_gate", _P), ("d_lat", _I), ("out", _P),
+                ("workspace", _P), ("workspace_bytes", _SZ), ("lse", _P)]
+
+
+class SparseBwdArgs(ctypes.Structure):
+    _fields_ = [("dt", _I), ("B", _I), ("Tq", _I), ("H", _I), ("d_qk", _I), ("d_v", _I),
+                ("S", _I), ("k", _I), ("q", _P), ("k_lat", _P), ("k_row_stride", _LL),
+                ("v_lat", _P), ("v_row_stride", _LL), ("idx", _P), ("scale", _F),
+                ("out", _P), ("lse", _P), ("dout", _P), ("dq", _P), ("dk", _P), ("dv", _P),
                 ("workspace", _P), ("workspace_bytes", _SZ)]
 
 
@@ -98,7 +107,8 @@ def load():
         lib.hca_compress.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
         lib.latent_gate.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P]
         for name, st in (("hca_attn_fwd", HcaArgs), ("dsa_index_topk", IndexArgs),
-                         ("sparse_attn_fwd", SparseArgs), ("hca_attn_bwd", HcaBwdArgs)):
+                         ("sparse_attn_fwd", SparseArgs), ("hca_attn_bwd", HcaBwdArgs),
+                         ("sparse_attn_bwd", SparseBwdArgs)):
             getattr(lib, name).argtypes = [ctypes.POINTER(st), _P]
             getattr(lib, name + "_workspace").argtypes = [ctypes.POINTER(st),
                                                           ctypes.POINTER(_SZ)]
@@ -310,20 +320,77 @@ def sparse_attn_fwd_workspace(a) -> int:
 
 
 def sparse_attn_fwd(q, k_lat, idx, v_lat=None, *, scale=None, q_lat=None, w_gate=None,
-                    out=None, workspace=None, stream=None):
-    """DSA sparse core attention over the latent rows listed in idx (optionally gated)."""
+                    out=None, lse=None, workspace=None, stream=None):
+    """DSA sparse core attention over the latent rows listed in idx (optionally gated); lse
+    [B,Tq,H] fp32, when given, receives each row's log-sum-exp for sparse_attn_bwd."""
     torch = _torch()
     B, Tq, H, _ = q.shape
     dv = (k_lat if v_lat is None else v_lat).shape[-1]
     if out is None:
         out = torch.empty((B, Tq, H, dv), dtype=q.dtype, device=q.device)
     a = sparse_args(q, k_lat, idx, v_lat, scale=scale, q_lat=q_lat, w_gate=w_gate, out=out)
+    a.lse = _dev(lse, "lse")
     if workspace is None:
         workspace, _ = _workspace(sparse_attn_fwd_workspace(a), q.device)
     a.workspace = None if workspace is None else workspace.data_ptr()
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("sparse_attn_fwd", load().sparse_attn_fwd(ctypes.byref(a), _stream(stream)))
     return out
+
+
+def _sparse_bwd_args(q, k_lat, idx, out, lse, dout, v_lat, scale, dq, dk, dv):
+    B, Tq, H, d_qk = q.shape
+    vl = k_lat if v_lat is None else v_lat
+    a = SparseBwdArgs()
+    a.dt = _dt(q)
+    a.B, a.Tq, a.H, a.d_qk, a.d_v = B, Tq, H, d_qk, dout.shape[-1]
+    a.S, a.k = k_lat.shape[1], idx.shape[-1]
+    a.q = _dev(q, "q")
+    a.k_lat, a.k_row_stride = _dev(k_lat, "k_lat"), k_lat.shape[-1]
+    a.v_lat, a.v_row_stride = _dev(vl, "v_lat"), vl.shape[-1]
+    a.idx = _dev(idx, "idx")
+    a.scale = 1.0 / math.sqrt(d_qk) if scale is None else scale
+    a.out, a.lse, a.dout = _dev(out, "out"), _dev(lse, "lse"), _dev(dout, "dout")
+    a.dq, a.dk, a.dv = _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv")
+    return a
+
+
+def sparse_attn_bwd(q, k_lat, idx, out, lse, dout, v_lat=None, *, scale=None, dq=None,
+                    dk=None, dv=None, workspace=None, stream=None):
+    """Backward of sparse_attn_fwd: returns (dq [B,Tq,H,256], dk [B,S,256], dv [B,S,256] or None
+    when v_lat is None, in which case dk holds the key and value gradients of the shared latent
+    rows); see include/lgsa.h.  out and lse are the forward's (ungated) output and
+    log-sum-exp.  A workspace smaller than sparse_attn_bwd_workspace_bytes() makes the call
+    take fewer query rows at a time."""
+    torch = _torch()
+    B, Tq, H, d_qk = q.shape
+    S = k_lat.shape[1]
+    dq = torch.empty_like(q) if dq is None else dq
+    if dk is None:
+        dk = torch.empty((B, S, d_qk), dtype=q.dtype, device=q.device)
+    if v_lat is not None and dv is None:
+        dv = torch.empty((B, S, dout.shape[-1]), dtype=q.dtype, device=q.device)
+    a = _sparse_bwd_args(q, k_lat, idx, out, lse, dout, v_lat, scale, dq, dk, dv)
+    if workspace is None:
+        n = _SZ(0)
+        _check("sparse_attn_bwd_workspace", load().sparse_attn_bwd_workspace(ctypes.byref(a),
+                                                                             ctypes.byref(n)))
+        workspace, _ = _workspace(n.value, q.device)
+    a.workspace = None if workspace is None else workspace.data_ptr()
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("sparse_attn_bwd", load().sparse_attn_bwd(ctypes.byref(a), _stream(stream)))
+    return dq, dk, dv
+
+
+def sparse_attn_bwd_workspace_bytes(q, k_lat, idx, out, lse, dout, v_lat=None) -> int:
+    """Default workspace of sparse_attn_bwd for these tensors (gradients assumed separate for
+    distinct values)."""
+    a = _sparse_bwd_args(q, k_lat, idx, out, lse, dout, v_lat, None, q, q,
+                         None if v_lat is None else q)
+    n = _SZ(0)
+    _check("sparse_attn_bwd_workspace", load().sparse_attn_bwd_workspace(ctypes.byref(a),
+                                                                         ctypes.byref(n)))
+    return n.value
 
 
 def hca_attn_bwd(q, k, v, kc, vc, out, lse, dout, *, window=128, block=128, scale=None,

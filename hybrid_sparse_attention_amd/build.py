@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "liblgsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "cache.hip", "compress.hip", "gate.hip", "gemm.hip", "hca_bf16.hip",
-           "hca_f32.hip", "indexer.hip", "sparse.hip", "vha.hip"]
+           "hca_f32.hip", "indexer.hip", "sparse.hip", "sparse_bwd.hip", "vha.hip"]
 
 # -packed-fp32-ops off: hand no packed fp32 math to the device code generator.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

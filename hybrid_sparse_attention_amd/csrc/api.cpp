@@ -185,6 +185,7 @@ lgsa::SparseParams to_params(const lgsa_sparse_args* a) {
   p.out = a->out;
   p.ws = a->workspace;
   p.ws_bytes = a->workspace_bytes;
+  p.lse = a->lse;
   return p;
 }
 
@@ -224,6 +225,61 @@ lgsa_status check_workspace(const char* name, const void* ws, size_t have, size_
   REQUIRE(need == 0 || ws != nullptr, LGSA_EWORKSPACE, "%s: workspace is NULL", name);
   REQUIRE(need == 0 || aligned(ws, 16), LGSA_EWORKSPACE, "%s: workspace must be 16-byte aligned",
           name);
+  return LGSA_OK;
+}
+
+lgsa::SparseBwdParams to_params(const lgsa_sparse_bwd_args* a) {
+  lgsa::SparseBwdParams p;
+  p.B = a->B;
+  p.Tq = a->Tq;
+  p.H = a->H;
+  p.S = a->S;
+  p.k = a->k;
+  p.q = a->q;
+  p.k_lat = a->k_lat;
+  p.k_stride = a->k_row_stride;
+  p.v_lat = a->v_lat;
+  p.v_stride = a->v_row_stride;
+  p.idx = a->idx;
+  p.scale = a->scale;
+  p.out = a->out;
+  p.lse = a->lse;
+  p.dout = a->dout;
+  p.dq = a->dq;
+  p.dk = a->dk;
+  p.dv = a->dv;
+  p.ws = a->workspace;
+  p.ws_bytes = a->workspace_bytes;
+  return p;
+}
+
+lgsa_status check_sparse_bwd(const lgsa_sparse_bwd_args* a) {
+  REQUIRE(a != nullptr, LGSA_EINVAL, "sparse_attn_bwd: args is NULL");
+  REQUIRE(a->dt == LGSA_BF16, LGSA_EUNSUPPORTED, "sparse_attn_bwd: only LGSA_BF16 is supported");
+  REQUIRE(a->B >= 1 && a->Tq >= 1 && a->H >= 1 && a->d_qk >= 1 && a->d_v >= 1 && a->S >= 1 &&
+              a->k >= 1,
+          LGSA_EINVAL, "sparse_attn_bwd: B, Tq, H, d_qk, d_v, S, k must be >= 1");
+  REQUIRE(a->q && a->k_lat && a->v_lat && a->idx && a->out && a->lse && a->dout && a->dq && a->dk,
+          LGSA_EINVAL, "sparse_attn_bwd: q, k_lat, v_lat, idx, out, lse, dout, dq and dk must be "
+          "non-NULL");
+  REQUIRE(a->dv != nullptr || (a->v_lat == a->k_lat && a->v_row_stride == a->k_row_stride),
+          LGSA_EINVAL, "sparse_attn_bwd: dv may be NULL only when v_lat is k_lat");
+  REQUIRE(a->k_row_stride >= a->d_qk && a->v_row_stride >= a->d_v, LGSA_EINVAL,
+          "sparse_attn_bwd: row strides must be >= the head dims");
+  REQUIRE(std::isfinite(a->scale), LGSA_EINVAL, "sparse_attn_bwd: scale is not finite");
+  REQUIRE(a->d_qk == 256 && a->d_v == 256, LGSA_EUNSUPPORTED,
+          "sparse_attn_bwd: d_qk and d_v must be 256 (got %d, %d)", a->d_qk, a->d_v);
+  REQUIRE(a->H % 64 == 0, LGSA_EUNSUPPORTED, "sparse_attn_bwd: H must be a multiple of 64");
+  REQUIRE(a->k_row_stride % 8 == 0 && a->v_row_stride % 8 == 0, LGSA_EUNSUPPORTED,
+          "sparse_attn_bwd: row strides must be multiples of 8 elements");
+  REQUIRE(a->S <= (1 << 26), LGSA_EUNSUPPORTED, "sparse_attn_bwd: S must be <= 2^26");
+  REQUIRE((long long)a->k * (a->H / 64) <= (1 << 24), LGSA_EUNSUPPORTED,
+          "sparse_attn_bwd: k * H / 64 must be <= 2^24");
+  const void* ptrs[] = {a->q, a->k_lat, a->v_lat, a->out, a->dout, a->dq, a->dk, a->dv};
+  for (const void* p : ptrs)
+    REQUIRE(aligned(p, 16), LGSA_EINVAL, "sparse_attn_bwd: tensors must be 16-byte aligned");
+  REQUIRE(aligned(a->lse, 4) && aligned(a->idx, 4), LGSA_EINVAL,
+          "sparse_attn_bwd: lse and idx must be 4-byte aligned");
   return LGSA_OK;
 }
 
@@ -417,6 +473,24 @@ lgsa_status latent_gate_bwd(const void* q_lat, const void* w_gate, const void* o
     e = lgsa::launch_gemm(q_lat, d_lat, true, workspace, N, true, dw_gate, N, d_lat, N, M, dt,
                           st);
   return hip_status(e, "latent_gate_bwd");
+}
+
+lgsa_status sparse_attn_bwd_workspace(const lgsa_sparse_bwd_args* a, size_t* bytes) {
+  REQUIRE(bytes != nullptr, LGSA_EINVAL, "sparse_attn_bwd_workspace: bytes is NULL");
+  const lgsa_status s = check_sparse_bwd(a);
+  if (s != LGSA_OK) return s;
+  *bytes = lgsa::sparse_bwd_workspace(to_params(a));
+  return LGSA_OK;
+}
+
+lgsa_status sparse_attn_bwd(const lgsa_sparse_bwd_args* a, void* stream) {
+  const lgsa_status s = check_sparse_bwd(a);
+  if (s != LGSA_OK) return s;
+  const lgsa::SparseBwdParams p = to_params(a);
+  const lgsa_status w = check_workspace("sparse_attn_bwd", a->workspace, a->workspace_bytes,
+                                        lgsa::sparse_bwd_min_workspace(p));
+  if (w != LGSA_OK) return w;
+  return hip_status(lgsa::launch_sparse_bwd(p, (hipStream_t)stream), "sparse_attn_bwd");
 }
 
 lgsa_status hca_attn_bwd_workspace(const lgsa_hca_bwd_args* a, size_t* bytes) {

@@ -124,9 +124,33 @@ struct SparseParams {
   void* out;
   void* ws;
   size_t ws_bytes;
+  float* lse;
 };
 
 size_t sparse_workspace(const SparseParams& p);
 hipError_t launch_sparse(const SparseParams& p, hipStream_t stream);
+
+struct SparseBwdParams {
+  int B, Tq, H, S, k;
+  const void* q;
+  const void* k_lat;
+  long long k_stride;
+  const void* v_lat;
+  long long v_stride;
+  const int32_t* idx;
+  float scale;
+  const void* out;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;  // NULL: the value rows are the key rows
+  void* ws;
+  size_t ws_bytes;
+};
+
+size_t sparse_bwd_workspace(const SparseBwdParams& p);      // rows of a sequence at once, within a budget
+size_t sparse_bwd_min_workspace(const SparseBwdParams& p);  // one row at a time
+hipError_t launch_sparse_bwd(const SparseBwdParams& p, hipStream_t stream);
 
 }  // namespace lgsa

@@ -20,16 +20,16 @@
 // matrix).
 #include "common.h"
 #include "kernels.h"
+#include "sparse_tile.h"
 
 namespace lgsa {
 
 namespace {
 
-constexpr int D = 256;
-constexpr int KT = 32;                  // keys per tile
-constexpr int TROW = 2 * D;             // bytes of one gathered row (no padding: swizzled)
-constexpr int TILE = KT * TROW;         // 16 KiB
+using namespace sparse_tile;
+
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.69314718055994531f;
 constexpr float LAZY = 8.0f;            // rescale O only when the max grows by more (log2)
 constexpr float NEG_BIG = -1.0e30f;     // masked logit (finite: no inf - inf)
 // Waves per workgroup: two of 32 heads when one gathered tile serves as keys and values, four
@@ -37,43 +37,12 @@ constexpr float NEG_BIG = -1.0e30f;     // masked logit (finite: no inf - inf)
 // workgroups per CU, and four waves keep eight waves on the CU).
 template <bool ALIAS> constexpr int waves_of() { return ALIAS ? 2 : 4; }
 
-// chunk swizzle of row r: rows 0..7 -> 0, 2, .., 14; rows 8..15 -> 1, 3, .., 15 (period 16)
-__device__ __forceinline__ int sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-
 template <int NHB>
 struct WaveState {
   f32x4_t o[NHB][16];  // o[hb][cb][r] = O[head 16hb + l16][16cb + 4g + r]
   float m[NHB];        // reference max (log2 domain)
   float l[NHB];        // running partial sum of this lane's keys
 };
-
-// Gather one tile: DMA instruction i (of 16) loads tile rows 2i (lanes 0..31) and 2i + 1
-// (lanes 32..63); wave w issues i = w, w + NW, ...  `ix` holds, in lane j < 32, the position
-// of tile row j (-1 when skipped: the row is then read from position 0 and masked).
-template <int NW>
-__device__ __forceinline__ void gather_tile(const uint16_t* rows, long long stride, int ix,
-                                            char* tile, int w, int lane) {
-  const int hi = lane >> 5;
-  for (int i = w; i < KT / 2; i += NW) {
-    const int sa = __builtin_amdgcn_readlane(ix, 2 * i);
-    const int sb = __builtin_amdgcn_readlane(ix, 2 * i + 1);
-    const int s = max(hi ? sb : sa, 0);
-    const int r = 2 * i + hi;
-    const int chunk = (lane & 31) ^ sw(r);
-    lds_dma16(rows + (size_t)s * stride + 8 * chunk, tile + 2 * i * TROW);
-  }
-}
-
-// raw list entries of tile rows j0 .. j0 + 31 (lane j < 32; -1 past j_end).  The range check
-// is left to valid_ix, applied only once the load has been drained with the tile's transfers:
-// using the loaded value earlier would make the wave wait for the gathers issued before it.
-__device__ __forceinline__ int load_ix(const int32_t* idx, int j0, int j_end, int lane) {
-  const int j = j0 + lane;
-  return (lane < KT && j < j_end) ? idx[j] : -1;
-}
-
-// the entry as a position, or -1 when it is skipped (negative or beyond the rows held)
-__device__ __forceinline__ int valid_ix(int s, int S) { return (s >= 0 && s < S) ? s : -1; }
 
 template <int NHB>
 __device__ __forceinline__ void scores(f32x4_t (&s)[NHB][2], const Frag8 (&qf)[NHB][8],
@@ -257,6 +226,8 @@ void sparse_kernel(SparseParams p, int n_split, int chunk, float* part_o, float*
       uint16_t* orow = (uint16_t*)p.out + ((size_t)r * p.H + h) * D;
 #pragma unroll
       for (int cb = 0; cb < 16; ++cb) store4(orow + 16 * cb + 4 * g, st.o[hb][cb] * inv);
+      if (p.lse != nullptr && g == 0)
+        p.lse[(size_t)r * p.H + h] = inv > 0.f ? (st.m[hb] + __log2f(lt)) * LN2 : -INFINITY;
       continue;
     }
     const size_t pr = ((size_t)r * n_split + sp) * p.H + h;
@@ -274,7 +245,8 @@ void sparse_kernel(SparseParams p, int n_split, int chunk, float* part_o, float*
 
 __global__ __launch_bounds__(64) void sparse_combine_kernel(const float* __restrict__ part_o,
                                                             const float* __restrict__ part_ml,
-                                                            uint16_t* __restrict__ out, int H,
+                                                            uint16_t* __restrict__ out,
+                                                            float* __restrict__ lse, int H,
                                                             int n_split) {
   const int rh = blockIdx.x;  // r * H + h
   const int r = rh / H, h = rh % H;
@@ -294,6 +266,7 @@ __global__ __launch_bounds__(64) void sparse_combine_kernel(const float* __restr
     acc[3] += a * v.w;
   }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (lse != nullptr && threadIdx.x == 0) lse[rh] = lt > 0.f ? (mt + __log2f(lt)) * LN2 : -INFINITY;
   uint2 o;
   o.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
   o.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
@@ -343,7 +316,7 @@ hipError_t launch_sparse(const SparseParams& p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   if (n_split > 1) {
     hipLaunchKernelGGL(sparse_combine_kernel, dim3((unsigned)(rows * p.H)), dim3(64), 0, stream,
-                       part_o, part_ml, (uint16_t*)p.out, p.H, n_split);
+                       part_o, part_ml, (uint16_t*)p.out, p.lse, p.H, n_split);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

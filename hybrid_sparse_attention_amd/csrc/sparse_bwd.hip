@@ -1,0 +1,570 @@
+// Backward of the DSA sparse core attention (ERNIE 5.5 Flash Base release blog, section 2.1:
+// core attention over the top-k positions the indexer picks, 256-wide MLA heads), by the chain
+// rule of the forward: with P rebuilt from the forward's log-sum-exp, dP = dO V^T and
+// D = rowsum(dO * O),
+//     dS = P (dP - D),  dq = scale dS K,  (row s of dk) += scale dS^T q,  (row s of dv) += P^T dO
+// over every (query row, entry) that lists s.
+//
+// Each query row lists its own keys, so the key-side gradients of one row are 32 rows of 256
+// columns per tile, scattered over the latent rows.  They are made deterministic without
+// atomics on floating point: a counting pass gives every (row, entry) a slot in an order sorted
+// by key and then by query row, the main kernel writes each contribution (bfloat16) to its
+// slot, and a reduction sums each key's slots in that order in fp32.  Rows are processed in
+// chunks that bound the slot buffer; a chunk's sums are carried in an fp32 accumulator.
+//
+//   rank    one workgroup per range of query rows: for each row in turn, each valid entry takes
+//           the next count of (key, range) with an integer atomic.  A row lists a key once
+//           (twice only as a duplicate, whose contributions are equal), and the rows of a range
+//           are ranked one after another, so the counts it returns follow the row order.
+//   scan    exclusive prefix sum over the (key, range) counts, key-major: each key's slots are
+//           contiguous and ordered by range.
+//   slot    slot = offset(key, range) + rank.
+//   main    one workgroup (8 waves) per query row and group of 64 heads.  Wave w takes heads
+//           16(w % 4) .. +15 and keys 16(w / 4) .. +15 of each 32-key tile for S^T = K Q^T and
+//           dP^T = V dO^T (K rows read row-wise, Q and dO in registers); P and scale*dS go to
+//           LDS as [key][head] bfloat16; then dq^T = K^T dS^T over the tile's 32 keys for dims
+//           128(w / 4) .. +127 (K through the transposing read) and the key-side contributions
+//           C^T = Q^T dS^T + dO^T P^T for dims 32w .. +31 (Q^T, dO^T in registers, staged
+//           through LDS once per row).  Gathers are double buffered as in the forward; the
+//           contributions are stored without waiting for them.
+//   reduce  one wave per key: its slots in order, plus the accumulator of earlier chunks.
+#include <algorithm>
+#include <cstdint>
+
+#include "common.h"
+#include "kernels.h"
+#include "sparse_tile.h"
+
+namespace lgsa {
+
+namespace {
+
+using namespace sparse_tile;
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr int NW = 8;                          // waves of the main kernel
+constexpr int PROW = 144;                      // bytes per key row of the P, dS tiles (64 heads + pad)
+constexpr int QROW = 544;                      // bytes per head row of the staged Q, dO (256 + pad)
+constexpr size_t BUF_BUDGET = 8ull << 30;      // bytes of contributions held per chunk of rows
+constexpr long long SCAN_BLOCK = 4096;         // counters per block of the scan
+constexpr long long MAX_COUNTERS = SCAN_BLOCK * 16384;  // what the two-level scan covers
+constexpr int MAX_RANGES = 256;
+
+__device__ __forceinline__ void store4(uint16_t* dst, const f32x4_t& v) {
+  uint2 r;
+  r.x = pack_bf16x2(v[0], v[1]);
+  r.y = pack_bf16x2(v[2], v[3]);
+  *(uint2*)dst = r;
+}
+
+__device__ __forceinline__ float dot8(const uint4& a, const uint4& b) {
+  const uint32_t x[4] = {a.x, a.y, a.z, a.w}, y[4] = {b.x, b.y, b.z, b.w};
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s += __uint_as_float(x[i] << 16) * __uint_as_float(y[i] << 16);
+    s += __uint_as_float(x[i] & 0xFFFF0000u) * __uint_as_float(y[i] & 0xFFFF0000u);
+  }
+  return s;
+}
+
+// slot row of tile key `lane` (lane < 32): a real slot, or this workgroup's scratch row for a
+// skipped entry (stores stay unconditional, so every tile issues the same number of them)
+__device__ __forceinline__ int load_slot(const int32_t* sl, int j0, int k, int lane) {
+  const int j = j0 + lane;
+  return (lane < KT && j < k) ? sl[j] : -1;
+}
+
+// grid: chunk row q (of n_rows) x head group; rows 0 .. n_wg - 1 of buf are the scratch rows
+template <bool ALIAS>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void sparse_bwd_kernel(SparseBwdParams p, long long row0, const int32_t* __restrict__ slot,
+                       uint16_t* __restrict__ buf) {
+  constexpr int RW = ALIAS ? D : 2 * D;  // columns of one contribution row
+  __shared__ __attribute__((aligned(1024))) char kt0[TILE];
+  __shared__ __attribute__((aligned(1024))) char kt1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vt0[ALIAS ? 16 : TILE];
+  __shared__ __attribute__((aligned(1024))) char vt1[ALIAS ? 16 : TILE];
+  __shared__ __attribute__((aligned(16))) char dst_[KT * PROW];  // scale*dS [key][head]
+  __shared__ __attribute__((aligned(16))) char pt[KT * PROW];    // P        [key][head]
+  __shared__ __attribute__((aligned(16))) char qs[64 * QROW];    // Q   [head][dim]
+  __shared__ __attribute__((aligned(16))) char ds[64 * QROW];    // dO  [head][dim]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int hb = wave & 3, kh = wave >> 2;
+  const int hl = 16 * hb + l16;  // this lane's head (S^T and dq^T column)
+  const int n_hg = p.H / 64;
+  const int hg = blockIdx.x % n_hg;
+  const int q = blockIdx.x / n_hg;
+  const long long row = row0 + q;  // b * Tq + i
+  const int b = (int)(row / p.Tq);
+  const long long n_wg = (long long)gridDim.x;
+  const size_t hrow = (size_t)row * p.H + 64 * hg;  // first head of the group
+  const uint16_t* Q = (const uint16_t*)p.q + hrow * D;
+  const uint16_t* dO = (const uint16_t*)p.dout + hrow * D;
+  const uint16_t* O = (const uint16_t*)p.out + hrow * D;
+  const int32_t* idx = p.idx + (size_t)row * p.k;
+  const int32_t* sl = slot + (size_t)q * p.k;
+  const uint16_t* kl = (const uint16_t*)p.k_lat + (size_t)b * p.S * p.k_stride;
+  const uint16_t* vl = (const uint16_t*)p.v_lat + (size_t)b * p.S * p.v_stride;
+  const int n_tiles = (p.k + KT - 1) / KT;
+
+  // tile 0 in flight first
+  const int ix0 = valid_ix(load_ix(idx, 0, p.k, lane), p.S);
+  uint32_t valid_cur = (uint32_t)__ballot(ix0 >= 0);
+  gather_tile<NW>(kl, p.k_stride, ix0, kt0, wave, lane);
+  if (!ALIAS) gather_tile<NW>(vl, p.v_stride, ix0, vt0, wave, lane);
+  int slot_cur = load_slot(sl, 0, p.k, lane);
+  int ix_nxt = load_ix(idx, KT, p.k, lane);
+  int slot_nxt = load_slot(sl, KT, p.k, lane);
+
+  // Q and dO of the 64 heads to LDS (for the transposed operands), and in registers for S^T
+  for (int i = tid; i < 64 * 32; i += 64 * NW) {
+    const int h = i >> 5, c = i & 31;
+    *(uint4*)(qs + h * QROW + 16 * c) = *(const uint4*)(Q + h * D + 8 * c);
+    *(uint4*)(ds + h * QROW + 16 * c) = *(const uint4*)(dO + h * D + 8 * c);
+  }
+  Frag8 qf[8], df[8];
+  float dsum = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    qf[kk].u = *(const uint4*)(Q + hl * D + 32 * kk + 8 * g);
+    df[kk].u = *(const uint4*)(dO + hl * D + 32 * kk + 8 * g);
+    dsum += dot8(df[kk].u, *(const uint4*)(O + hl * D + 32 * kk + 8 * g));
+  }
+  const float Dh = wave_sum16(dsum);
+  const float lse2 = p.lse[hrow + hl] * LOG2E;
+  const bool live = lse2 > -INFINITY;
+  const float scale_log2 = p.scale * LOG2E;
+  wait_all();
+  __syncthreads();
+
+  // A operand of C^T: rows = dims 32w + 16mb + l16, contraction = heads 32(ks & 1) + 8g .. +7
+  // of Q (ks < 2) or dO (ks >= 2), read through the transposing LDS read
+  Frag8 cq[4][2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const char* base = (ks < 2 ? qs : ds) + (32 * (ks & 1) + 8 * g + (l16 >> 2)) * QROW;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int col = 32 * wave + 16 * mb + 4 * (l16 & 3);
+      const uint2 lo = lds_read_tr16(base + 2 * col);
+      const uint2 hi = lds_read_tr16(base + 4 * QROW + 2 * col);
+      cq[ks][mb].u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  }
+
+  // lane-constant LDS offsets: key rows 16kh + l16 read row-wise (as the forward's scores) and
+  // the transposing reads of K^T (rows 4g + l16/4 and +16, as the forward's V^T)
+  const int ksw = sw(l16);
+  int kb[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) kb[c] = l16 * TROW + 16 * ((4 * c + g) ^ ksw) + 16 * TROW * kh;
+  const int vr = 4 * g + (l16 >> 2);
+  const int vrow = vr * TROW + 8 * (l16 & 1);
+  const int vsw = sw(vr);
+  const int vh = (l16 & 3) >> 1;
+  // dS^T operand of dq^T: column = head hl, contraction slots 8g .. 8g+7 = keys 4g .. 4g+3 and
+  // 16 + 4g .. 16 + 4g + 3 (the order the K^T read gives)
+  const int dsb = (4 * g + (l16 >> 2)) * PROW + 2 * (16 * hb + 4 * (l16 & 3));
+
+  f32x4_t dq[8];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) dq[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto body = [&](int ti, const char* kc, const char* vc, char* kn, char* vn) {
+    uint32_t valid_nxt = 0;
+    if (ti + 1 < n_tiles) {
+      const int ixv = valid_ix(ix_nxt, p.S);
+      valid_nxt = (uint32_t)__ballot(ixv >= 0);
+      gather_tile<NW>(kl, p.k_stride, ixv, kn, wave, lane);
+      if (!ALIAS) gather_tile<NW>(vl, p.v_stride, ixv, vn, wave, lane);
+    }
+    const int ix_after = load_ix(idx, KT * (ti + 2), p.k, lane);
+    const int slot_after = load_slot(sl, KT * (ti + 2), p.k, lane);
+
+    // S^T and dP^T: keys 16kh + 4g + r, head hl
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      Frag8 ka;
+      ka.u = *(const uint4*)(kc + kb[kk & 3] + 256 * (kk >> 2));
+      s = mfma_16x16x32(ka, qf[kk], s);
+      if (ALIAS) {
+        dp = mfma_16x16x32(ka, df[kk], dp);
+      } else {
+        Frag8 va;
+        va.u = *(const uint4*)(vc + kb[kk & 3] + 256 * (kk >> 2));
+        dp = mfma_16x16x32(va, df[kk], dp);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = 16 * kh + 4 * g + r;
+      const bool v = live && ((valid_cur >> key) & 1u);
+      const float pr = v ? fast_exp2(s[r] * scale_log2 - lse2) : 0.f;
+      const float dsv = pr * (dp[r] - Dh) * p.scale;
+      const bf16x2_t pp = {(__bf16)pr, (__bf16)dsv};
+      const uint32_t u = __builtin_bit_cast(uint32_t, pp);
+      *(uint16_t*)(pt + key * PROW + 2 * hl) = (uint16_t)(u & 0xFFFFu);
+      *(uint16_t*)(dst_ + key * PROW + 2 * hl) = (uint16_t)(u >> 16);
+    }
+    lds_barrier();  // P and dS of the tile are in LDS (the next tile's gathers stay in flight)
+
+    // dq^T (dims 128kh + 16mb + l16, head hl) += K^T dS^T
+    Frag8 bds;
+    {
+      const uint2 lo = lds_read_tr16(dst_ + dsb);
+      const uint2 hi = lds_read_tr16(dst_ + dsb + 16 * PROW);
+      bds.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+    const int vh_t = opaque(vh);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const int pos = (2 * (8 * kh + mb) + vh_t) ^ vsw;
+      const char* a = kc + vrow + 16 * pos;
+      const uint2 lo = lds_read_tr16(a);
+      const uint2 hi = lds_read_tr16(a + 16 * TROW);
+      Frag8 ka;
+      ka.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      dq[mb] = mfma_16x16x32(ka, bds, dq[mb]);
+    }
+
+    // C^T (dims 32w + 16mb + 4g + r, key 16nb + l16) = Q^T dS^T (+ dO^T P^T)
+    f32x4_t ck[2][2], cv[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) ck[mb][nb] = cv[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // the dS products first: the compiler waits for the gathers in flight before the first read
+    // of P (it cannot tell that they do not write it), so that wait comes as late as it can
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        Frag8 bd;
+        bd.u = *(const uint4*)(dst_ + (16 * nb + l16) * PROW + 16 * g + 64 * ks);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) ck[mb][nb] = mfma_16x16x32(cq[ks][mb], bd, ck[mb][nb]);
+      }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        Frag8 bp;
+        bp.u = *(const uint4*)(pt + (16 * nb + l16) * PROW + 16 * g + 64 * ks);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          if (ALIAS)
+            ck[mb][nb] = mfma_16x16x32(cq[2 + ks][mb], bp, ck[mb][nb]);
+          else
+            cv[mb][nb] = mfma_16x16x32(cq[2 + ks][mb], bp, cv[mb][nb]);
+        }
+      }
+    const int rix = slot_cur >= 0 ? (int)(n_wg + (long long)slot_cur * n_hg + hg) : (int)blockIdx.x;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int rk = __shfl(rix, 16 * nb + l16);
+      uint16_t* dst = buf + (size_t)rk * RW + 32 * wave + 4 * g;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        store4(dst + 16 * mb, ck[mb][nb]);
+        if (!ALIAS) store4(dst + D + 16 * mb, cv[mb][nb]);
+      }
+    }
+    // this wave's gathers of tile ti + 1 and the entries of tile ti + 2 have landed (they
+    // were issued before the stores, and vector memory operations complete in order); the
+    // stores themselves stay in flight
+    wait_vm<ALIAS ? 4 : 8>();
+    lds_barrier();
+    valid_cur = valid_nxt;
+    ix_nxt = ix_after;
+    slot_cur = slot_nxt;
+    slot_nxt = slot_after;
+  };
+  for (int ti = 0; ti < n_tiles; ti += 2) {
+    body(ti, kt0, vt0, kt1, vt1);
+    if (ti + 1 < n_tiles) body(ti + 1, kt1, vt1, kt0, vt0);
+  }
+
+  uint16_t* dqr = (uint16_t*)p.dq + (hrow + hl) * D + 128 * kh + 4 * g;
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) store4(dqr + 16 * mb, dq[mb]);
+}
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (long long)gridDim.x * 256)
+    p[i] = 0;
+}
+
+// range r = blockIdx.x of rows [r*qr, min(n_rows, (r+1)*qr)): rows one after another
+__global__ __launch_bounds__(256) void sparse_bwd_rank_kernel(const int32_t* __restrict__ idx,
+                                                              int k, int S, int n_rows, int qr,
+                                                              int R, int32_t* __restrict__ cnt,
+                                                              int32_t* __restrict__ rank) {
+  const int r = blockIdx.x;
+  const int q1 = min(n_rows, (r + 1) * qr);
+  for (int q = r * qr; q < q1; ++q) {
+    const int32_t* ir = idx + (size_t)q * k;
+    int32_t* rr = rank + (size_t)q * k;
+    for (int j = threadIdx.x; j < k; j += 256) {
+      const int s = ir[j];
+      int rk = -1;
+      if (s >= 0 && s < S) rk = atomicAdd(&cnt[(size_t)s * R + r], 1);
+      rr[j] = rk;  // uses the returned count: the atomic has been performed before the barrier
+    }
+    __syncthreads();
+  }
+}
+
+// exclusive scan of one block of 4096 counters in place; the block's total to bsum
+template <int NT>
+__device__ __forceinline__ void block_scan16(int32_t* __restrict__ data, long long n,
+                                             long long base, int32_t* total) {
+  __shared__ int32_t wsum[NT / 64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const long long i0 = base + 16ll * threadIdx.x;
+  int v[16];
+  int sum = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int x = i0 + e < n ? data[i0 + e] : 0;
+    v[e] = sum;
+    sum += x;
+  }
+  int x = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int pre = 0;
+  for (int i = 0; i < w; ++i) pre += wsum[i];
+  const int ex = pre + x - sum;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if (i0 + e < n) data[i0 + e] = v[e] + ex;
+  if (threadIdx.x == NT - 1) *total = pre + x;
+}
+
+__global__ __launch_bounds__(256) void scan_local_kernel(int32_t* __restrict__ data, long long n,
+                                                         int32_t* __restrict__ bsum) {
+  block_scan16<256>(data, n, (long long)blockIdx.x * SCAN_BLOCK, bsum + blockIdx.x);
+}
+
+// one workgroup: the block totals (at most 16384) scanned in place, the grand total after them
+__global__ __launch_bounds__(1024) void scan_top_kernel(int32_t* __restrict__ bsum, int nblk) {
+  block_scan16<1024>(bsum, nblk, 0, bsum + nblk);
+}
+
+__global__ __launch_bounds__(256) void scan_add_kernel(int32_t* __restrict__ data, long long n,
+                                                       const int32_t* __restrict__ bsum) {
+  const long long i0 = (long long)blockIdx.x * SCAN_BLOCK + 16ll * threadIdx.x;
+  const int add = bsum[blockIdx.x];
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if (i0 + e < n) data[i0 + e] += add;
+}
+
+__global__ __launch_bounds__(256) void sparse_bwd_slot_kernel(const int32_t* __restrict__ idx,
+                                                              long long n, int k, int S, int qr,
+                                                              int R, const int32_t* __restrict__ off,
+                                                              int32_t* __restrict__ rank) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (long long)gridDim.x * 256) {
+    const int rk = rank[i];
+    if (rk < 0) continue;
+    const int r = (int)(i / k) / qr;
+    rank[i] = off[(size_t)idx[i] * R + r] + rk;
+  }
+}
+
+// One wave per key: its slots [off(s, 0), off(s + 1, 0)) in order, then the accumulator.
+// mode 0: acc = sum; 1: acc += sum; 2: out = acc + sum; 3: out = sum.
+template <bool ALIAS>
+__global__ __launch_bounds__(256) void sparse_bwd_reduce_kernel(
+    const uint16_t* __restrict__ buf, long long row_base, const int32_t* __restrict__ off,
+    const int32_t* __restrict__ total, int R, int S, int n_hg, float* __restrict__ acc, int mode,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+  constexpr int RW = ALIAS ? D : 2 * D;
+  constexpr int PER = RW / 64;  // columns per lane
+  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (s >= S) return;
+  const int lane = threadIdx.x & 63;
+  const long long a = row_base + (long long)off[(size_t)s * R] * n_hg;
+  const long long e = row_base + (long long)(s + 1 < S ? off[(size_t)(s + 1) * R] : *total) * n_hg;
+  float sum[PER];
+#pragma unroll
+  for (int c = 0; c < PER; ++c) sum[c] = 0.f;
+  const uint16_t* src = buf + PER * lane;
+  auto add = [&](const uint4& u) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int c = 0; c < PER / 2; ++c) {
+      sum[2 * c] += __uint_as_float(w[c] << 16);
+      sum[2 * c + 1] += __uint_as_float(w[c] & 0xFFFF0000u);
+    }
+  };
+  auto load = [&](long long i) {
+    if constexpr (ALIAS) {
+      const uint2 x = *(const uint2*)(src + (size_t)i * RW);
+      return make_uint4(x.x, x.y, 0u, 0u);
+    }
+    return *(const uint4*)(src + (size_t)i * RW);
+  };
+  long long i = a;
+  for (; i + 8 <= e; i += 8) {
+    uint4 u[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) u[t] = load(i + t);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) add(u[t]);
+  }
+  for (; i < e; ++i) add(load(i));
+  float* ac = acc + (size_t)s * RW + PER * lane;
+  if (mode == 1 || mode == 2) {
+#pragma unroll
+    for (int c = 0; c < PER; ++c) sum[c] = ac[c] + sum[c];
+  }
+  if (mode <= 1) {
+#pragma unroll
+    for (int c = 0; c < PER; ++c) ac[c] = sum[c];
+    return;
+  }
+  uint32_t o[PER / 2];
+#pragma unroll
+  for (int c = 0; c < PER / 2; ++c) o[c] = pack_bf16x2(sum[2 * c], sum[2 * c + 1]);
+  if constexpr (ALIAS) {
+    *(uint2*)(dk + (size_t)s * D + PER * lane) = make_uint2(o[0], o[1]);
+  } else {
+    uint16_t* dst =
+        lane < 32 ? dk + (size_t)s * D + PER * lane : dv + (size_t)s * D + PER * (lane - 32);
+    *(uint4*)dst = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct SbwdPlan {
+  bool alias;
+  int rw, n_hg, qc, qr, rmax;
+  int chunks;  // per sequence
+  size_t o_cnt, o_bsum, o_rank, o_buf, o_acc, bytes;
+};
+
+// layout for chunks of qc query rows
+size_t sbwd_layout(const SparseBwdParams& p, long long qc, SbwdPlan& pl) {
+  pl.alias = p.dv == nullptr;
+  pl.rw = pl.alias ? D : 2 * D;
+  pl.n_hg = p.H / 64;
+  long long rmax = std::max(1ll, std::min((long long)MAX_RANGES, MAX_COUNTERS / p.S));
+  rmax = std::min(rmax, qc);
+  pl.qr = (int)((qc + rmax - 1) / rmax);
+  pl.rmax = (int)((qc + pl.qr - 1) / pl.qr);
+  pl.qc = (int)qc;
+  pl.chunks = (int)((p.Tq + qc - 1) / qc);
+  const long long counters = (long long)p.S * pl.rmax;
+  const long long nblk = (counters + SCAN_BLOCK - 1) / SCAN_BLOCK;
+  size_t o = 0;
+  pl.o_cnt = o;
+  o = align256(o + (size_t)counters * 4);
+  pl.o_bsum = o;
+  o = align256(o + (size_t)(nblk + 1) * 4);
+  pl.o_rank = o;
+  o = align256(o + (size_t)qc * p.k * 4);
+  pl.o_buf = o;
+  o = align256(o + ((size_t)qc * pl.n_hg + (size_t)qc * p.k * pl.n_hg) * pl.rw * 2);
+  pl.o_acc = o;
+  if (pl.chunks > 1) o = align256(o + (size_t)p.S * pl.rw * 4);
+  pl.bytes = o;
+  return o;
+}
+
+// The largest chunk that fits `avail` bytes, at most the one whose contributions fill the
+// default budget (and at most one sequence).
+SbwdPlan sbwd_plan(const SparseBwdParams& p, size_t avail) {
+  SbwdPlan pl;
+  const size_t row_bytes = (size_t)p.k * (p.H / 64) * (p.dv == nullptr ? D : 2 * D) * 2;
+  long long qc = (long long)(BUF_BUDGET / std::max<size_t>(row_bytes, 1));
+  qc = std::max(1ll, std::min(qc, (long long)p.Tq));
+  if (sbwd_layout(p, qc, pl) <= avail) return pl;
+  long long lo = 1, hi = qc - 1;  // below qc every size includes the accumulator: monotone
+  while (lo < hi) {
+    const long long mid = (lo + hi + 1) / 2;
+    if (sbwd_layout(p, mid, pl) <= avail)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  sbwd_layout(p, lo, pl);
+  return pl;
+}
+
+}  // namespace
+
+size_t sparse_bwd_workspace(const SparseBwdParams& p) { return sbwd_plan(p, SIZE_MAX).bytes; }
+
+size_t sparse_bwd_min_workspace(const SparseBwdParams& p) {
+  SbwdPlan pl;
+  return sbwd_layout(p, 1, pl);
+}
+
+hipError_t launch_sparse_bwd(const SparseBwdParams& p, hipStream_t stream) {
+  const SbwdPlan pl = sbwd_plan(p, p.ws_bytes);
+  char* ws = (char*)p.ws;
+  int32_t* cnt = (int32_t*)(ws + pl.o_cnt);
+  int32_t* bsum = (int32_t*)(ws + pl.o_bsum);
+  int32_t* rank = (int32_t*)(ws + pl.o_rank);
+  uint16_t* buf = (uint16_t*)(ws + pl.o_buf);
+  float* acc = (float*)(ws + pl.o_acc);
+  for (int b = 0; b < p.B; ++b) {
+    uint16_t* dk = (uint16_t*)p.dk + (size_t)b * p.S * D;
+    uint16_t* dv = pl.alias ? nullptr : (uint16_t*)p.dv + (size_t)b * p.S * D;
+    for (int c = 0; c < pl.chunks; ++c) {
+      const int t0 = c * pl.qc, n_rows = std::min(pl.qc, p.Tq - t0);
+      const long long row0 = (long long)b * p.Tq + t0;
+      const int R = (n_rows + pl.qr - 1) / pl.qr;
+      const long long counters = (long long)p.S * R;
+      const long long nblk = (counters + SCAN_BLOCK - 1) / SCAN_BLOCK;
+      const int32_t* idx = p.idx + (size_t)row0 * p.k;
+      const long long n_pairs = (long long)n_rows * p.k;
+      hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)std::min(4096ll, (counters + 255) / 256)),
+                         dim3(256), 0, stream, cnt, counters);
+      hipLaunchKernelGGL(sparse_bwd_rank_kernel, dim3(R), dim3(256), 0, stream, idx, p.k, p.S,
+                         n_rows, pl.qr, R, cnt, rank);
+      hipLaunchKernelGGL(scan_local_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, cnt,
+                         counters, bsum);
+      hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(1024), 0, stream, bsum, (int)nblk);
+      hipLaunchKernelGGL(scan_add_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, cnt,
+                         counters, bsum);
+      hipLaunchKernelGGL(sparse_bwd_slot_kernel,
+                         dim3((unsigned)std::min(8192ll, (n_pairs + 255) / 256)), dim3(256), 0,
+                         stream, idx, n_pairs, p.k, p.S, pl.qr, R, cnt, rank);
+      const unsigned grid = (unsigned)n_rows * pl.n_hg;
+      if (pl.alias)
+        hipLaunchKernelGGL(sparse_bwd_kernel<true>, dim3(grid), dim3(64 * NW), 0, stream, p,
+                           row0, rank, buf);
+      else
+        hipLaunchKernelGGL(sparse_bwd_kernel<false>, dim3(grid), dim3(64 * NW), 0, stream, p,
+                           row0, rank, buf);
+      const int mode = pl.chunks == 1 ? 3 : c == 0 ? 0 : c + 1 < pl.chunks ? 1 : 2;
+      const dim3 rgrid((unsigned)((p.S + 3) / 4));
+      if (pl.alias)
+        hipLaunchKernelGGL(sparse_bwd_reduce_kernel<true>, rgrid, dim3(256), 0, stream, buf,
+                           (long long)grid, cnt, bsum + nblk, R, p.S, pl.n_hg, acc, mode, dk, dv);
+      else
+        hipLaunchKernelGGL(sparse_bwd_reduce_kernel<false>, rgrid, dim3(256), 0, stream, buf,
+                           (long long)grid, cnt, bsum + nblk, R, p.S, pl.n_hg, acc, mode, dk, dv);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace lgsa

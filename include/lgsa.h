@@ -250,12 +250,56 @@ typedef struct {
   void* out;             /* [B, Tq, H, d_v] */
   void* workspace;       /* scratch, sparse_attn_fwd_workspace() bytes */
   size_t workspace_bytes;
+  float* lse;            /* [B, Tq, H] or NULL: natural log of each row's softmax denominator
+                            over its scaled logits (-inf for a row with no valid entry), for
+                            sparse_attn_bwd */
 } lgsa_sparse_args;
 /* Supported: LGSA_BF16, d_qk == d_v == 256, H % 64 == 0, row strides % 8 == 0,
  * d_lat % 64 == 0; every tensor 16-byte aligned.  The gate, when requested, runs as a second
  * kernel on the same stream that rescales out in place. */
 lgsa_status sparse_attn_fwd(const lgsa_sparse_args* a, void* stream);
 lgsa_status sparse_attn_fwd_workspace(const lgsa_sparse_args* a, size_t* bytes);
+
+/* ---------------------------------------------------------------------------------------
+ * sparse_attn_bwd -- backward of sparse_attn_fwd (the chain rule of its definition; the
+ * pages' training is the reason to have it).  For query row (b, i), head h, the listed keys
+ * K_j, values V_j, P the softmax of the row's scaled logits (rebuilt from the forward's lse),
+ * dP_j = <dO, V_j> and D = <dO, O>:
+ *     dS_j = P_j (dP_j - D),   dq = scale sum_j dS_j K_j,
+ *     row s_j of dk gains scale sum_h dS_j q_h,   row s_j of dv gains sum_h P_j dO_h,
+ * summed over every (row, entry) that lists s_j (an entry listed twice counts twice; skipped
+ * entries contribute nothing; rows no entry lists get zeros).  When v_lat is k_lat the two
+ * gradients land on the same latent row: dk then holds their sum on its first d_qk columns and
+ * dv must be NULL.  A gated layer runs latent_gate_bwd first and passes its d_o as dout.
+ * Deterministic: the contributions of every (row, entry) are written to slots ordered by key
+ * and then by row, and each key's slots are summed in that order (fp32).
+ * --------------------------------------------------------------------------------------- */
+typedef struct {
+  int dt;                /* LGSA_BF16 */
+  int B, Tq, H, d_qk, d_v, S, k;
+  const void* q;         /* [B, Tq, H, d_qk] */
+  const void* k_lat;     /* [B, S, k_row_stride] */
+  long long k_row_stride;
+  const void* v_lat;     /* [B, S, v_row_stride] (may equal k_lat) */
+  long long v_row_stride;
+  const int32_t* idx;    /* [B, Tq, k] as in the forward */
+  float scale;           /* as in the forward */
+  const void* out;       /* [B, Tq, H, d_v] the forward's output O (ungated) */
+  const float* lse;      /* [B, Tq, H] the forward's log-sum-exp */
+  const void* dout;      /* [B, Tq, H, d_v] gradient of the loss with respect to O */
+  void* dq;              /* [B, Tq, H, d_qk] */
+  void* dk;              /* [B, S, d_qk] gradient of the key columns of every latent row */
+  void* dv;              /* [B, S, d_v] gradient of the value columns; NULL when v_lat == k_lat */
+  void* workspace;       /* scratch: sparse_attn_bwd_workspace() bytes hold the slot order
+                            and the contributions of up to a sequence's rows at a time (within
+                            about 8 GiB); less, down to the size for one row, makes the call
+                            take fewer rows at a time (same result up to summation order) */
+  size_t workspace_bytes;
+} lgsa_sparse_bwd_args;
+/* Supported: LGSA_BF16, d_qk == d_v == 256, H % 64 == 0, row strides % 8 == 0, every tensor
+ * 16-byte aligned.  Errors as for sparse_attn_fwd; LGSA_EWORKSPACE when the workspace is short. */
+lgsa_status sparse_attn_bwd(const lgsa_sparse_bwd_args* a, void* stream);
+lgsa_status sparse_attn_bwd_workspace(const lgsa_sparse_bwd_args* a, size_t* bytes);
 
 /* ---------------------------------------------------------------------------------------
  * vha_mix -- Virtual Head Attention (release blog, section 2.1: after attention, a light

@@ -125,3 +125,30 @@ def sparse_attn_bwd(q, k_lat, idx, dout, v_lat=None, *, dqk=None, dv=None, scale
                 gk[b, s, :dqk] += g_k[j]
                 gv[b, s, :dv] += g_v[j]
     return gq, gk, (None if v_lat is None else gv)
+
+
+def sparse_attn_lse(q, k_lat, idx, *, dqk=None, scale=None):
+    """Log-sum-exp of each DSA sparse attention row (release blog, section 2.1): for query
+    (b, i) and head h, log sum_j exp(scale <q[b,i,h], K_j>) over the keys idx[b, i, :] lists
+    (entries < 0 or >= S skipped, a repeated entry counted each time it appears), or -inf for
+    a row with no valid entry.  This is the normaliser the softmax divides by, in natural log.
+
+    q [B, Tq, H, d]; k_lat [B, S, wk]; idx [B, Tq, k] -> [B, Tq, H] float64."""
+    Q, KL = _f64(q), _f64(k_lat)
+    B, Tq, H, d = Q.shape
+    S = KL.shape[1]
+    dqk = d if dqk is None else dqk
+    if scale is None:
+        scale = 1.0 / np.sqrt(dqk)
+    idx = np.asarray(idx)
+    out = np.full((B, Tq, H), -np.inf)
+    for b in range(B):
+        for i in range(Tq):
+            sel = [int(s) for s in idx[b, i] if 0 <= int(s) < S]
+            if not sel:
+                continue
+            z = scale * (Q[b, i, :, :dqk] @ KL[b, sel, :dqk].T)
+            m = z.max(axis=1)
+            out[b, i] = m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+    return out
+

@@ -364,3 +364,52 @@ def test_hca_bwd_short_sequence_needs_no_entries(lib):
     assert lib.hca_attn_bwd_workspace(ctypes.byref(b), ctypes.byref(n_long)) == lgsa.LGSA_OK
     assert n_short.value == n_long.value > 0
 
+
+FAKE2 = FAKE + 4096
+
+
+def _sparse_bwd(**kw):
+    a = lgsa.SparseBwdArgs()
+    vals = dict(dt=lgsa.LGSA_BF16, B=1, Tq=64, H=64, d_qk=256, d_v=256, S=1000, k=128,
+                q=FAKE, k_lat=FAKE, k_row_stride=256, v_lat=FAKE, v_row_stride=256, idx=FAKE,
+                scale=0.0625, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=None,
+                workspace=None, workspace_bytes=0)
+    vals.update(kw)
+    for k, v in vals.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(dt=lgsa.LGSA_F32), lgsa.LGSA_EUNSUPPORTED, "LGSA_BF16"),
+    (dict(d_qk=128), lgsa.LGSA_EUNSUPPORTED, "256"),
+    (dict(H=32), lgsa.LGSA_EUNSUPPORTED, "multiple of 64"),
+    (dict(k=0), lgsa.LGSA_EINVAL, ">= 1"),
+    (dict(lse=None), lgsa.LGSA_EINVAL, "non-NULL"),
+    (dict(v_lat=FAKE2), lgsa.LGSA_EINVAL, "dv may be NULL only"),
+    (dict(k_row_stride=260, v_row_stride=260), lgsa.LGSA_EUNSUPPORTED, "multiples of 8"),
+    (dict(dq=FAKE_ODD), lgsa.LGSA_EINVAL, "aligned"),
+    (dict(), lgsa.LGSA_EWORKSPACE, "workspace"),
+])
+def test_sparse_bwd_validation(lib, kw, code, msg):
+    a = _sparse_bwd(**kw)
+    assert _call(lib, "sparse_attn_bwd", a) == code
+    assert msg in lgsa.last_error()
+
+
+def test_sparse_bwd_workspace_sizes(lib):
+    """The default workspace holds a whole sequence's contributions up to a budget of about
+    8 GiB (bf16 rows of 256 columns, 512 with distinct values); a long prefill is taken in
+    chunks; a workspace below the size for one row is refused."""
+    def size(**kw):
+        n = ctypes.c_size_t(0)
+        assert lib.sparse_attn_bwd_workspace(ctypes.byref(_sparse_bwd(**kw)), ctypes.byref(n)) == 0
+        return n.value
+    small = size(Tq=64, k=128)
+    assert small >= 64 * 128 * (256 * 2 + 4)
+    big = size(Tq=65536, S=65536, k=2048)
+    assert 8 << 30 <= big <= 9 << 30
+    assert size(Tq=64, k=128, v_lat=FAKE2, dv=FAKE) > small
+    a = _sparse_bwd(Tq=64, k=128, workspace=FAKE, workspace_bytes=1024)
+    assert _call(lib, "sparse_attn_bwd", a) == lgsa.LGSA_EWORKSPACE
+

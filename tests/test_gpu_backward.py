@@ -1,5 +1,6 @@
-"""Backward of the gate on the GPU against the NumPy float64 backward oracle (chain rule of the
-forward definitions; ERNIE 5.5 Flash Base release blog, section 2.1 for the gate)."""
+"""Backward of the gate, of prefill HCA and of DSA sparse attention on the GPU against the NumPy
+float64 backward oracle (chain rule of the forward definitions; ERNIE 5.5 Flash Base release
+blog, section 2.1)."""
 import numpy as np
 import pytest
 
@@ -110,3 +111,75 @@ def test_hca_backward_deterministic(torch):
     _, g2 = _hca_case(torch, 170, 1, 700, 4, 128, 128)
     for a, b in zip(g1, g2):
         assert np.array_equal(a, b)
+
+
+def _sparse_case(torch, seed, B, Tq, S, k, distinct_v, idx=None, ws_frac=None):
+    """GPU forward (ungated, with its lse) and backward of sparse attention on seeded bf16
+    inputs; ws_frac < 1 hands the backward that fraction of its default workspace, so that it
+    takes the rows in several chunks."""
+    x = synth.dsa_sparse(seed, B=B, Tq=Tq, S=S, H=64, distinct_v=distinct_v, gated=False)
+    if idx is None:
+        idx = synth.random_topk(seed, B, Tq, S, k, [S - Tq] * B)
+    dout = synth.normal(seed + 7, (B, Tq, 64, 256), 1.0, True)
+    q, kl = to_dev(x["q"]), to_dev(x["kv_lat"])
+    vl = to_dev(x["v_lat"]) if distinct_v else None
+    ix = to_dev(idx)
+    lse = torch.empty((B, Tq, 64), dtype=torch.float32, device="cuda")
+    out = lgsa.sparse_attn_fwd(q, kl, ix, v_lat=vl, lse=lse)
+    do = to_dev(dout)
+    ws = None
+    if ws_frac is not None:
+        n = lgsa.sparse_attn_bwd_workspace_bytes(q, kl, ix, out, lse, do, v_lat=vl)
+        ws = torch.empty(int(n * ws_frac) // 16 * 16, dtype=torch.uint8, device="cuda")
+    g = lgsa.sparse_attn_bwd(q, kl, ix, out, lse, do, v_lat=vl, workspace=ws)
+    torch.cuda.synchronize()
+    return x, idx, dout, from_dev(lse), [None if t is None else from_dev(t) for t in g]
+
+
+@pytest.mark.parametrize("B,Tq,S,k,distinct_v,ws_frac", [
+    (1, 40, 300, 64, False, None),     # two tiles per row, every row a full list
+    (2, 33, 200, 100, True, None),     # ragged last tile, distinct values, two sequences
+    (1, 70, 90, 128, False, None),     # early rows list fewer keys than k (-1 padding)
+    (1, 57, 400, 96, False, 0.45),     # rows taken in three chunks (accumulator carried)
+    (2, 20, 150, 40, True, 0.6),       # chunks and distinct values
+])
+def test_sparse_backward(torch, B, Tq, S, k, distinct_v, ws_frac):
+    """dq and the latent-row gradients (dk, and dv when the values are distinct) against the
+    float64 oracle, which rebuilds the softmax from q and the rows; the forward's lse against
+    the oracle's log-sum-exp."""
+    x, idx, dout, lse, (dq, dk, dv) = _sparse_case(torch, 300 + Tq, B, Tq, S, k, distinct_v,
+                                                   ws_frac=ws_frac)
+    r_q, r_k, r_v = backward.sparse_attn_bwd(x["q"], x["kv_lat"], idx, dout,
+                                             v_lat=x.get("v_lat"))
+    bf16_ok(dq, r_q, "dq")
+    bf16_ok(dk, r_k, "dk")
+    if distinct_v:
+        bf16_ok(dv, r_v, "dv")
+    r_lse = backward.sparse_attn_lse(x["q"], x["kv_lat"], idx)
+    assert np.allclose(lse, r_lse, rtol=0, atol=1e-3), float(np.max(np.abs(lse - r_lse)))
+
+
+def test_sparse_backward_repeats_skips_and_empty_rows(torch):
+    """Entries listed twice count twice, out-of-range and negative entries are skipped, a row
+    with no valid entry gets dq = 0 and lse = -inf, and rows no entry lists get zero gradient."""
+    B, Tq, S, k = 1, 6, 80, 48
+    rng = np.random.default_rng(11)
+    idx = rng.integers(0, 60, size=(B, Tq, k)).astype(np.int32)
+    idx[0, 0, 5] = idx[0, 0, 6]
+    idx[0, 1, :10] = -1
+    idx[0, 2, 3] = S + 3
+    idx[0, 3, :] = -1
+    x, idx, dout, lse, (dq, dk, _) = _sparse_case(torch, 320, B, Tq, S, k, False, idx=idx)
+    r_q, r_k, _ = backward.sparse_attn_bwd(x["q"], x["kv_lat"], idx, dout)
+    bf16_ok(dq, r_q, "dq")
+    bf16_ok(dk, r_k, "dk")
+    assert np.all(dq[0, 3] == 0) and np.all(lse[0, 3] == -np.inf)
+    assert np.all(dk[0, 60:] == 0)
+
+
+def test_sparse_backward_deterministic(torch):
+    g1 = _sparse_case(torch, 330, 1, 64, 500, 128, False)[-1]
+    g2 = _sparse_case(torch, 330, 1, 64, 500, 128, False)[-1]
+    for a, b in zip(g1[:2], g2[:2]):
+        assert np.array_equal(a, b)
+

@@ -109,3 +109,42 @@ def test_sparse_backward_matches_finite_differences(orc):
     assert np.allclose(dq2, _fd(loss2, q), rtol=1e-5, atol=1e-7)
     assert np.allclose(dk2, _fd(loss2, lat), rtol=1e-5, atol=1e-7)
     assert np.allclose(dv2, _fd(loss2, vl), rtol=1e-5, atol=1e-7)
+
+
+def test_sparse_lse_closed_forms():
+    """Equal keys: lse = scale <q, k> + log n (n counts repeats); one key: scale <q, k>; no
+    valid entry: -inf; a huge logit does not overflow."""
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, 3, 2, 8))
+    row = rng.standard_normal(8)
+    lat = np.tile(row, (1, 6, 1))
+    idx = np.array([[[0, 1, 2, 2, -1], [4, -1, -1, 9, -1], [-1, -1, 6, 7, -3]]], np.int32)
+    lse = backward.sparse_attn_lse(q, lat, idx, scale=0.5)
+    dot = 0.5 * (q[0] @ row)
+    assert np.allclose(lse[0, 0], dot[0] + np.log(4.0), rtol=0, atol=1e-12)
+    assert np.allclose(lse[0, 1], dot[1], rtol=0, atol=1e-12)
+    assert np.all(lse[0, 2] == -np.inf)
+    big = backward.sparse_attn_lse(np.full((1, 1, 1, 2), 300.0), np.ones((1, 2, 2)),
+                                   np.array([[[0, 1]]], np.int32), scale=1.0)
+    assert np.isclose(big[0, 0, 0], 600.0 + np.log(2.0), rtol=0, atol=1e-9)
+
+
+def test_sparse_lse_normalises_the_forward(orc):
+    """exp(scale <q, K_j> - lse) are the softmax weights of the forward oracle: with V set to
+    the identity rows, the forward returns exactly those weights."""
+    rng = np.random.default_rng(8)
+    S, d = 12, 16
+    q = rng.standard_normal((1, 2, 3, d))
+    lat = rng.standard_normal((1, S, d))
+    idx = np.array([[[0, 3, 5, 11], [2, 2, 7, -1]]], np.int32)
+    lse = backward.sparse_attn_lse(q, lat, idx)
+    eye = np.zeros((1, S, d))
+    eye[0, np.arange(S), np.arange(S)] = 1.0
+    out = orc.sparse_attn(q, lat, idx, v_lat=eye)
+    for i in range(2):
+        w = np.zeros((3, d))
+        for s in idx[0, i]:
+            if s >= 0:
+                w[:, s] += np.exp(q[0, i] @ lat[0, s] / np.sqrt(d) - lse[0, i])
+        assert np.allclose(out[i] if out.ndim == 3 else out[0, i], w, rtol=0, atol=1e-12)
+
