@@ -225,8 +225,36 @@ def run_c3(torch, lgsa, synth, to_dev, iters):
     sp_flops = 4.0 * d * pairs * H + 2.0 * T * 1024 * H * d
     ind_pairs = T * (T + 1) // 2
     ind_flops = ind_pairs * (4 * 2 * 64 + 8)
+
+    # backward of the sparse attention over the same lists: an ungated forward that also
+    # writes the log-sum-exp, an N(0,1) output gradient, then sparse_attn_bwd (the latent rows
+    # serve as keys and values, so dk holds both gradients); 10 d flops per (row, key, head)
+    lse = torch.empty((1, T, H), dtype=torch.float32, device="cuda")
+    o_ung = lgsa.sparse_attn_fwd(ds["q"], ds["kv_lat"], idx, lse=lse)
+    g = torch.Generator(device="cuda").manual_seed(13)
+    dout = torch.randn(1, T, H, d, device="cuda", generator=g).to(torch.bfloat16)
+    dq = torch.empty_like(ds["q"])
+    dk = torch.empty((1, T, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(lgsa.sparse_attn_bwd_workspace_bytes(ds["q"], ds["kv_lat"], idx, o_ung, lse,
+                                                          dout), dtype=torch.uint8, device="cuda")
+
+    def bwd():
+        lgsa.sparse_attn_bwd(ds["q"], ds["kv_lat"], idx, o_ung, lse, dout, dq=dq, dk=dk,
+                             workspace=ws)
+
+    bwd()
+    torch.cuda.synchronize()
+    bwd_ms = []
+    for _ in range(iters):
+        a = tm.event()
+        bwd()
+        b = tm.event()
+        torch.cuda.synchronize()
+        bwd_ms.append(a.elapsed_time(b))
+    del ws, dq, dk, dout, o_ung, lse
     return dict(index_ms=float(np.median(idx_ms)), sparse_ms=float(np.median(sp_ms)),
-                sparse_flops=sp_flops, index_flops=float(ind_flops))
+                sparse_flops=sp_flops, index_flops=float(ind_flops),
+                bwd_ms=float(np.median(bwd_ms)), bwd_flops=10.0 * d * pairs * H)
 
 
 def run_csa(torch, lgsa, synth, to_dev, iters):
@@ -570,6 +598,9 @@ def main():
             sparse_mfma_frac=round(sp_tf / PEAK_BF16_TFLOPS, 4),
             indexer_ms=round(r3["index_ms"], 3), indexer_TFLOPs=round(ix_tf, 1),
             indexer_fp32_frac=round(ix_tf / PEAK_FP32_TFLOPS, 4))
+        bw_tf = r3["bwd_flops"] / (r3["bwd_ms"] * 1e-3) / 1e12
+        secondary["sparse_bwd_prefill"] = dict(ms=round(r3["bwd_ms"], 3), TFLOPs=round(bw_tf, 1),
+                                               mfma_frac=round(bw_tf / PEAK_BF16_TFLOPS, 4))
     if 3 in cfgs:
         rc = run_csa(torch, lgsa, synth, to_dev, 3)
         tf = rc["flops"] / (rc["ms"] * 1e-3) / 1e12

@@ -49,6 +49,7 @@ constexpr size_t BUF_BUDGET = 8ull << 30;      // bytes of contributions held pe
 constexpr long long SCAN_BLOCK = 4096;         // counters per block of the scan
 constexpr long long MAX_COUNTERS = SCAN_BLOCK * 16384;  // what the two-level scan covers
 constexpr int MAX_RANGES = 256;
+constexpr int RANK_LDS_KEYS = 65536;                   // keys the LDS counters of a range hold
 
 __device__ __forceinline__ void store4(uint16_t* dst, const f32x4_t& v) {
   uint2 r;
@@ -73,6 +74,28 @@ __device__ __forceinline__ float dot8(const uint4& a, const uint4& b) {
 __device__ __forceinline__ int load_slot(const int32_t* sl, int j0, int k, int lane) {
   const int j = j0 + lane;
   return (lane < KT && j < k) ? sl[j] : -1;
+}
+
+// The four P fragments of C^T (key rows 16nb + l16, heads 32ks + 8g .. +7) read in one asm
+// block that waits for them itself.  Read through the builtins, the compiler made each tile
+// wait for the next tile's gathers before these reads (it could not tell that the LDS DMA in
+// flight does not write P), which took away most of the overlap of gathers with compute.
+__device__ __forceinline__ void read_p(Frag8 (&bp)[2][2], const char* a) {
+  const uint32_t ad = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)a;
+  uint4 x0, x1, x2, x3;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:64\n\t"
+      "ds_read_b128 %2, %4 offset:%5\n\t"
+      "ds_read_b128 %3, %4 offset:%6\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(x3)
+      : "v"(ad), "i"(16 * PROW), "i"(16 * PROW + 64)
+      : "memory");
+  bp[0][0].u = x0;
+  bp[0][1].u = x1;
+  bp[1][0].u = x2;
+  bp[1][1].u = x3;
 }
 
 // grid: chunk row q (of n_rows) x head group; rows 0 .. n_wg - 1 of buf are the scratch rows
@@ -238,8 +261,6 @@ void sparse_bwd_kernel(SparseBwdParams p, long long row0, const int32_t* __restr
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) ck[mb][nb] = cv[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // the dS products first: the compiler waits for the gathers in flight before the first read
-    // of P (it cannot tell that they do not write it), so that wait comes as late as it can
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -249,20 +270,19 @@ void sparse_bwd_kernel(SparseBwdParams p, long long row0, const int32_t* __restr
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) ck[mb][nb] = mfma_16x16x32(cq[ks][mb], bd, ck[mb][nb]);
       }
+    Frag8 bp[2][2];
+    read_p(bp, pt + l16 * PROW + 16 * g);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        Frag8 bp;
-        bp.u = *(const uint4*)(pt + (16 * nb + l16) * PROW + 16 * g + 64 * ks);
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
           if (ALIAS)
-            ck[mb][nb] = mfma_16x16x32(cq[2 + ks][mb], bp, ck[mb][nb]);
+            ck[mb][nb] = mfma_16x16x32(cq[2 + ks][mb], bp[nb][ks], ck[mb][nb]);
           else
-            cv[mb][nb] = mfma_16x16x32(cq[2 + ks][mb], bp, cv[mb][nb]);
+            cv[mb][nb] = mfma_16x16x32(cq[2 + ks][mb], bp[nb][ks], cv[mb][nb]);
         }
-      }
     const int rix = slot_cur >= 0 ? (int)(n_wg + (long long)slot_cur * n_hg + hg) : (int)blockIdx.x;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -318,6 +338,35 @@ __global__ __launch_bounds__(256) void sparse_bwd_rank_kernel(const int32_t* __r
     }
     __syncthreads();
   }
+}
+
+// The same ranks with the counters of the range in LDS: two 16-bit counters per word (key s
+// in half s & 1 of word s / 2), so up to 65536 keys; a count stays below 2^16 because the range
+// holds fewer than 2^16 entries.  The range's counts then go to cnt (every key written).
+__global__ __launch_bounds__(1024) void sparse_bwd_rank_lds_kernel(
+    const int32_t* __restrict__ idx, int k, int S, int n_rows, int qr, int R,
+    int32_t* __restrict__ cnt, int32_t* __restrict__ rank) {
+  __shared__ uint32_t c16[RANK_LDS_KEYS / 2];
+  const int r = blockIdx.x;
+  for (int i = threadIdx.x; i < (S + 1) / 2; i += 1024) c16[i] = 0u;
+  __syncthreads();
+  const int q1 = min(n_rows, (r + 1) * qr);
+  for (int q = r * qr; q < q1; ++q) {
+    const int32_t* ir = idx + (size_t)q * k;
+    int32_t* rr = rank + (size_t)q * k;
+    for (int j = threadIdx.x; j < k; j += 1024) {
+      const int s = ir[j];
+      int rk = -1;
+      if (s >= 0 && s < S) {
+        const int sh = 16 * (s & 1);
+        rk = (int)((atomicAdd(&c16[s >> 1], 1u << sh) >> sh) & 0xFFFFu);
+      }
+      rr[j] = rk;
+    }
+    __syncthreads();
+  }
+  for (int s = threadIdx.x; s < S; s += 1024)
+    cnt[(size_t)s * R + r] = (int32_t)((c16[s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
 }
 
 // exclusive scan of one block of 4096 counters in place; the block's total to bsum
@@ -465,6 +514,9 @@ size_t sbwd_layout(const SparseBwdParams& p, long long qc, SbwdPlan& pl) {
   long long rmax = std::max(1ll, std::min((long long)MAX_RANGES, MAX_COUNTERS / p.S));
   rmax = std::min(rmax, qc);
   pl.qr = (int)((qc + rmax - 1) / rmax);
+  // ranges short enough for the 16-bit LDS counters when the keys fit (a few more ranges)
+  if (p.S <= RANK_LDS_KEYS && (long long)pl.qr * p.k >= 65536 && p.k < 65536)
+    pl.qr = std::max(1, 65535 / p.k);
   pl.rmax = (int)((qc + pl.qr - 1) / pl.qr);
   pl.qc = (int)qc;
   pl.chunks = (int)((p.Tq + qc - 1) / qc);
@@ -509,9 +561,10 @@ SbwdPlan sbwd_plan(const SparseBwdParams& p, size_t avail) {
 
 size_t sparse_bwd_workspace(const SparseBwdParams& p) { return sbwd_plan(p, SIZE_MAX).bytes; }
 
+// one row at a time, unless the default (a single chunk needs no accumulator) is smaller
 size_t sparse_bwd_min_workspace(const SparseBwdParams& p) {
   SbwdPlan pl;
-  return sbwd_layout(p, 1, pl);
+  return std::min(sbwd_layout(p, 1, pl), sparse_bwd_workspace(p));
 }
 
 hipError_t launch_sparse_bwd(const SparseBwdParams& p, hipStream_t stream) {
@@ -533,10 +586,16 @@ hipError_t launch_sparse_bwd(const SparseBwdParams& p, hipStream_t stream) {
       const long long nblk = (counters + SCAN_BLOCK - 1) / SCAN_BLOCK;
       const int32_t* idx = p.idx + (size_t)row0 * p.k;
       const long long n_pairs = (long long)n_rows * p.k;
-      hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)std::min(4096ll, (counters + 255) / 256)),
-                         dim3(256), 0, stream, cnt, counters);
-      hipLaunchKernelGGL(sparse_bwd_rank_kernel, dim3(R), dim3(256), 0, stream, idx, p.k, p.S,
-                         n_rows, pl.qr, R, cnt, rank);
+      if (p.S <= RANK_LDS_KEYS && (long long)pl.qr * p.k < 65536) {
+        hipLaunchKernelGGL(sparse_bwd_rank_lds_kernel, dim3(R), dim3(1024), 0, stream, idx, p.k,
+                           p.S, n_rows, pl.qr, R, cnt, rank);
+      } else {
+        hipLaunchKernelGGL(fill_i32_kernel,
+                           dim3((unsigned)std::min(4096ll, (counters + 255) / 256)), dim3(256), 0,
+                           stream, cnt, counters);
+        hipLaunchKernelGGL(sparse_bwd_rank_kernel, dim3(R), dim3(256), 0, stream, idx, p.k, p.S,
+                           n_rows, pl.qr, R, cnt, rank);
+      }
       hipLaunchKernelGGL(scan_local_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, cnt,
                          counters, bsum);
       hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(1024), 0, stream, bsum, (int)nblk);

@@ -142,6 +142,7 @@ def _sparse_case(torch, seed, B, Tq, S, k, distinct_v, idx=None, ws_frac=None):
     (1, 70, 90, 128, False, None),     # early rows list fewer keys than k (-1 padding)
     (1, 57, 400, 96, False, 0.45),     # rows taken in three chunks (accumulator carried)
     (2, 20, 150, 40, True, 0.6),       # chunks and distinct values
+    (1, 12, 70000, 64, False, None),   # more keys than the LDS counters hold: global counters
 ])
 def test_sparse_backward(torch, B, Tq, S, k, distinct_v, ws_frac):
     """dq and the latent-row gradients (dk, and dv when the values are distinct) against the
