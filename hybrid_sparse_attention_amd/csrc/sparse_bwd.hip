@@ -25,8 +25,10 @@
 //           LDS as [key][head] bfloat16; then dq^T = K^T dS^T over the tile's 32 keys for dims
 //           128(w / 4) .. +127 (K through the transposing read) and the key-side contributions
 //           C^T = Q^T dS^T + dO^T P^T for dims 32w .. +31 (Q^T, dO^T in registers, staged
-//           through LDS once per row).  Gathers are double buffered as in the forward; the
-//           contributions are stored without waiting for them.
+//           through LDS once per row).  Tiles are pipelined (the scores of tile t + 1 are
+//           computed between the same two barriers as the products of tile t), K tiles are
+//           gathered by LDS DMA two tiles ahead, and the contributions are stored without
+//           waiting for them.
 //   reduce  one wave per key: its slots in order, plus the accumulator of earlier chunks.
 #include <algorithm>
 #include <cstdint>
@@ -76,13 +78,20 @@ __device__ __forceinline__ int load_slot(const int32_t* sl, int j0, int k, int l
   return (lane < KT && j < k) ? sl[j] : -1;
 }
 
-// The four P fragments of C^T (key rows 16nb + l16, heads 32ks + 8g .. +7) read in one asm
-// block that waits for them itself.  Read through the builtins, the compiler made each tile
-// wait for the next tile's gathers before these reads (it could not tell that the LDS DMA in
-// flight does not write P), which took away most of the overlap of gathers with compute.
-__device__ __forceinline__ void read_p(Frag8 (&bp)[2][2], const char* a) {
-  const uint32_t ad = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)a;
-  uint4 x0, x1, x2, x3;
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t lds_addr(const char* a) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)a;
+}
+
+// The P and dS tiles are read in asm blocks that wait for their own reads.  Read through the
+// builtins, the compiler made each tile wait for the gathers in flight before these reads (it
+// could not tell that the LDS DMA does not write them), which took away the overlap of the
+// gathers with compute.  Four 16-byte rows: key rows l16 and 16 + l16, heads 8g .. 8g+7 and
+// 32 + 8g .. 32 + 8g + 7, from `a` = row l16, column 8g.
+__device__ __forceinline__ void read_rows4(Frag8 (&f)[2][2], const char* a) {
+  v4i_t x0, x1, x2, x3;
   asm volatile(
       "ds_read_b128 %0, %4\n\t"
       "ds_read_b128 %1, %4 offset:64\n\t"
@@ -90,28 +99,47 @@ __device__ __forceinline__ void read_p(Frag8 (&bp)[2][2], const char* a) {
       "ds_read_b128 %3, %4 offset:%6\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(x3)
-      : "v"(ad), "i"(16 * PROW), "i"(16 * PROW + 64)
-      : "memory");
-  bp[0][0].u = x0;
-  bp[0][1].u = x1;
-  bp[1][0].u = x2;
-  bp[1][1].u = x3;
+      : "v"(lds_addr(a)), "i"(16 * PROW), "i"(16 * PROW + 64));
+  f[0][0].u = make_uint4(x0[0], x0[1], x0[2], x0[3]);
+  f[0][1].u = make_uint4(x1[0], x1[1], x1[2], x1[3]);
+  f[1][0].u = make_uint4(x2[0], x2[1], x2[2], x2[3]);
+  f[1][1].u = make_uint4(x3[0], x3[1], x3[2], x3[3]);
 }
 
-// grid: chunk row q (of n_rows) x head group; rows 0 .. n_wg - 1 of buf are the scratch rows
+// two transposing reads, of rows K_0..K_3 at `a` and of the rows 16 further down
+__device__ __forceinline__ Frag8 read_tr_pair(const char* a) {
+  v2i_t lo, hi;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %2\n\t"
+      "ds_read_b64_tr_b16 %1, %2 offset:%3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(lo), "=v"(hi)
+      : "v"(lds_addr(a)), "i"(16 * PROW));
+  Frag8 f;
+  f.u = make_uint4(lo[0], lo[1], hi[0], hi[1]);
+  return f;
+}
+
+// grid: chunk row q (of n_rows) x head group; rows 0 .. n_wg - 1 of buf are the scratch rows.
+// Tiles are pipelined: between two barriers a wave computes S^T, dP^T and writes P, dS of tile
+// t + 1 (stage A) and the products of tile t (stage B), so one barrier per tile suffices and
+// the VALU work of A overlaps the matrix work of B.  K tiles are triple buffered (t, t + 1, and
+// t + 2 in flight), P / dS double buffered.
 template <bool ALIAS>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sparse_bwd_kernel(SparseBwdParams p, long long row0, const int32_t* __restrict__ slot,
                        uint16_t* __restrict__ buf) {
   constexpr int RW = ALIAS ? D : 2 * D;  // columns of one contribution row
+  constexpr int PD_P = KT * PROW;        // P after scale*dS in one P / dS buffer
+  constexpr int PD = 2 * PD_P;
   __shared__ __attribute__((aligned(1024))) char kt0[TILE];
   __shared__ __attribute__((aligned(1024))) char kt1[TILE];
+  __shared__ __attribute__((aligned(1024))) char kt2[TILE];
   __shared__ __attribute__((aligned(1024))) char vt0[ALIAS ? 16 : TILE];
   __shared__ __attribute__((aligned(1024))) char vt1[ALIAS ? 16 : TILE];
-  __shared__ __attribute__((aligned(16))) char dst_[KT * PROW];  // scale*dS [key][head]
-  __shared__ __attribute__((aligned(16))) char pt[KT * PROW];    // P        [key][head]
-  __shared__ __attribute__((aligned(16))) char qs[64 * QROW];    // Q   [head][dim]
-  __shared__ __attribute__((aligned(16))) char ds[64 * QROW];    // dO  [head][dim]
+  __shared__ __attribute__((aligned(1024))) char vt2[ALIAS ? 16 : TILE];
+  __shared__ __attribute__((aligned(16))) char pd[2 * PD];     // [key][head] bf16, two tiles
+  __shared__ __attribute__((aligned(16))) char qs[64 * QROW];  // Q, then dO [head][dim]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -134,21 +162,24 @@ void sparse_bwd_kernel(SparseBwdParams p, long long row0, const int32_t* __restr
   const uint16_t* vl = (const uint16_t*)p.v_lat + (size_t)b * p.S * p.v_stride;
   const int n_tiles = (p.k + KT - 1) / KT;
 
-  // tile 0 in flight first
+  // tiles 0 and 1 in flight first
   const int ix0 = valid_ix(load_ix(idx, 0, p.k, lane), p.S);
-  uint32_t valid_cur = (uint32_t)__ballot(ix0 >= 0);
+  const uint32_t valid0 = (uint32_t)__ballot(ix0 >= 0);
   gather_tile<NW>(kl, p.k_stride, ix0, kt0, wave, lane);
   if (!ALIAS) gather_tile<NW>(vl, p.v_stride, ix0, vt0, wave, lane);
-  int slot_cur = load_slot(sl, 0, p.k, lane);
-  int ix_nxt = load_ix(idx, KT, p.k, lane);
-  int slot_nxt = load_slot(sl, KT, p.k, lane);
-
-  // Q and dO of the 64 heads to LDS (for the transposed operands), and in registers for S^T
-  for (int i = tid; i < 64 * 32; i += 64 * NW) {
-    const int h = i >> 5, c = i & 31;
-    *(uint4*)(qs + h * QROW + 16 * c) = *(const uint4*)(Q + h * D + 8 * c);
-    *(uint4*)(ds + h * QROW + 16 * c) = *(const uint4*)(dO + h * D + 8 * c);
+  uint32_t valid_n1 = 0;
+  if (n_tiles > 1) {
+    const int ix1 = valid_ix(load_ix(idx, KT, p.k, lane), p.S);
+    valid_n1 = (uint32_t)__ballot(ix1 >= 0);
+    gather_tile<NW>(kl, p.k_stride, ix1, kt1, wave, lane);
+    if (!ALIAS) gather_tile<NW>(vl, p.v_stride, ix1, vt1, wave, lane);
   }
+  int ix_n2 = load_ix(idx, 2 * KT, p.k, lane);
+  int slot_cur = load_slot(sl, 0, p.k, lane);
+
+  // Q and dO in registers for S^T (and D), and through LDS (one after the other) for the
+  // transposed A operand of C^T: rows = dims 32w + 16mb + l16, contraction = heads
+  // 32(ks & 1) + 8g .. +7 of Q (ks < 2) or dO (ks >= 2)
   Frag8 qf[8], df[8];
   float dsum = 0.f;
 #pragma unroll
@@ -161,22 +192,27 @@ void sparse_bwd_kernel(SparseBwdParams p, long long row0, const int32_t* __restr
   const float lse2 = p.lse[hrow + hl] * LOG2E;
   const bool live = lse2 > -INFINITY;
   const float scale_log2 = p.scale * LOG2E;
-  wait_all();
-  __syncthreads();
-
-  // A operand of C^T: rows = dims 32w + 16mb + l16, contraction = heads 32(ks & 1) + 8g .. +7
-  // of Q (ks < 2) or dO (ks >= 2), read through the transposing LDS read
   Frag8 cq[4][2];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const char* base = (ks < 2 ? qs : ds) + (32 * (ks & 1) + 8 * g + (l16 >> 2)) * QROW;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int col = 32 * wave + 16 * mb + 4 * (l16 & 3);
-      const uint2 lo = lds_read_tr16(base + 2 * col);
-      const uint2 hi = lds_read_tr16(base + 4 * QROW + 2 * col);
-      cq[ks][mb].u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  for (int half = 0; half < 2; ++half) {
+    const uint16_t* src = half ? dO : Q;
+    for (int i = tid; i < 64 * 32; i += 64 * NW) {
+      const int h = i >> 5, c = i & 31;
+      *(uint4*)(qs + h * QROW + 16 * c) = *(const uint4*)(src + h * D + 8 * c);
     }
+    __syncthreads();
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq) {
+      const char* base = qs + (32 * kq + 8 * g + (l16 >> 2)) * QROW;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int col = 32 * wave + 16 * mb + 4 * (l16 & 3);
+        const uint2 lo = lds_read_tr16(base + 2 * col);
+        const uint2 hi = lds_read_tr16(base + 4 * QROW + 2 * col);
+        cq[2 * half + kq][mb].u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    }
+    __syncthreads();
   }
 
   // lane-constant LDS offsets: key rows 16kh + l16 read row-wise (as the forward's scores) and
@@ -192,98 +228,103 @@ void sparse_bwd_kernel(SparseBwdParams p, long long row0, const int32_t* __restr
   // dS^T operand of dq^T: column = head hl, contraction slots 8g .. 8g+7 = keys 4g .. 4g+3 and
   // 16 + 4g .. 16 + 4g + 3 (the order the K^T read gives)
   const int dsb = (4 * g + (l16 >> 2)) * PROW + 2 * (16 * hb + 4 * (l16 & 3));
+  const int rwb = l16 * PROW + 16 * g;  // C^T operand rows l16 (+16), heads 8g (+32)
 
   f32x4_t dq[8];
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) dq[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto body = [&](int ti, const char* kc, const char* vc, char* kn, char* vn) {
-    uint32_t valid_nxt = 0;
-    if (ti + 1 < n_tiles) {
-      const int ixv = valid_ix(ix_nxt, p.S);
-      valid_nxt = (uint32_t)__ballot(ixv >= 0);
-      gather_tile<NW>(kl, p.k_stride, ixv, kn, wave, lane);
-      if (!ALIAS) gather_tile<NW>(vl, p.v_stride, ixv, vn, wave, lane);
-    }
-    const int ix_after = load_ix(idx, KT * (ti + 2), p.k, lane);
-    const int slot_after = load_slot(sl, KT * (ti + 2), p.k, lane);
-
-    // S^T and dP^T: keys 16kh + 4g + r, head hl
+  // stage A: S^T and dP^T of a tile (keys 16kh + 4g + r, head hl), P and scale*dS to LDS
+  auto stage_a = [&](const char* kx, const char* vx, uint32_t valid, char* pw) {
     f32x4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       Frag8 ka;
-      ka.u = *(const uint4*)(kc + kb[kk & 3] + 256 * (kk >> 2));
+      ka.u = *(const uint4*)(kx + kb[kk & 3] + 256 * (kk >> 2));
       s = mfma_16x16x32(ka, qf[kk], s);
       if (ALIAS) {
         dp = mfma_16x16x32(ka, df[kk], dp);
       } else {
         Frag8 va;
-        va.u = *(const uint4*)(vc + kb[kk & 3] + 256 * (kk >> 2));
+        va.u = *(const uint4*)(vx + kb[kk & 3] + 256 * (kk >> 2));
         dp = mfma_16x16x32(va, df[kk], dp);
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int key = 16 * kh + 4 * g + r;
-      const bool v = live && ((valid_cur >> key) & 1u);
+      const bool v = live && ((valid >> key) & 1u);
       const float pr = v ? fast_exp2(s[r] * scale_log2 - lse2) : 0.f;
       const float dsv = pr * (dp[r] - Dh) * p.scale;
       const bf16x2_t pp = {(__bf16)pr, (__bf16)dsv};
       const uint32_t u = __builtin_bit_cast(uint32_t, pp);
-      *(uint16_t*)(pt + key * PROW + 2 * hl) = (uint16_t)(u & 0xFFFFu);
-      *(uint16_t*)(dst_ + key * PROW + 2 * hl) = (uint16_t)(u >> 16);
+      *(uint16_t*)(pw + PD_P + key * PROW + 2 * hl) = (uint16_t)(u & 0xFFFFu);
+      *(uint16_t*)(pw + key * PROW + 2 * hl) = (uint16_t)(u >> 16);
     }
-    lds_barrier();  // P and dS of the tile are in LDS (the next tile's gathers stay in flight)
+  };
 
-    // dq^T (dims 128kh + 16mb + l16, head hl) += K^T dS^T
-    Frag8 bds;
-    {
-      const uint2 lo = lds_read_tr16(dst_ + dsb);
-      const uint2 hi = lds_read_tr16(dst_ + dsb + 16 * PROW);
-      bds.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    }
-    const int vh_t = opaque(vh);
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const int pos = (2 * (8 * kh + mb) + vh_t) ^ vsw;
-      const char* a = kc + vrow + 16 * pos;
-      const uint2 lo = lds_read_tr16(a);
-      const uint2 hi = lds_read_tr16(a + 16 * TROW);
-      Frag8 ka;
-      ka.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      dq[mb] = mfma_16x16x32(ka, bds, dq[mb]);
-    }
-
-    // C^T (dims 32w + 16mb + 4g + r, key 16nb + l16) = Q^T dS^T (+ dO^T P^T)
+  // Stages A (of the next tile: S^T, dP^T from kx, then P and scale*dS to pw) and B (of the
+  // current tile: dq^T += K^T dS^T from kc, and the contributions C^T = Q^T dS^T (+ dO^T P^T)
+  // from pr) written interleaved, one step of each per contraction step, so that the matrix
+  // cores have independent work while A's chains and LDS reads wait.
+  auto tile_ops = [&](const char* kx, const char* vx, uint32_t valid, char* pw, const char* kc,
+                      const char* pr_, int slot_c) {
+    const Frag8 bds = read_tr_pair(pr_ + dsb);
+    Frag8 bd[2][2], bp[2][2];
+    read_rows4(bd, pr_ + rwb);
+    read_rows4(bp, pr_ + PD_P + rwb);
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
     f32x4_t ck[2][2], cv[2][2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) ck[mb][nb] = cv[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int vh_t = opaque(vh);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        Frag8 bd;
-        bd.u = *(const uint4*)(dst_ + (16 * nb + l16) * PROW + 16 * g + 64 * ks);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) ck[mb][nb] = mfma_16x16x32(cq[ks][mb], bd, ck[mb][nb]);
+    for (int kk = 0; kk < 8; ++kk) {
+      Frag8 ka;
+      ka.u = *(const uint4*)(kx + kb[kk & 3] + 256 * (kk >> 2));
+      const int pos = (2 * (8 * kh + kk) + vh_t) ^ vsw;
+      const char* at = kc + vrow + 16 * pos;
+      const uint2 lo = lds_read_tr16(at);
+      const uint2 hi = lds_read_tr16(at + 16 * TROW);
+      Frag8 kq;
+      kq.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      s = mfma_16x16x32(ka, qf[kk], s);
+      if (ALIAS) {
+        dp = mfma_16x16x32(ka, df[kk], dp);
+      } else {
+        Frag8 va;
+        va.u = *(const uint4*)(vx + kb[kk & 3] + 256 * (kk >> 2));
+        dp = mfma_16x16x32(va, df[kk], dp);
       }
-    Frag8 bp[2][2];
-    read_p(bp, pt + l16 * PROW + 16 * g);
+      dq[kk] = mfma_16x16x32(kq, bds, dq[kk]);
+      // C^T products j = 2kk, 2kk + 1 of 16: nb = j / 8, ks = (j / 4) % 2, mb = (j / 2) % 2,
+      // and j % 2 picks the dS (Q) or the P (dO) term
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * kk + jj;
+        const int nb = j >> 3, ks = (j >> 2) & 1, mb = (j >> 1) & 1;
+        if ((j & 1) == 0)
+          ck[mb][nb] = mfma_16x16x32(cq[ks][mb], bd[nb][ks], ck[mb][nb]);
+        else if (ALIAS)
+          ck[mb][nb] = mfma_16x16x32(cq[2 + ks][mb], bp[nb][ks], ck[mb][nb]);
+        else
+          cv[mb][nb] = mfma_16x16x32(cq[2 + ks][mb], bp[nb][ks], cv[mb][nb]);
+      }
+    }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          if (ALIAS)
-            ck[mb][nb] = mfma_16x16x32(cq[2 + ks][mb], bp[nb][ks], ck[mb][nb]);
-          else
-            cv[mb][nb] = mfma_16x16x32(cq[2 + ks][mb], bp[nb][ks], cv[mb][nb]);
-        }
-    const int rix = slot_cur >= 0 ? (int)(n_wg + (long long)slot_cur * n_hg + hg) : (int)blockIdx.x;
+    for (int r = 0; r < 4; ++r) {
+      const int key = 16 * kh + 4 * g + r;
+      const bool v = live && ((valid >> key) & 1u);
+      const float pv = v ? fast_exp2(s[r] * scale_log2 - lse2) : 0.f;
+      const float dsv = pv * (dp[r] - Dh) * p.scale;
+      const bf16x2_t pp = {(__bf16)pv, (__bf16)dsv};
+      const uint32_t u = __builtin_bit_cast(uint32_t, pp);
+      *(uint16_t*)(pw + PD_P + key * PROW + 2 * hl) = (uint16_t)(u & 0xFFFFu);
+      *(uint16_t*)(pw + key * PROW + 2 * hl) = (uint16_t)(u >> 16);
+    }
+    const int rix = slot_c >= 0 ? (int)(n_wg + (long long)slot_c * n_hg + hg) : (int)blockIdx.x;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int rk = __shfl(rix, 16 * nb + l16);
@@ -294,19 +335,38 @@ void sparse_bwd_kernel(SparseBwdParams p, long long row0, const int32_t* __restr
         if (!ALIAS) store4(dst + D + 16 * mb, cv[mb][nb]);
       }
     }
-    // this wave's gathers of tile ti + 1 and the entries of tile ti + 2 have landed (they
-    // were issued before the stores, and vector memory operations complete in order); the
-    // stores themselves stay in flight
+  };
+
+  wait_all();  // tiles 0 and 1 (this wave's part) and the entries loaded so far
+  __syncthreads();
+  stage_a(kt0, vt0, valid0, pd);
+  lds_barrier();
+
+  auto body = [&](int ti, const char* kc, const char* k1, const char* v1, char* k2, char* v2) {
+    uint32_t valid_n2 = 0;
+    if (ti + 2 < n_tiles) {
+      const int ixv = valid_ix(ix_n2, p.S);
+      valid_n2 = (uint32_t)__ballot(ixv >= 0);
+      gather_tile<NW>(kl, p.k_stride, ixv, k2, wave, lane);
+      if (!ALIAS) gather_tile<NW>(vl, p.v_stride, ixv, v2, wave, lane);
+    }
+    const int ix_after = load_ix(idx, KT * (ti + 3), p.k, lane);
+    const int slot_after = load_slot(sl, KT * (ti + 1), p.k, lane);
+    // past the last tile, stage A works on a stale buffer with no valid key and writes zeros
+    // that nobody reads
+    tile_ops(k1, v1, valid_n1, pd + ((ti + 1) & 1) * PD, kc, pd + (ti & 1) * PD, slot_cur);
+    // this wave's gathers of tile ti + 2 and its entry loads have landed (issued before the
+    // stores, and vector memory operations complete in order); the stores stay in flight
     wait_vm<ALIAS ? 4 : 8>();
     lds_barrier();
-    valid_cur = valid_nxt;
-    ix_nxt = ix_after;
-    slot_cur = slot_nxt;
-    slot_nxt = slot_after;
+    valid_n1 = valid_n2;
+    ix_n2 = ix_after;
+    slot_cur = slot_after;
   };
-  for (int ti = 0; ti < n_tiles; ti += 2) {
-    body(ti, kt0, vt0, kt1, vt1);
-    if (ti + 1 < n_tiles) body(ti + 1, kt1, vt1, kt0, vt0);
+  for (int ti = 0; ti < n_tiles; ti += 3) {
+    body(ti, kt0, kt1, vt1, kt2, vt2);
+    if (ti + 1 < n_tiles) body(ti + 1, kt1, kt2, vt2, kt0, vt0);
+    if (ti + 2 < n_tiles) body(ti + 2, kt2, kt0, vt0, kt1, vt1);
   }
 
   uint16_t* dqr = (uint16_t*)p.dq + (hrow + hl) * D + 128 * kh + 4 * g;
