@@ -186,10 +186,15 @@ __device__ __forceinline__ int g2_qswz(int r) { return (r >> 1) & 7; }
 __shared__ __attribute__((aligned(1024))) char g2_stage0[G2_STAGE];
 __shared__ __attribute__((aligned(1024))) char g2_stage1[G2_STAGE];
 
+// BWD: the backward's elementwise part instead of the gate: out = dout * s and
+// dg = dout * o * s * (1 - s), s = sigmoid(G).
+template <bool BWD>
 __global__ __launch_bounds__(512, 1) void gate_bf16_big_kernel(const uint16_t* __restrict__ ql,
                                                                const uint16_t* __restrict__ w,
                                                                const uint16_t* o, uint16_t* out,
-                                                               int M, int d_lat, int N) {
+                                                               int M, int d_lat, int N,
+                                                               const uint16_t* dout,
+                                                               uint16_t* dg) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
@@ -302,6 +307,66 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_big_kernel(const uint16_t* _
     m = m0 + 64 * (2 * hl + (blk >> 1)) + rr;
     n = n0 + 128 * (blk & 1) + (c & 15) * 8;
   };
+  if constexpr (BWD) {
+    // o and dout of one half at a time (the accumulators are still live in the first half);
+    // the second half's loads go out once the first half's values are consumed
+    uint4 ov[8], dv[8];
+    auto load_half = [&](int hl) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        int blk, rr, m, n;
+        chunk_mn(hl, u, blk, rr, m, n);
+        const size_t off = (size_t)min(m, M - 1) * N + min(n, N - 8);
+        ov[u] = load16_nt(o + off);
+        dv[u] = load16_nt(dout + off);
+      }
+    };
+    load_half(0);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if ((wave >> 2) == half) {
+        float* fw = fblk(wave & 3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            f32x4_t f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) f[r] = sigmoidf_fast(acc[i][j][r]);
+            *(f32x4_t*)(fw + (16 * j + l16) * 128 + 4 * ((4 * i + g) ^ l16)) = f;
+          }
+      }
+      lds_barrier();
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        int blk, rr, m, n;
+        chunk_mn(half, u, blk, rr, m, n);
+        const int c0 = (tid & 15) * 2;
+        const float* fw = fblk(blk) + rr * 128;
+        const f32x4_t f0 = *(const f32x4_t*)(fw + 4 * (c0 ^ (rr & 15)));
+        const f32x4_t f1 = *(const f32x4_t*)(fw + 4 * ((c0 + 1) ^ (rr & 15)));
+        const float sg[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
+        const uint32_t xo[4] = {ov[u].x, ov[u].y, ov[u].z, ov[u].w};
+        const uint32_t xd[4] = {dv[u].x, dv[u].y, dv[u].z, dv[u].w};
+        uint32_t ro[4], rg[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float o0 = __uint_as_float(xo[c] << 16), o1 = __uint_as_float(xo[c] & 0xFFFF0000u);
+          const float d0 = __uint_as_float(xd[c] << 16), d1 = __uint_as_float(xd[c] & 0xFFFF0000u);
+          const float s0 = sg[2 * c], s1 = sg[2 * c + 1];
+          ro[c] = pack_bf16x2(d0 * s0, d1 * s1);
+          rg[c] = pack_bf16x2(d0 * o0 * s0 * (1.f - s0), d1 * o1 * s1 * (1.f - s1));
+        }
+        if (m < M && n < N) {
+          store16_nt(out + (size_t)m * N + n, make_uint4(ro[0], ro[1], ro[2], ro[3]));
+          store16_nt(dg + (size_t)m * N + n, make_uint4(rg[0], rg[1], rg[2], rg[3]));
+        }
+      }
+      if (half == 0) load_half(1);
+      lds_barrier();
+    }
+    return;
+  }
   // the o loads of both halves are issued before any gate factor is staged, so the second
   // half's loads are in flight while the first half is processed
   uint4 ov[2][8];
@@ -542,9 +607,9 @@ hipError_t launch_gate(const void* q_lat, const void* w, const void* o, void* ou
   if (M == 0) return hipSuccess;
   if (dt == DT_BF16 && M >= G2_BM && N >= G2_BN) {
     const int grid = ((N + G2_BN - 1) / G2_BN) * ((M + G2_BM - 1) / G2_BM);
-    hipLaunchKernelGGL(gate_bf16_big_kernel, dim3(grid), dim3(512), 0, stream,
+    hipLaunchKernelGGL(gate_bf16_big_kernel<false>, dim3(grid), dim3(512), 0, stream,
                        (const uint16_t*)q_lat, (const uint16_t*)w, (const uint16_t*)o,
-                       (uint16_t*)out, M, d_lat, N);
+                       (uint16_t*)out, M, d_lat, N, nullptr, nullptr);
   } else if (dt == DT_BF16 && M <= 64 && d_lat == 16 * SK_K) {
     hipLaunchKernelGGL(gate_bf16_skinny_kernel<16>, dim3((N + SK_N - 1) / SK_N), dim3(256), 0,
                        stream, (const uint16_t*)q_lat, (const uint16_t*)w, (const uint16_t*)o,
@@ -569,7 +634,12 @@ hipError_t launch_gate_bwd_elem(const void* q_lat, const void* w, const void* o,
                                 const void* dout, void* d_o, void* dg, int M, int d_lat, int N,
                                 int dt, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  if (dt == DT_BF16) {
+  if (dt == DT_BF16 && M >= G2_BM && N >= G2_BN) {
+    const int grid = ((N + G2_BN - 1) / G2_BN) * ((M + G2_BM - 1) / G2_BM);
+    hipLaunchKernelGGL(gate_bf16_big_kernel<true>, dim3(grid), dim3(512), 0, stream,
+                       (const uint16_t*)q_lat, (const uint16_t*)w, (const uint16_t*)o,
+                       (uint16_t*)d_o, M, d_lat, N, (const uint16_t*)dout, (uint16_t*)dg);
+  } else if (dt == DT_BF16) {
     const int grid = ((N + GT_N - 1) / GT_N) * ((M + GT_M - 1) / GT_M);
     hipLaunchKernelGGL(gate_bf16_kernel<true>, dim3(grid), dim3(256), 0, stream,
                        (const uint16_t*)q_lat, (const uint16_t*)w, (const uint16_t*)o,
