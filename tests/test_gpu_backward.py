@@ -113,18 +113,18 @@ def test_hca_backward_deterministic(torch):
         assert np.array_equal(a, b)
 
 
-def _sparse_case(torch, seed, B, Tq, S, k, distinct_v, idx=None, ws_frac=None):
+def _sparse_case(torch, seed, B, Tq, S, k, distinct_v, idx=None, ws_frac=None, H=64):
     """GPU forward (ungated, with its lse) and backward of sparse attention on seeded bf16
     inputs; ws_frac < 1 hands the backward that fraction of its default workspace, so that it
     takes the rows in several chunks."""
-    x = synth.dsa_sparse(seed, B=B, Tq=Tq, S=S, H=64, distinct_v=distinct_v, gated=False)
+    x = synth.dsa_sparse(seed, B=B, Tq=Tq, S=S, H=H, distinct_v=distinct_v, gated=False)
     if idx is None:
         idx = synth.random_topk(seed, B, Tq, S, k, [S - Tq] * B)
-    dout = synth.normal(seed + 7, (B, Tq, 64, 256), 1.0, True)
+    dout = synth.normal(seed + 7, (B, Tq, H, 256), 1.0, True)
     q, kl = to_dev(x["q"]), to_dev(x["kv_lat"])
     vl = to_dev(x["v_lat"]) if distinct_v else None
     ix = to_dev(idx)
-    lse = torch.empty((B, Tq, 64), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device="cuda")
     out = lgsa.sparse_attn_fwd(q, kl, ix, v_lat=vl, lse=lse)
     do = to_dev(dout)
     ws = None
@@ -176,6 +176,21 @@ def test_sparse_backward_repeats_skips_and_empty_rows(torch):
     bf16_ok(dk, r_k, "dk")
     assert np.all(dq[0, 3] == 0) and np.all(lse[0, 3] == -np.inf)
     assert np.all(dk[0, 60:] == 0)
+
+
+@pytest.mark.parametrize("distinct_v", [False, True])
+def test_sparse_backward_two_head_groups(torch, distinct_v):
+    """128 heads: two workgroups per row, each writing its own contribution of every entry
+    (summed by the reduction); with a small workspace so that chunks are carried too."""
+    B, Tq, S, k = 1, 24, 180, 72
+    x, idx, dout, lse, (dq, dk, dv) = _sparse_case(torch, 340, B, Tq, S, k, distinct_v,
+                                                   ws_frac=0.7, H=128)
+    r_q, r_k, r_v = backward.sparse_attn_bwd(x["q"], x["kv_lat"], idx, dout,
+                                             v_lat=x.get("v_lat"))
+    bf16_ok(dq, r_q, "dq")
+    bf16_ok(dk, r_k, "dk")
+    if distinct_v:
+        bf16_ok(dv, r_v, "dv")
 
 
 def test_sparse_backward_deterministic(torch):
