@@ -296,8 +296,11 @@ typedef struct {
                             take fewer rows at a time (same result up to summation order) */
   size_t workspace_bytes;
 } lgsa_sparse_bwd_args;
-/* Supported: LGSA_BF16, d_qk == d_v == 256, H % 64 == 0, row strides % 8 == 0, every tensor
- * 16-byte aligned.  Errors as for sparse_attn_fwd; LGSA_EWORKSPACE when the workspace is short. */
+/* Supported: LGSA_BF16, d_qk == d_v == 256, H % 64 == 0, row strides % 8 == 0, S <= 2^26,
+ * k * H / 64 <= 2^24; q, the latent rows, out, dout, dq, dk, dv 16-byte aligned; lse, idx 4-byte
+ * aligned.  dq, dk, dv are overwritten (dk and dv entirely).  Errors as for sparse_attn_fwd
+ * (LGSA_EINVAL, LGSA_EUNSUPPORTED); LGSA_EWORKSPACE when the workspace is below the size for one
+ * row.  Runs on the given stream; the workspace must stay untouched until the call completes. */
 lgsa_status sparse_attn_bwd(const lgsa_sparse_bwd_args* a, void* stream);
 lgsa_status sparse_attn_bwd_workspace(const lgsa_sparse_bwd_args* a, size_t* bytes);
 
