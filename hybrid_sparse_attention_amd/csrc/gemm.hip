@@ -9,6 +9,8 @@
 // 16-byte chunks per thread, a k-major one as one 8 x 8 block per thread transposed in
 // registers.  The next K step is loaded into registers while the current one is used.
 // float32: 64 x 64 tiles of plain FMA (the small fp32 configurations).
+// Large bfloat16 products (M, N multiples of 256, K of 64) take a 256 x 256 LDS-DMA kernel
+// instead (below).
 #include "common.h"
 #include "kernels.h"
 
@@ -52,6 +54,140 @@ __device__ __forceinline__ void gemm_store(uint16_t* s, int t, const uint4 (&st)
     for (int j = 0; j < 8; ++j) {
       const int c = t + 128 * j;
       *(uint4*)(&s[(c >> 3) * GM_LD + 8 * (c & 7)]) = st[j];
+    }
+  }
+}
+
+// Large bfloat16 products (M, N multiples of 256, K of 64): 256 x 256 tiles, 8 waves of
+// 128 (n) x 64 (m), the transposed product C^T = B^T A^T on v_mfma_f32_16x16x32_bf16 so that a
+// lane's accumulator holds four consecutive columns of one C row.  Both operand tiles reach LDS
+// by LDS DMA (no register staging), two stages deep, as in the forward gate kernel: a k-major
+// operand as 64 k-rows of 256 values, read through the transposing LDS read; a k-contiguous one
+// as 256 rows of 64 k, read as 16-byte fragments.  16-byte chunks are XOR-swizzled against
+// bank conflicts by choosing which chunk each lane fetches.
+constexpr int GB_T = 256, GB_K = 64;
+constexpr int GB_KROW = GB_T * 2;  // bytes per staged k-major row
+constexpr int GB_CROW = GB_K * 2;  // bytes per staged k-contiguous row
+constexpr int GB_OP = 32768;       // bytes of one staged operand tile (either layout)
+
+__device__ __forceinline__ int gb_kswz(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+__device__ __forceinline__ int gb_cswz(int r) { return (r >> 1) & 7; }
+
+// two stages, each [N-side operand][M-side operand]; separate LDS objects named where used
+__shared__ __attribute__((aligned(1024))) char gb_st0[2 * GB_OP];
+__shared__ __attribute__((aligned(1024))) char gb_st1[2 * GB_OP];
+
+// DMA of one operand tile (tile rows r0 .. r0 + 255, contraction k0 .. k0 + 63): 32
+// instructions, 4 per wave
+template <bool KM>
+__device__ __forceinline__ void gb_dma(const uint16_t* x, long long ld, int r0, int k0, char* dst,
+                                       int wave, int lane) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int ins = wave + 8 * u;
+    if (KM) {
+      const int kr = 2 * ins + (lane >> 5);  // k-row of this lane
+      const int chunk = (lane & 31) ^ gb_kswz(kr);
+      lds_dma16(x + (size_t)(k0 + kr) * ld + r0 + 8 * chunk, dst + 2 * ins * GB_KROW);
+    } else {
+      const int r = 8 * ins + (lane >> 3);  // tile row of this lane
+      const int chunk = (lane & 7) ^ gb_cswz(r);
+      lds_dma16(x + (size_t)(r0 + r) * ld + k0 + 8 * chunk, dst + 8 * ins * GB_CROW);
+    }
+  }
+}
+
+// MFMA operand of tile rows 16 blk + l16, contraction 32 ks + 8g .. +7
+template <bool KM>
+__device__ __forceinline__ Frag8 gb_frag(const char* st, int blk, int ks, int lane) {
+  const int l16 = lane & 15, g = lane >> 4;
+  Frag8 f;
+  if (KM) {
+    const int a = l16 >> 2, c4 = l16 & 3;
+    const int kf = gb_kswz(8 * g + a);  // the same for k-rows 32 ks + 8g + 4h + a
+    const char* row = st + (32 * ks + 8 * g + a) * GB_KROW + 16 * ((2 * blk + (c4 >> 1)) ^ kf) +
+                      8 * (c4 & 1);
+    const uint2 lo = lds_read_tr16(row);
+    const uint2 hi = lds_read_tr16(row + 4 * GB_KROW);
+    f.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  } else {
+    f.u = *(const uint4*)(st + (16 * blk + l16) * GB_CROW + 16 * ((4 * ks + g) ^ gb_cswz(l16)));
+  }
+  return f;
+}
+
+template <bool AK, bool BK>
+__global__ __launch_bounds__(512, 1) void gemm_big_kernel(const uint16_t* __restrict__ a,
+                                                          long long lda,
+                                                          const uint16_t* __restrict__ b,
+                                                          long long ldb, uint16_t* __restrict__ c,
+                                                          long long ldc, int M, int N, int K) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int wn = wave & 1, wm = wave >> 1;
+  // XCD-aware order (XCD x = id % 8 takes a contiguous run of tiles), then groups of 4 n-tiles
+  // x 8 m-tiles so that the workgroups an XCD runs together share operand tiles in its L2
+  const int n_nt = N / GB_T, n_mt = M / GB_T;
+  const int tiles = n_nt * n_mt;
+  int lin = blockIdx.x;
+  if (tiles % 8 == 0) lin = (blockIdx.x % 8) * (tiles / 8) + blockIdx.x / 8;
+  int nt, mt;
+  if (n_nt % 4 == 0 && n_mt % 8 == 0) {
+    const int grp = lin / 32, in = lin % 32;
+    const int groups_m = n_mt / 8;
+    nt = (grp / groups_m) * 4 + in / 8;
+    mt = (grp % groups_m) * 8 + in % 8;
+  } else {
+    nt = lin / n_mt;
+    mt = lin % n_mt;
+  }
+  const int n0 = nt * GB_T, m0 = mt * GB_T;
+
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto dma = [&](int k0, char* st) {
+    gb_dma<BK>(b, ldb, n0, k0, st, wave, lane);
+    gb_dma<AK>(a, lda, m0, k0, st + GB_OP, wave, lane);
+  };
+  const int nk = K / GB_K;
+  auto step = [&](int kt, const char* cur, char* nxt) {
+    if (kt + 1 < nk) dma((kt + 1) * GB_K, nxt);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      Frag8 bm[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bm[j] = gb_frag<AK>(cur + GB_OP, 4 * wm + j, ks, lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const Frag8 an = gb_frag<BK>(cur, 8 * wn + i, ks, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(an, bm[j], acc[i][j]);
+      }
+    }
+    wait_all();
+    __syncthreads();
+  };
+  dma(0, gb_st0);
+  wait_all();
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, gb_st0, gb_st1);
+    if (kt + 1 < nk) step(kt + 1, gb_st1, gb_st0);
+  }
+  // lane holds C[m0 + 64 wm + 16 j + l16][n0 + 128 wn + 16 i + 4g .. +3]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint16_t* crow = c + (size_t)(m0 + 64 * wm + 16 * j + l16) * ldc + n0 + 128 * wn + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint2 r;
+      r.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+      r.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+      *(uint2*)(crow + 16 * i) = r;
     }
   }
 }
@@ -184,7 +320,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 template <bool AK, bool BK>
 hipError_t gemm_launch(const void* a, long long lda, const void* b, long long ldb, void* c,
                        long long ldc, int M, int N, int K, int dt, hipStream_t stream) {
-  if (dt == DT_BF16) {
+  const bool big = M % GB_T == 0 && N % GB_T == 0 && K % GB_K == 0 && K > 0 &&
+                   (long long)(M / GB_T) * (N / GB_T) >= 64 && lda % 8 == 0 && ldb % 8 == 0 &&
+                   ldc % 4 == 0 && ((uintptr_t)a & 15) == 0 && ((uintptr_t)b & 15) == 0 &&
+                   ((uintptr_t)c & 7) == 0;
+  if (dt == DT_BF16 && big) {
+    const int grid = (N / GB_T) * (M / GB_T);
+    hipLaunchKernelGGL((gemm_big_kernel<AK, BK>), dim3(grid), dim3(512), 0, stream,
+                       (const uint16_t*)a, lda, (const uint16_t*)b, ldb, (uint16_t*)c, ldc, M, N,
+                       K);
+  } else if (dt == DT_BF16) {
     const int grid = ((N + GM_T - 1) / GM_T) * ((M + GM_T - 1) / GM_T);
     hipLaunchKernelGGL((gemm_bf16_kernel<AK, BK, false>), dim3(grid), dim3(256), 0, stream,
                        (const uint16_t*)a, lda, (const uint16_t*)b, ldb, c, ldc, M, N, K, K);
