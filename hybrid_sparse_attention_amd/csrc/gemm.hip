@@ -116,12 +116,15 @@ __device__ __forceinline__ Frag8 gb_frag(const char* st, int blk, int ks, int la
   return f;
 }
 
-template <bool AK, bool BK>
+// F32: C is fp32 and blockIdx.y selects the contraction range y * kchunk .. (split K; the
+// partials at C + y * M * ldc are summed afterwards).
+template <bool AK, bool BK, bool F32>
 __global__ __launch_bounds__(512, 1) void gemm_big_kernel(const uint16_t* __restrict__ a,
                                                           long long lda,
                                                           const uint16_t* __restrict__ b,
-                                                          long long ldb, uint16_t* __restrict__ c,
-                                                          long long ldc, int M, int N, int K) {
+                                                          long long ldb, void* __restrict__ c,
+                                                          long long ldc, int M, int N, int K,
+                                                          int kchunk) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
@@ -153,9 +156,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(const uint16_t* __rest
     gb_dma<BK>(b, ldb, n0, k0, st, wave, lane);
     gb_dma<AK>(a, lda, m0, k0, st + GB_OP, wave, lane);
   };
-  const int nk = K / GB_K;
+  const int kbeg = F32 ? blockIdx.y * kchunk : 0;
+  const int nk = ((F32 ? min(K, kbeg + kchunk) : K) - kbeg) / GB_K;
   auto step = [&](int kt, const char* cur, char* nxt) {
-    if (kt + 1 < nk) dma((kt + 1) * GB_K, nxt);
+    if (kt + 1 < nk) dma(kbeg + (kt + 1) * GB_K, nxt);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       Frag8 bm[4];
@@ -171,7 +175,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(const uint16_t* __rest
     wait_all();
     __syncthreads();
   };
-  dma(0, gb_st0);
+  if (nk > 0) dma(kbeg, gb_st0);
   wait_all();
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
@@ -181,15 +185,28 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(const uint16_t* __rest
   // lane holds C[m0 + 64 wm + 16 j + l16][n0 + 128 wn + 16 i + 4g .. +3]
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    uint16_t* crow = c + (size_t)(m0 + 64 * wm + 16 * j + l16) * ldc + n0 + 128 * wn + 4 * g;
+    const size_t crow = (size_t)(m0 + 64 * wm + 16 * j + l16) * ldc + n0 + 128 * wn + 4 * g;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint2 r;
-      r.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-      r.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-      *(uint2*)(crow + 16 * i) = r;
+      if constexpr (F32) {
+        float* cp = (float*)c + (size_t)blockIdx.y * M * ldc + crow + 16 * i;
+        *(f32x4_t*)cp = acc[i][j];
+      } else {
+        uint2 r;
+        r.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+        r.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+        *(uint2*)((uint16_t*)c + crow + 16 * i) = r;
+      }
     }
   }
+}
+
+// whether a bfloat16 product suits the 256 x 256 kernel
+bool gemm_big_ok(const void* a, long long lda, const void* b, long long ldb, long long ldc, int M,
+                 int N, int K, long long min_tiles) {
+  return M % GB_T == 0 && N % GB_T == 0 && K % GB_K == 0 && K > 0 &&
+         (long long)(M / GB_T) * (N / GB_T) >= min_tiles && lda % 8 == 0 && ldb % 8 == 0 &&
+         ldc % 4 == 0 && ((uintptr_t)a & 15) == 0 && ((uintptr_t)b & 15) == 0;
 }
 
 // OUT_F32: C is fp32 and blockIdx.y selects a range of `kchunk` contraction indices whose
@@ -320,15 +337,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 template <bool AK, bool BK>
 hipError_t gemm_launch(const void* a, long long lda, const void* b, long long ldb, void* c,
                        long long ldc, int M, int N, int K, int dt, hipStream_t stream) {
-  const bool big = M % GB_T == 0 && N % GB_T == 0 && K % GB_K == 0 && K > 0 &&
-                   (long long)(M / GB_T) * (N / GB_T) >= 64 && lda % 8 == 0 && ldb % 8 == 0 &&
-                   ldc % 4 == 0 && ((uintptr_t)a & 15) == 0 && ((uintptr_t)b & 15) == 0 &&
-                   ((uintptr_t)c & 7) == 0;
-  if (dt == DT_BF16 && big) {
+  if (dt == DT_BF16 && gemm_big_ok(a, lda, b, ldb, ldc, M, N, K, 64) && ((uintptr_t)c & 7) == 0) {
     const int grid = (N / GB_T) * (M / GB_T);
-    hipLaunchKernelGGL((gemm_big_kernel<AK, BK>), dim3(grid), dim3(512), 0, stream,
-                       (const uint16_t*)a, lda, (const uint16_t*)b, ldb, (uint16_t*)c, ldc, M, N,
-                       K);
+    hipLaunchKernelGGL((gemm_big_kernel<AK, BK, false>), dim3(grid), dim3(512), 0, stream,
+                       (const uint16_t*)a, lda, (const uint16_t*)b, ldb, c, ldc, M, N, K, K);
   } else if (dt == DT_BF16) {
     const int grid = ((N + GM_T - 1) / GM_T) * ((M + GM_T - 1) / GM_T);
     hipLaunchKernelGGL((gemm_bf16_kernel<AK, BK, false>), dim3(grid), dim3(256), 0, stream,
@@ -363,7 +375,12 @@ hipError_t launch_gemm_splitk_f32(const void* a, long long lda, bool a_kmajor, c
   const dim3 grid(((N + GM_T - 1) / GM_T) * ((M + GM_T - 1) / GM_T), splits);
   const uint16_t* pa = (const uint16_t*)a;
   const uint16_t* pb = (const uint16_t*)b;
-  if (a_kmajor && b_kmajor)
+  if (gemm_big_ok(a, lda, b, ldb, N, M, N, K, 1) && a_kmajor && b_kmajor) {
+    // the 256 x 256 kernel with the same split (kchunk is a multiple of 64)
+    hipLaunchKernelGGL((gemm_big_kernel<true, true, true>), dim3((N / GB_T) * (M / GB_T), splits),
+                       dim3(512), 0, stream, pa, lda, pb, ldb, (void*)part, (long long)N, M, N, K,
+                       kchunk);
+  } else if (a_kmajor && b_kmajor)
     hipLaunchKernelGGL((gemm_bf16_kernel<true, true, true>), grid, dim3(256), 0, stream, pa, lda,
                        pb, ldb, (void*)part, (long long)N, M, N, K, kchunk);
   else if (a_kmajor)

@@ -796,7 +796,7 @@ BwdWs bwd_layout(const HcaBwdParams& p, size_t* total) {
   BwdWs w;
   const size_t rows = (size_t)p.B * p.T * p.H;
   w.ne_pad = (std::max(p.ne, 1) + 7) / 8 * 8;
-  w.splits = (int)std::max<size_t>(1, std::min<size_t>(64, rows / 4096));
+  w.splits = (int)std::max<size_t>(1, std::min<size_t>(128, rows / 4096));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
