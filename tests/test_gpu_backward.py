@@ -93,7 +93,7 @@ def _hca_case(torch, seed, B, T, H, window, block):
 
 
 @pytest.mark.parametrize("B,T,H,window,block", [(2, 300, 4, 48, 32), (1, 1100, 4, 128, 128),
-                                                (1, 40, 8, 64, 128)])
+                                                (1, 40, 8, 64, 128), (1, 260, 4, 100, 64)])
 def test_hca_backward(torch, B, T, H, window, block):
     """dq, dk, dv against the float64 oracle (which rebuilds everything from q, k, v): the
     window path, the pooled path (an entry's gradient spread over its block) and a sequence
