@@ -17,7 +17,8 @@
 //           (twice only as a duplicate, whose contributions are equal), and the rows of a range
 //           are ranked one after another, so the counts it returns follow the row order.
 //   scan    exclusive prefix sum over the (key, range) counts, key-major: each key's slots are
-//           contiguous and ordered by range.
+//           contiguous and ordered by range (per block of counters, plus the blocks' prefix,
+//           which the readers add).
 //   slot    slot = offset(key, range) + rank.
 //   main    one workgroup (8 waves) per query row and group of 64 heads.  Wave w takes heads
 //           16(w % 4) .. +15 and keys 16(w / 4) .. +15 of each 32-key tile for S^T = K Q^T and
@@ -437,10 +438,23 @@ __device__ __forceinline__ void block_scan16(int32_t* __restrict__ data, long lo
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const long long i0 = base + 16ll * threadIdx.x;
   int v[16];
+  if (i0 + 16 <= n) {  // 64 aligned bytes
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int4 x = *(const int4*)(data + i0 + 4 * c);
+      v[4 * c] = x.x;
+      v[4 * c + 1] = x.y;
+      v[4 * c + 2] = x.z;
+      v[4 * c + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = i0 + e < n ? data[i0 + e] : 0;
+  }
   int sum = 0;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int x = i0 + e < n ? data[i0 + e] : 0;
+    const int x = v[e];
     v[e] = sum;
     sum += x;
   }
@@ -455,9 +469,16 @@ __device__ __forceinline__ void block_scan16(int32_t* __restrict__ data, long lo
   int pre = 0;
   for (int i = 0; i < w; ++i) pre += wsum[i];
   const int ex = pre + x - sum;
+  if (i0 + 16 <= n) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e)
-    if (i0 + e < n) data[i0 + e] = v[e] + ex;
+    for (int c = 0; c < 4; ++c)
+      *(int4*)(data + i0 + 4 * c) = make_int4(v[4 * c] + ex, v[4 * c + 1] + ex, v[4 * c + 2] + ex,
+                                              v[4 * c + 3] + ex);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (i0 + e < n) data[i0 + e] = v[e] + ex;
+  }
   if (threadIdx.x == NT - 1) *total = pre + x;
 }
 
@@ -471,25 +492,22 @@ __global__ __launch_bounds__(1024) void scan_top_kernel(int32_t* __restrict__ bs
   block_scan16<1024>(bsum, nblk, 0, bsum + nblk);
 }
 
-__global__ __launch_bounds__(256) void scan_add_kernel(int32_t* __restrict__ data, long long n,
-                                                       const int32_t* __restrict__ bsum) {
-  const long long i0 = (long long)blockIdx.x * SCAN_BLOCK + 16ll * threadIdx.x;
-  const int add = bsum[blockIdx.x];
-#pragma unroll
-  for (int e = 0; e < 16; ++e)
-    if (i0 + e < n) data[i0 + e] += add;
+// offset of counter x: its exclusive sum within its block plus the blocks before it
+__device__ __forceinline__ int scan_at(const int32_t* off, const int32_t* bsum, size_t x) {
+  return off[x] + bsum[x / SCAN_BLOCK];
 }
 
 __global__ __launch_bounds__(256) void sparse_bwd_slot_kernel(const int32_t* __restrict__ idx,
                                                               long long n, int k, int S, int qr,
                                                               int R, const int32_t* __restrict__ off,
+                                                              const int32_t* __restrict__ bsum,
                                                               int32_t* __restrict__ rank) {
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n;
        i += (long long)gridDim.x * 256) {
     const int rk = rank[i];
     if (rk < 0) continue;
     const int r = (int)(i / k) / qr;
-    rank[i] = off[(size_t)idx[i] * R + r] + rk;
+    rank[i] = scan_at(off, bsum, (size_t)idx[i] * R + r) + rk;
   }
 }
 
@@ -498,15 +516,17 @@ __global__ __launch_bounds__(256) void sparse_bwd_slot_kernel(const int32_t* __r
 template <bool ALIAS>
 __global__ __launch_bounds__(256) void sparse_bwd_reduce_kernel(
     const uint16_t* __restrict__ buf, long long row_base, const int32_t* __restrict__ off,
-    const int32_t* __restrict__ total, int R, int S, int n_hg, float* __restrict__ acc, int mode,
+    const int32_t* __restrict__ bsum, const int32_t* __restrict__ total, int R, int S, int n_hg,
+    float* __restrict__ acc, int mode,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
   constexpr int RW = ALIAS ? D : 2 * D;
   constexpr int PER = RW / 64;  // columns per lane
   const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (s >= S) return;
   const int lane = threadIdx.x & 63;
-  const long long a = row_base + (long long)off[(size_t)s * R] * n_hg;
-  const long long e = row_base + (long long)(s + 1 < S ? off[(size_t)(s + 1) * R] : *total) * n_hg;
+  const long long a = row_base + (long long)scan_at(off, bsum, (size_t)s * R) * n_hg;
+  const long long e =
+      row_base + (long long)(s + 1 < S ? scan_at(off, bsum, (size_t)(s + 1) * R) : *total) * n_hg;
   float sum[PER];
 #pragma unroll
   for (int c = 0; c < PER; ++c) sum[c] = 0.f;
@@ -659,11 +679,9 @@ hipError_t launch_sparse_bwd(const SparseBwdParams& p, hipStream_t stream) {
       hipLaunchKernelGGL(scan_local_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, cnt,
                          counters, bsum);
       hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(1024), 0, stream, bsum, (int)nblk);
-      hipLaunchKernelGGL(scan_add_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, cnt,
-                         counters, bsum);
       hipLaunchKernelGGL(sparse_bwd_slot_kernel,
                          dim3((unsigned)std::min(8192ll, (n_pairs + 255) / 256)), dim3(256), 0,
-                         stream, idx, n_pairs, p.k, p.S, pl.qr, R, cnt, rank);
+                         stream, idx, n_pairs, p.k, p.S, pl.qr, R, cnt, bsum, rank);
       const unsigned grid = (unsigned)n_rows * pl.n_hg;
       if (pl.alias)
         hipLaunchKernelGGL(sparse_bwd_kernel<true>, dim3(grid), dim3(64 * NW), 0, stream, p,
@@ -675,10 +693,12 @@ hipError_t launch_sparse_bwd(const SparseBwdParams& p, hipStream_t stream) {
       const dim3 rgrid((unsigned)((p.S + 3) / 4));
       if (pl.alias)
         hipLaunchKernelGGL(sparse_bwd_reduce_kernel<true>, rgrid, dim3(256), 0, stream, buf,
-                           (long long)grid, cnt, bsum + nblk, R, p.S, pl.n_hg, acc, mode, dk, dv);
+                           (long long)grid, cnt, bsum, bsum + nblk, R, p.S, pl.n_hg, acc, mode, dk,
+                           dv);
       else
         hipLaunchKernelGGL(sparse_bwd_reduce_kernel<false>, rgrid, dim3(256), 0, stream, buf,
-                           (long long)grid, cnt, bsum + nblk, R, p.S, pl.n_hg, acc, mode, dk, dv);
+                           (long long)grid, cnt, bsum, bsum + nblk, R, p.S, pl.n_hg, acc, mode, dk,
+                           dv);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
