@@ -16,9 +16,9 @@
 //           the next count of (key, range) with an integer atomic.  A row lists a key once
 //           (twice only as a duplicate, whose contributions are equal), and the rows of a range
 //           are ranked one after another, so the counts it returns follow the row order.
-//   scan    exclusive prefix sum over the (key, range) counts, key-major: each key's slots are
-//           contiguous and ordered by range (per block of counters, plus the blocks' prefix,
-//           which the readers add).
+//   scan    exclusive prefix sum over the (key, range) counts in key-major order (stored
+//           range-major, as counted): each key's slots are contiguous and ordered by range (per
+//           block of counters, plus the blocks' prefix, which the readers add).
 //   slot    slot = offset(key, range) + rank.
 //   main    one workgroup (8 waves) per query row and group of 64 heads.  Wave w takes heads
 //           16(w % 4) .. +15 and keys 16(w / 4) .. +15 of each 32-key tile for S^T = K Q^T and
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(256) void sparse_bwd_rank_kernel(const int32_t* __r
     for (int j = threadIdx.x; j < k; j += 256) {
       const int s = ir[j];
       int rk = -1;
-      if (s >= 0 && s < S) rk = atomicAdd(&cnt[(size_t)s * R + r], 1);
+      if (s >= 0 && s < S) rk = atomicAdd(&cnt[(size_t)r * S + s], 1);
       rr[j] = rk;  // uses the returned count: the atomic has been performed before the barrier
     }
     __syncthreads();
@@ -427,10 +427,10 @@ __global__ __launch_bounds__(1024) void sparse_bwd_rank_lds_kernel(
     __syncthreads();
   }
   for (int s = threadIdx.x; s < S; s += 1024)
-    cnt[(size_t)s * R + r] = (int32_t)((c16[s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
+    cnt[(size_t)r * S + s] = (int32_t)((c16[s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
 }
 
-// exclusive scan of one block of 4096 counters in place; the block's total to bsum
+// exclusive scan of 16 * NT values in place (global or LDS); their total to *total
 template <int NT>
 __device__ __forceinline__ void block_scan16(int32_t* __restrict__ data, long long n,
                                              long long base, int32_t* total) {
@@ -482,9 +482,24 @@ __device__ __forceinline__ void block_scan16(int32_t* __restrict__ data, long lo
   if (threadIdx.x == NT - 1) *total = pre + x;
 }
 
-__global__ __launch_bounds__(256) void scan_local_kernel(int32_t* __restrict__ data, long long n,
-                                                         int32_t* __restrict__ bsum) {
-  block_scan16<256>(data, n, (long long)blockIdx.x * SCAN_BLOCK, bsum + blockIdx.x);
+// Counts are stored range-major (data[r * S + s], as counted); the scan runs key-major.  A
+// block takes kb whole keys (kb * R <= 4096 counters): it reads them along the keys (coalesced
+// runs), scans them key-major in LDS and writes them back; the blocks' totals go to bsum.
+__global__ __launch_bounds__(256) void scan_keys_kernel(int32_t* __restrict__ data, int S, int R,
+                                                        int kb, int32_t* __restrict__ bsum) {
+  __shared__ __attribute__((aligned(16))) int32_t sv[SCAN_BLOCK];
+  const int s0 = blockIdx.x * kb, ns = min(kb, S - s0), n = ns * R;
+  for (int j = threadIdx.x; j < n; j += 256) {
+    const int sl = j % ns, r = j / ns;
+    sv[sl * R + r] = data[(size_t)r * S + s0 + sl];
+  }
+  __syncthreads();
+  block_scan16<256>(sv, n, 0, bsum + blockIdx.x);
+  __syncthreads();
+  for (int j = threadIdx.x; j < n; j += 256) {
+    const int sl = j % ns, r = j / ns;
+    data[(size_t)r * S + s0 + sl] = sv[sl * R + r];
+  }
 }
 
 // one workgroup: the block totals (at most 16384) scanned in place, the grand total after them
@@ -492,14 +507,16 @@ __global__ __launch_bounds__(1024) void scan_top_kernel(int32_t* __restrict__ bs
   block_scan16<1024>(bsum, nblk, 0, bsum + nblk);
 }
 
-// offset of counter x: its exclusive sum within its block plus the blocks before it
-__device__ __forceinline__ int scan_at(const int32_t* off, const int32_t* bsum, size_t x) {
-  return off[x] + bsum[x / SCAN_BLOCK];
+// offset of the counter of (key s, range r): its exclusive sum within its block of kb keys
+// plus the blocks before it
+__device__ __forceinline__ int scan_at(const int32_t* off, const int32_t* bsum, int S, int kb,
+                                       int s, int r) {
+  return off[(size_t)r * S + s] + bsum[s / kb];
 }
 
 __global__ __launch_bounds__(256) void sparse_bwd_slot_kernel(const int32_t* __restrict__ idx,
                                                               long long n, int k, int S, int qr,
-                                                              int R, const int32_t* __restrict__ off,
+                                                              int kb, const int32_t* __restrict__ off,
                                                               const int32_t* __restrict__ bsum,
                                                               int32_t* __restrict__ rank) {
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n;
@@ -507,7 +524,7 @@ __global__ __launch_bounds__(256) void sparse_bwd_slot_kernel(const int32_t* __r
     const int rk = rank[i];
     if (rk < 0) continue;
     const int r = (int)(i / k) / qr;
-    rank[i] = scan_at(off, bsum, (size_t)idx[i] * R + r) + rk;
+    rank[i] = scan_at(off, bsum, S, kb, idx[i], r) + rk;
   }
 }
 
@@ -516,7 +533,7 @@ __global__ __launch_bounds__(256) void sparse_bwd_slot_kernel(const int32_t* __r
 template <bool ALIAS>
 __global__ __launch_bounds__(256) void sparse_bwd_reduce_kernel(
     const uint16_t* __restrict__ buf, long long row_base, const int32_t* __restrict__ off,
-    const int32_t* __restrict__ bsum, const int32_t* __restrict__ total, int R, int S, int n_hg,
+    const int32_t* __restrict__ bsum, const int32_t* __restrict__ total, int kb, int S, int n_hg,
     float* __restrict__ acc, int mode,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
   constexpr int RW = ALIAS ? D : 2 * D;
@@ -524,9 +541,9 @@ __global__ __launch_bounds__(256) void sparse_bwd_reduce_kernel(
   const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (s >= S) return;
   const int lane = threadIdx.x & 63;
-  const long long a = row_base + (long long)scan_at(off, bsum, (size_t)s * R) * n_hg;
+  const long long a = row_base + (long long)scan_at(off, bsum, S, kb, s, 0) * n_hg;
   const long long e =
-      row_base + (long long)(s + 1 < S ? scan_at(off, bsum, (size_t)(s + 1) * R) : *total) * n_hg;
+      row_base + (long long)(s + 1 < S ? scan_at(off, bsum, S, kb, s + 1, 0) : *total) * n_hg;
   float sum[PER];
 #pragma unroll
   for (int c = 0; c < PER; ++c) sum[c] = 0.f;
@@ -591,17 +608,24 @@ size_t sbwd_layout(const SparseBwdParams& p, long long qc, SbwdPlan& pl) {
   pl.alias = p.dv == nullptr;
   pl.rw = pl.alias ? D : 2 * D;
   pl.n_hg = p.H / 64;
-  long long rmax = std::max(1ll, std::min((long long)MAX_RANGES, MAX_COUNTERS / p.S));
+  // a scan block holds SCAN_BLOCK / R whole keys, and the top level at most 16384 blocks
+  const long long kmin = (p.S + 16383) / 16384;
+  const long long rcap = std::max(1ll, SCAN_BLOCK / kmin);
+  long long rmax =
+      std::max(1ll, std::min(std::min((long long)MAX_RANGES, MAX_COUNTERS / p.S), rcap));
   rmax = std::min(rmax, qc);
   pl.qr = (int)((qc + rmax - 1) / rmax);
   // ranges short enough for the 16-bit LDS counters when the keys fit (a few more ranges)
-  if (p.S <= RANK_LDS_KEYS && (long long)pl.qr * p.k >= 65536 && p.k < 65536)
-    pl.qr = std::max(1, 65535 / p.k);
+  if (p.S <= RANK_LDS_KEYS && (long long)pl.qr * p.k >= 65536 && p.k < 65536) {
+    const int q2 = std::max(1, 65535 / p.k);
+    if ((qc + q2 - 1) / q2 <= rcap) pl.qr = q2;
+  }
   pl.rmax = (int)((qc + pl.qr - 1) / pl.qr);
   pl.qc = (int)qc;
   pl.chunks = (int)((p.Tq + qc - 1) / qc);
   const long long counters = (long long)p.S * pl.rmax;
-  const long long nblk = (counters + SCAN_BLOCK - 1) / SCAN_BLOCK;
+  const long long nblk = (p.S + std::max(1ll, SCAN_BLOCK / pl.rmax) - 1) /
+                         std::max(1ll, SCAN_BLOCK / pl.rmax);
   size_t o = 0;
   pl.o_cnt = o;
   o = align256(o + (size_t)counters * 4);
@@ -663,7 +687,8 @@ hipError_t launch_sparse_bwd(const SparseBwdParams& p, hipStream_t stream) {
       const long long row0 = (long long)b * p.Tq + t0;
       const int R = (n_rows + pl.qr - 1) / pl.qr;
       const long long counters = (long long)p.S * R;
-      const long long nblk = (counters + SCAN_BLOCK - 1) / SCAN_BLOCK;
+      const int kb = (int)std::max(1ll, SCAN_BLOCK / R);  // keys per scan block
+      const long long nblk = (p.S + kb - 1) / kb;
       const int32_t* idx = p.idx + (size_t)row0 * p.k;
       const long long n_pairs = (long long)n_rows * p.k;
       if (p.S <= RANK_LDS_KEYS && (long long)pl.qr * p.k < 65536) {
@@ -676,12 +701,12 @@ hipError_t launch_sparse_bwd(const SparseBwdParams& p, hipStream_t stream) {
         hipLaunchKernelGGL(sparse_bwd_rank_kernel, dim3(R), dim3(256), 0, stream, idx, p.k, p.S,
                            n_rows, pl.qr, R, cnt, rank);
       }
-      hipLaunchKernelGGL(scan_local_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, cnt,
-                         counters, bsum);
+      hipLaunchKernelGGL(scan_keys_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, cnt, p.S,
+                         R, kb, bsum);
       hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(1024), 0, stream, bsum, (int)nblk);
       hipLaunchKernelGGL(sparse_bwd_slot_kernel,
                          dim3((unsigned)std::min(8192ll, (n_pairs + 255) / 256)), dim3(256), 0,
-                         stream, idx, n_pairs, p.k, p.S, pl.qr, R, cnt, bsum, rank);
+                         stream, idx, n_pairs, p.k, p.S, pl.qr, kb, cnt, bsum, rank);
       const unsigned grid = (unsigned)n_rows * pl.n_hg;
       if (pl.alias)
         hipLaunchKernelGGL(sparse_bwd_kernel<true>, dim3(grid), dim3(64 * NW), 0, stream, p,
@@ -693,11 +718,11 @@ hipError_t launch_sparse_bwd(const SparseBwdParams& p, hipStream_t stream) {
       const dim3 rgrid((unsigned)((p.S + 3) / 4));
       if (pl.alias)
         hipLaunchKernelGGL(sparse_bwd_reduce_kernel<true>, rgrid, dim3(256), 0, stream, buf,
-                           (long long)grid, cnt, bsum, bsum + nblk, R, p.S, pl.n_hg, acc, mode, dk,
+                           (long long)grid, cnt, bsum, bsum + nblk, kb, p.S, pl.n_hg, acc, mode, dk,
                            dv);
       else
         hipLaunchKernelGGL(sparse_bwd_reduce_kernel<false>, rgrid, dim3(256), 0, stream, buf,
-                           (long long)grid, cnt, bsum, bsum + nblk, R, p.S, pl.n_hg, acc, mode, dk,
+                           (long long)grid, cnt, bsum, bsum + nblk, kb, p.S, pl.n_hg, acc, mode, dk,
                            dv);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
