@@ -193,6 +193,27 @@ def test_sparse_backward_two_head_groups(torch, distinct_v):
         bf16_ok(dv, r_v, "dv")
 
 
+def test_sparse_lse_and_backward_split_rows(torch):
+    """Few rows with long lists: the forward splits each list over workgroups and writes the
+    log-sum-exp from its combine kernel; the backward then uses it (two sequences at different
+    positions, one row with a short list)."""
+    B, S, k = 2, 5000, 2048
+    x = synth.dsa_sparse(350, B=B, Tq=2, S=S, H=64, gated=False)
+    idx = synth.random_topk(350, B, 2, S, k, [4990, 1500])
+    dout = synth.normal(357, (B, 2, 64, 256), 1.0, True)
+    q, kl, ix = to_dev(x["q"]), to_dev(x["kv_lat"]), to_dev(idx)
+    lse = torch.empty((B, 2, 64), dtype=torch.float32, device="cuda")
+    out = lgsa.sparse_attn_fwd(q, kl, ix, lse=lse)
+    dq, dk, _ = lgsa.sparse_attn_bwd(q, kl, ix, out, lse, to_dev(dout))
+    torch.cuda.synchronize()
+    r_lse = backward.sparse_attn_lse(x["q"], x["kv_lat"], idx)
+    got = from_dev(lse)
+    assert np.allclose(got, r_lse, rtol=0, atol=1e-3), float(np.max(np.abs(got - r_lse)))
+    r_q, r_k, _ = backward.sparse_attn_bwd(x["q"], x["kv_lat"], idx, dout)
+    bf16_ok(from_dev(dq), r_q, "dq")
+    bf16_ok(from_dev(dk), r_k, "dk")
+
+
 def test_sparse_backward_deterministic(torch):
     g1 = _sparse_case(torch, 330, 1, 64, 500, 128, False)[-1]
     g2 = _sparse_case(torch, 330, 1, 64, 500, 128, False)[-1]
