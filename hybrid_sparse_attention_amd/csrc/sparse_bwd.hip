@@ -356,8 +356,10 @@ void sparse_bwd_kernel(SparseBwdParams p, long long row0, const int32_t* __restr
     // past the last tile, stage A works on a stale buffer with no valid key and writes zeros
     // that nobody reads
     tile_ops(k1, v1, valid_n1, pd + ((ti + 1) & 1) * PD, kc, pd + (ti & 1) * PD, slot_cur);
-    // this wave's gathers of tile ti + 2 and its entry loads have landed (issued before the
-    // stores, and vector memory operations complete in order); the stores stay in flight
+    // this wave's gathers of tile ti + 2 and its entry loads have landed: they were issued
+    // before the stores, and on this target vector memory loads and stores leave the counter
+    // in issue order (the compiler's own waits rely on the same: after a load and a later
+    // store, it uses the load's result behind vmcnt(1)); the stores stay in flight
     wait_vm<ALIAS ? 4 : 8>();
     lds_barrier();
     valid_n1 = valid_n2;
