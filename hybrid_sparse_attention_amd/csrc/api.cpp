@@ -80,11 +80,13 @@ lgsa_status check_hca(const lgsa_hca_args* a) {
           "hca_attn_fwd: q, pos0, k_win, v_win and out must be non-NULL");
   REQUIRE(a->win_len >= 1 && a->window >= 1, LGSA_EINVAL,
           "hca_attn_fwd: win_len and window must be >= 1");
-  // the window rows of one query must not alias in the ring: either the ring is at least a
-  // window long, or no position reaches past its end
-  REQUIRE(a->window <= a->win_len || a->max_pos < a->win_len, LGSA_EINVAL,
-          "hca_attn_fwd: window (%d) exceeds the rows held in k_win/v_win (%d)", a->window,
-          a->win_len);
+  // the window rows a call reads must not alias in the ring: either no position reaches past
+  // its end, or it holds the window of the first row plus the call's other Tq - 1 rows
+  // (positions pos0 - window + 1 .. pos0 + Tq - 1 of one sequence)
+  REQUIRE(a->max_pos < a->win_len || (long long)a->win_len >= (long long)a->window + a->Tq - 1,
+          LGSA_EINVAL,
+          "hca_attn_fwd: k_win/v_win hold %d rows, fewer than window + Tq - 1 = %lld, and "
+          "positions reach past them", a->win_len, (long long)a->window + a->Tq - 1);
   REQUIRE(a->block >= 1, LGSA_EINVAL, "hca_attn_fwd: block must be >= 1");
   REQUIRE(a->lse == nullptr || (a->dt == LGSA_BF16 && a->Tq > 1), LGSA_EUNSUPPORTED,
           "hca_attn_fwd: lse is written by the bf16 path with Tq > 1 only");
@@ -425,8 +427,8 @@ lgsa_status latent_gate(const void* q_lat, const void* w_gate, const void* o, vo
   if (dt == LGSA_BF16) {
     REQUIRE(d_lat % 64 == 0 && N % 16 == 0, LGSA_EUNSUPPORTED,
             "latent_gate: bf16 needs d_lat %% 64 == 0 and N %% 16 == 0 (got %d, %d)", d_lat, N);
-    REQUIRE(aligned(q_lat, 16) && aligned(w_gate, 16) && aligned(o, 8) && aligned(out, 8),
-            LGSA_EINVAL, "latent_gate: q_lat and w_gate must be 16-byte aligned, o and out 8");
+    REQUIRE(aligned(q_lat, 16) && aligned(w_gate, 16) && aligned(o, 16) && aligned(out, 16),
+            LGSA_EINVAL, "latent_gate: bf16 tensors must be 16-byte aligned");
   }
   return hip_status(lgsa::launch_gate(q_lat, w_gate, o, out, M, d_lat, N, dt,
                                       (hipStream_t)stream),

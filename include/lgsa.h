@@ -76,8 +76,8 @@ lgsa_status hca_compress(const void* k, const void* v, void* kc, void* vc, int B
  *   q_lat  [M, d_lat]   query latent rows (dt)
  *   w_gate [d_lat, N]   gate projection (dt)
  *   o      [M, N]       attention output (dt);  out [M, N] (dt).  out may equal o.
- * Supported: LGSA_BF16 with d_lat % 64 == 0 and N % 16 == 0 (q_lat, w_gate 16-byte aligned,
- * o, out 8-byte aligned); LGSA_F32 with any sizes.  M == 0 enqueues nothing.
+ * Supported: LGSA_BF16 with d_lat % 64 == 0 and N % 16 == 0 (every tensor 16-byte
+ * aligned); LGSA_F32 with any sizes.  M == 0 enqueues nothing.
  * ------------------------------------------------------------------------------------- */
 lgsa_status latent_gate(const void* q_lat, const void* w_gate, const void* o, void* out, int M,
                         int d_lat, int N, int dt, void* stream);
@@ -141,8 +141,11 @@ typedef struct {
                           (-inf for a row with no visible key), for hca_attn_bwd; bf16 with
                           Tq > 1 only */
 } lgsa_hca_args;
-/* Validation: every size >= 1 (n_cap >= 0); window <= win_len unless max_pos < win_len (then
- * no window row wraps around the ring); max_pos >= Tq - 1; kc / vc non-NULL when n_cap > 0.
+/* Validation: every size >= 1 (n_cap >= 0); unless max_pos < win_len (no window row wraps
+ * around the ring), win_len >= window + Tq - 1: a call of Tq rows reads positions
+ * pos0 - window + 1 .. pos0 + Tq - 1 of a sequence, which must sit in distinct ring rows (a
+ * decode call, Tq == 1, needs win_len >= window); max_pos >= Tq - 1; kc / vc non-NULL when
+ * n_cap > 0.
  * Entries e >= n_cap are absent: a query sees min(n_cap, (t + 1) / block) entries.
  * Supported: LGSA_BF16 with d == 512 and d_lat % 64 == 0; LGSA_F32 with d <= 512, d % 4 == 0;
  * every tensor 16-byte aligned.

@@ -80,15 +80,16 @@ void attend(const void* q, int dt_q, long long q_off, long long dqk, long long d
 // Low-rank output gate of [blog 2.1]: the attention output of query row `row` is multiplied,
 // channel by channel, by sigma(q_lat[row] . W[:, n]) where n runs over the H*dv output
 // channels (head-major).  q_lat has d_lat entries per row; W is [d_lat, H*dv] row-major.
+// Each logit g[n] is summed over i in ascending order; the i loop is the outer one so that W
+// is read row by row (every g[n] sees the same additions in the same order either way).
 void apply_gate(const void* q_lat, const void* w, int dt_g, long long d_lat, long long n_out,
                 long long row, double* o) {
-  std::vector<double> ql(d_lat);
-  for (long long i = 0; i < d_lat; ++i) ql[i] = widen(q_lat, dt_g, row * d_lat + i);
-  for (long long n = 0; n < n_out; ++n) {
-    double g = 0.0;
-    for (long long i = 0; i < d_lat; ++i) g += ql[i] * widen(w, dt_g, i * n_out + n);
-    o[n] *= logistic(g);
+  std::vector<double> g(n_out, 0.0);
+  for (long long i = 0; i < d_lat; ++i) {
+    const double qi = widen(q_lat, dt_g, row * d_lat + i);
+    for (long long n = 0; n < n_out; ++n) g[n] += qi * widen(w, dt_g, i * n_out + n);
   }
+  for (long long n = 0; n < n_out; ++n) o[n] *= logistic(g[n]);
 }
 
 }  // namespace
@@ -195,13 +196,12 @@ int orc_latent_gate(const void* q_lat, int dt_l, const void* w, int dt_w, const 
 #pragma omp parallel for schedule(dynamic, 1)
   for (long long r = 0; r < n_rows; ++r) {
     const long long m = rows[r];
-    std::vector<double> ql(d_lat);
-    for (long long i = 0; i < d_lat; ++i) ql[i] = widen(q_lat, dt_l, m * d_lat + i);
-    for (long long n = 0; n < N; ++n) {
-      double g = 0.0;
-      for (long long i = 0; i < d_lat; ++i) g += ql[i] * widen(w, dt_w, i * N + n);
-      out[r * N + n] = widen(o, dt_o, m * N + n) * logistic(g);
+    std::vector<double> g(N, 0.0);  // g[n] summed over i in ascending order, W read by rows
+    for (long long i = 0; i < d_lat; ++i) {
+      const double qi = widen(q_lat, dt_l, m * d_lat + i);
+      for (long long n = 0; n < N; ++n) g[n] += qi * widen(w, dt_w, i * N + n);
     }
+    for (long long n = 0; n < N; ++n) out[r * N + n] = widen(o, dt_o, m * N + n) * logistic(g[n]);
   }
   return 0;
 }

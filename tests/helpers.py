@@ -48,21 +48,65 @@ def f32_ok(got, ref, what=""):
     return err, tol
 
 
-def check_topk_row(gpu_row, orc_row, t, k, scores, kth):
+def check_topk_row(gpu_row, orc_row, t, k, scores, kth, n_vis=None):
     """One query row: structure of the GPU list (ascending, distinct, causal, -1 padded) and
     equality with the oracle's set up to the tie band.  `scores` are the oracle's float64
-    scores of positions 0..t.  Returns True when the sets are identical."""
-    n = min(k, t + 1)
+    scores of positions 0..t; `n_vis` the number of visible keys (t + 1 by default).
+
+    The pass criterion is the band 1e-5 * max(1, |s_k|) around the k-th score s_k.  The
+    literal absolute band 1e-5 is also counted: the returned TopkRow says how many of the
+    differing positions lie outside it (0 whenever |s_k| <= 1, where the two bands agree)."""
+    n_vis = t + 1 if n_vis is None else n_vis
+    n = min(k, n_vis)
     g = [int(x) for x in gpu_row]
     assert all(x == -1 for x in g[n:]), "padding"
     sel = g[:n]
-    assert all(0 <= x <= t for x in sel), "causal range"
+    assert all(0 <= x < n_vis for x in sel), "causal range"
     assert all(sel[i] < sel[i + 1] for i in range(n - 1)), "ascending and distinct"
     o = set(int(x) for x in orc_row[:n])
-    if set(sel) == o:
-        return True
+    diff = set(sel) ^ o
     band = 1e-5 * max(1.0, abs(kth))
-    for s in set(sel) ^ o:
+    outside_abs = 0
+    for s in diff:
         assert abs(scores[s] - kth) <= band, \
             "position %d (score %.9g) outside the tie band of s_k=%.9g" % (s, scores[s], kth)
-    return False
+        outside_abs += abs(scores[s] - kth) > 1e-5
+    return TopkRow(not diff, len(diff), outside_abs)
+
+
+class TopkRow:
+    """Outcome of check_topk_row: identical sets, differing positions, and how many of those
+    lie outside the absolute 1e-5 band (all lie inside the relative band, or the check fails)."""
+
+    def __init__(self, same, n_diff, outside_abs):
+        self.same, self.n_diff, self.outside_abs = same, n_diff, outside_abs
+
+    def __bool__(self):
+        return self.same
+
+    def __int__(self):
+        return int(self.same)
+
+    def __radd__(self, other):
+        return other + int(self.same)
+
+
+def declared_rows(T, seed, n_random=2048, edge=256, block=128):
+    """The declared sample of query rows of a full-size prefill check: the first and last
+    `edge` rows, both rows on each side of every block boundary (t = block*b + block - 1 and
+    block*b + block, where entry b becomes visible), and `n_random` seeded uniform rows."""
+    rows = set(range(min(edge, T))) | set(range(max(0, T - edge), T))
+    for b in range(T // block):
+        rows.update((block * b + block - 1, block * b + block))
+    rng = np.random.default_rng(seed)
+    rows.update(int(x) for x in rng.integers(0, T, n_random))
+    return np.array(sorted(r for r in rows if 0 <= r < T), dtype=np.int64)
+
+
+def rows_of(t, rows):
+    """Rows `rows` of the first sequence of a [1, T, ...] device tensor, as float64 numpy
+    (gathered on the device, so only the sampled rows cross to the host)."""
+    import torch
+
+    idx = torch.from_numpy(np.asarray(rows, dtype=np.int64)).to(t.device)
+    return from_dev(t[0].index_select(0, idx))

@@ -72,6 +72,11 @@ def test_gate_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, 10, 100, 64, 1, None) == lgsa.LGSA_EUNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, 10, 64, 24, 1, None) == lgsa.LGSA_EUNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, 10, 64, 64, 5, None) == lgsa.LGSA_EINVAL
+    # the bf16 kernels read o and write out 16 bytes at a time: an 8-byte aligned view is refused
+    FAKE8 = FAKE + 8
+    assert f(FAKE, FAKE, FAKE8, FAKE, 10, 64, 64, 1, None) == lgsa.LGSA_EINVAL
+    assert "aligned" in lgsa.last_error()
+    assert f(FAKE, FAKE, FAKE, FAKE8, 10, 64, 64, 1, None) == lgsa.LGSA_EINVAL
 
 
 def _hca(**kw):
@@ -93,7 +98,12 @@ def _call(lib, name, a):
 @pytest.mark.parametrize("kw,code,msg", [
     (dict(B=0), lgsa.LGSA_EINVAL, "must be >= 1"),
     (dict(q=None), lgsa.LGSA_EINVAL, "non-NULL"),
-    (dict(window=300, max_pos=300, win_len=256), lgsa.LGSA_EINVAL, "exceeds"),
+    (dict(window=300, max_pos=300, win_len=256), lgsa.LGSA_EINVAL, "window + Tq - 1"),
+    # a multi-row call over a ring of window rows: its rows' windows would alias in the ring
+    (dict(Tq=32, win_len=128, window=128, max_pos=1031, n_cap=8), lgsa.LGSA_EINVAL,
+     "window + Tq - 1"),
+    # a chunk-only window (win_len = Tq) at a later position reaches back before the chunk
+    (dict(Tq=256, win_len=256, max_pos=1279, n_cap=9), lgsa.LGSA_EINVAL, "window + Tq - 1"),
     (dict(block=0), lgsa.LGSA_EINVAL, "block"),
     (dict(kc=None), lgsa.LGSA_EINVAL, "kc and vc"),
     (dict(max_pos=10), lgsa.LGSA_EINVAL, "max_pos"),
