@@ -21,7 +21,7 @@ LGSA_OK, LGSA_EINVAL, LGSA_EUNSUPPORTED, LGSA_EWORKSPACE, LGSA_EHIP = 0, -1, -2,
 LGSA_F32, LGSA_BF16 = 0, 1
 
 EXPORTS = ["lgsa_last_error", "hca_compress", "latent_gate", "hca_attn_fwd",
-           "hca_attn_fwd_workspace", "dsa_index_topk", "dsa_index_topk_workspace",
+           "hca_attn_fwd_workspace", "hca_attn_fwd_static", "dsa_index_topk", "dsa_index_topk_workspace",
            "sparse_attn_fwd", "sparse_attn_fwd_workspace", "hca_cache_append",
            "dsa_cache_append", "vha_mix", "latent_gate_bwd", "latent_gate_bwd_workspace",
            "hca_attn_bwd", "hca_attn_bwd_workspace",
@@ -112,6 +112,7 @@ def load():
             getattr(lib, name).argtypes = [ctypes.POINTER(st), _P]
             getattr(lib, name + "_workspace").argtypes = [ctypes.POINTER(st),
                                                           ctypes.POINTER(_SZ)]
+        lib.hca_attn_fwd_static.argtypes = [ctypes.POINTER(HcaArgs), _P]
         lib.vha_mix.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
         lib.latent_gate_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _SZ,
                                         _P]
@@ -242,6 +243,21 @@ def hca_attn_fwd(q, pos0, k_win, v_win, kc=None, vc=None, *, max_pos, window=128
     a.workspace = None if workspace is None else workspace.data_ptr()
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("hca_attn_fwd", load().hca_attn_fwd(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def hca_attn_fwd_static(q, pos0, k_win, v_win, kc=None, vc=None, *, max_pos, window=128,
+                        block=128, scale=None, q_lat=None, w_gate=None, out=None, stream=None,
+                        lse=None):
+    """hca_attn_fwd without a workspace: the library's per-GPU static scratch serves the
+    decode partials (see include/lgsa.h).  Allocates only `out` when it is not given."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(q)
+    a = hca_args(q, pos0, k_win, v_win, kc, vc, max_pos=max_pos, window=window, block=block,
+                 scale=scale, q_lat=q_lat, w_gate=w_gate, out=out)
+    a.lse = _dev(lse, "lse")
+    _check("hca_attn_fwd_static", load().hca_attn_fwd_static(ctypes.byref(a), _stream(stream)))
     return out
 
 

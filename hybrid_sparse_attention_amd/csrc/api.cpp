@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/lgsa.h"
@@ -531,6 +532,63 @@ lgsa_status hca_attn_fwd(const lgsa_hca_args* a, void* stream) {
   const hipError_t e = a->dt == LGSA_BF16 ? lgsa::launch_hca_bf16(p, (hipStream_t)stream)
                                           : lgsa::launch_hca_f32(p, (hipStream_t)stream);
   return hip_status(e, "hca_attn_fwd");
+}
+
+// ------------------------------------------------------------------ allocation-free variant
+// hca_attn_fwd_static takes its scratch from `scratch`, a file-scope device array that every
+// GPU the library runs on holds until the process ends.  In host code the array's name is a
+// host-side stand-in, not a device address: its device address on the current GPU is looked up
+// once per device (first call on that device, with the device current) and kept in
+// g_scratch_dev, which is what the launch receives.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[LGSA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+lgsa_status static_scratch(const char* who, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LGSA_EHIP, "%s: hipGetDevice failed: %s", who, hipGetErrorString(e));
+  REQUIRE(dev >= 0 && dev < kMaxDevices, LGSA_EUNSUPPORTED,
+          "%s: device ordinal %d is beyond the %d devices the static scratch tracks", who, dev,
+          kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(LGSA_EHIP, "%s: hipGetSymbolAddress of the static scratch failed: %s", who,
+                  hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return LGSA_OK;
+}
+
+}  // namespace
+
+lgsa_status hca_attn_fwd_static(const lgsa_hca_args* a, void* stream) {
+  const lgsa_status s = check_hca(a);
+  if (s != LGSA_OK) return s;
+  const size_t need = hca_ws(a);
+  REQUIRE(need <= (size_t)LGSA_STATIC_SCRATCH_BYTES, LGSA_EWORKSPACE,
+          "hca_attn_fwd_static: the call needs %zu bytes of scratch, more than the %zu the "
+          "library holds per GPU (LGSA_STATIC_SCRATCH_BYTES); use hca_attn_fwd with a workspace",
+          need, (size_t)LGSA_STATIC_SCRATCH_BYTES);
+  lgsa::HcaParams p = to_params(a);
+  p.ws = nullptr;
+  p.ws_bytes = 0;
+  if (need > 0) {
+    const lgsa_status g = static_scratch("hca_attn_fwd_static", &p.ws);
+    if (g != LGSA_OK) return g;
+    p.ws_bytes = (size_t)LGSA_STATIC_SCRATCH_BYTES;
+  }
+  const hipError_t e = a->dt == LGSA_BF16 ? lgsa::launch_hca_bf16(p, (hipStream_t)stream)
+                                          : lgsa::launch_hca_f32(p, (hipStream_t)stream);
+  return hip_status(e, "hca_attn_fwd_static");
 }
 
 lgsa_status dsa_index_topk_workspace(const lgsa_index_args* a, size_t* bytes) {

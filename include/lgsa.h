@@ -155,6 +155,23 @@ lgsa_status hca_attn_fwd(const lgsa_hca_args* a, void* stream);
 lgsa_status hca_attn_fwd_workspace(const lgsa_hca_args* a, size_t* bytes);
 
 /* ---------------------------------------------------------------------------------------
+ * hca_attn_fwd_static -- hca_attn_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, validation, kernels and result as hca_attn_fwd, except that a->workspace and
+ * a->workspace_bytes are ignored: the scratch (the decode path's split partials) comes from a
+ * device array of LGSA_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs on,
+ * until the process ends.  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).  A call whose hca_attn_fwd_workspace() exceeds LGSA_STATIC_SCRATCH_BYTES
+ * returns LGSA_EWORKSPACE and enqueues nothing (prefill needs no scratch; decode of up to 128
+ * sequences of 64 heads, at any context, fits).  Every call on one GPU shares that GPU's
+ * array: calls ordered on one stream are safe, but calls that overlap in time on one GPU
+ * (other streams, other threads) race on it.  Each call writes every scratch entry it later
+ * reads, so the array needs no clearing.  LGSA_EHIP if the array's address cannot be obtained.
+ * --------------------------------------------------------------------------------------- */
+#define LGSA_STATIC_SCRATCH_BYTES (40u << 20)
+lgsa_status hca_attn_fwd_static(const lgsa_hca_args* a, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * hca_attn_bwd -- backward of hca_attn_fwd in prefill (the chain rule of its definition;
  * training runs whole sequences): every sequence b holds T positions from position 0, query
  * row i sits at position i, the window rows are the sequence's own k, v (win_len = T) and the

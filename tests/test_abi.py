@@ -138,6 +138,17 @@ def test_hca_workspace_queries(lib):
     assert _call(lib, "hca_attn_fwd", a) == lgsa.LGSA_EWORKSPACE
 
 
+def test_hca_static_scratch_limit(lib):
+    # decode of 160 sequences x 64 heads needs 42,106,880 bytes of split partials, more than the
+    # library's static scratch (40 MiB): refused before anything touches the GPU
+    a = _hca(B=160, Tq=1, max_pos=131071, win_len=128, n_cap=1024)
+    assert _call(lib, "hca_attn_fwd_static", a) == lgsa.LGSA_EWORKSPACE
+    assert "LGSA_STATIC_SCRATCH_BYTES" in lgsa.last_error()
+    # arguments are validated exactly as by hca_attn_fwd
+    assert _call(lib, "hca_attn_fwd_static", _hca(B=0)) == lgsa.LGSA_EINVAL
+    assert _call(lib, "hca_attn_fwd_static", _hca(q=FAKE_ODD)) == lgsa.LGSA_EINVAL
+
+
 def _idx(**kw):
     a = lgsa.IndexArgs()
     vals = dict(B=1, Tq=4096, S=4096, Hi=4, di=64, k=2048, q_idx=FAKE, w_idx=FAKE, k_idx=FAKE,
