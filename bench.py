@@ -5,11 +5,11 @@
 A step is one pass of the hot path over one batch of synthetic input of the HCA prefill at
 model shape (seq 32768, 64 query heads sharing one KV head, head dim 512, bf16, 256 mean-pooled
 compressed entries + 128-token window, gate from the 1024-wide query latent): hca_compress,
-hca_attn_fwd, then latent_gate in place on the attention output (the same two kernels that
-hca_attn_fwd enqueues when given the gate operands).  `value` is its algorithmic TFLOP/s
-(attention over the visible pairs + the gate GEMM).  `roofline` describes the kernel that takes
-the largest share of the step, bounded by MFMA or HBM according to its algorithmic work.  The decode and MLA-DSA workloads are timed too and reported
-under "secondary" in the same JSON line.  Inputs are seeded synthetic data already resident
+then hca_attn_fwd with the gate operands, whose kernel applies the gate in the attention
+epilogue.  `value` is its algorithmic TFLOP/s (attention over the visible pairs + the gate
+GEMM).  `roofline` describes the kernel that takes the largest share of the step, bounded by
+MFMA or HBM according to its algorithmic work.  The decode and MLA-DSA workloads are timed too
+and reported under "secondary" in the same JSON line.  Inputs are seeded synthetic data already resident
 in HBM when timing starts.  The CPU baseline times the fp64 oracle on a bounded sample of
 query rows of the same workload.
 """
@@ -78,9 +78,9 @@ def flush_cache(torch, buf):
 
 # --------------------------------------------------------------------------- workloads
 def run_c1(torch, lgsa, synth, to_dev, steps, warmup):
-    """Step = hca_compress -> hca_attn_fwd -> latent_gate (in place on the attention output).
-    hca_attn_fwd called with q_lat/w_gate enqueues exactly these two kernels back to back;
-    calling the gate through its own entry point lets HIP events bracket each kernel."""
+    """Step = hca_compress -> hca_attn_fwd with the gate operands, whose gated prefill kernel
+    applies sigmoid(q_lat W) in its epilogue (O never goes to memory).  A HIP event between
+    the two calls brackets each kernel."""
     T, H, d = 32768, 64, 512
     log("[bench] C1: generating inputs (seq %d, %d heads, d %d)" % (T, H, d))
     x = synth.hca_prefill(1, T=T, H=H, d=d, bf16=True, qkv_scale=1.0 / math.sqrt(512))
@@ -90,18 +90,13 @@ def run_c1(torch, lgsa, synth, to_dev, steps, warmup):
     out = torch.empty_like(dev["q"])
     stream = torch.cuda.current_stream()
     tm = Timer(torch, stream)
-    o2 = out.view(T, H * d)
-    ql2 = dev["q_lat"].view(T, -1)
 
     def step(evs=None):
         lgsa.hca_compress(dev["k"], dev["v"], kc, vc)
         if evs is not None:
             evs.append(tm.event())
         lgsa.hca_attn_fwd(dev["q"], dev["pos0"], dev["k"], dev["v"], kc, vc, max_pos=T - 1,
-                          out=out)
-        if evs is not None:
-            evs.append(tm.event())
-        lgsa.latent_gate(ql2, dev["w_gate"], o2, out=o2)
+                          q_lat=dev["q_lat"], w_gate=dev["w_gate"], out=out)
 
     for _ in range(warmup):
         step()
@@ -115,26 +110,47 @@ def run_c1(torch, lgsa, synth, to_dev, steps, warmup):
     t1 = tm.event()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    # marks per step: [after compress, after attention, after gate]
-    ends = [t0] + marks[2::3][:-1]
-    comp_ms = [a.elapsed_time(b) for a, b in zip(ends, marks[0::3])]
-    attn_ms = [a.elapsed_time(b) for a, b in zip(marks[0::3], marks[1::3])]
-    gate_ms = [a.elapsed_time(b) for a, b in zip(marks[1::3], marks[2::3])]
+    # marks per step: [after compress, after the gated attention]
+    ends = [t0] + marks[1::2][:-1]
+    comp_ms = [a.elapsed_time(b) for a, b in zip(ends, marks[0::2])]
+    attn_ms = [a.elapsed_time(b) for a, b in zip(marks[0::2], marks[1::2])]
     att, gate = hca_prefill_flops(T, H, d)
     gib = 1 << 30
     # algorithmic bytes: each input read once, each output written once
-    att_bytes = (2 * gib + 2 * gib + 2 * (T * d * 2) + 2 * (T // 128) * d * 2)
-    gate_bytes = (T * 1024 * 2 + 1024 * H * d * 2 + 2 * gib + 2 * gib)
+    fused_bytes = (2 * gib + 2 * gib + 2 * (T * d * 2) + 2 * (T // 128) * d * 2 +
+                   T * 1024 * 2 + 1024 * H * d * 2)
     comp_bytes = 2 * T * d * 2 + 2 * (T // 128) * d * 2
     kernels = [
-        dict(name="hca_prefill_kernel", call="hca_attn_fwd", ms=float(np.mean(attn_ms)),
-             flops=att, bytes=att_bytes, src="hca_bf16.hip"),
-        dict(name="gate_bf16_big_kernel", call="latent_gate", ms=float(np.mean(gate_ms)),
-             flops=gate, bytes=gate_bytes, src="gate.hip"),
+        dict(name="hca_prefill_gated_kernel", call="hca_attn_fwd",
+             ms=float(np.mean(attn_ms)), ms_median=float(np.median(attn_ms)), flops=att + gate,
+             bytes=fused_bytes, src="hca_bf16.hip"),
         dict(name="compress_kernel", call="hca_compress", ms=float(np.mean(comp_ms)),
-             flops=0.0, bytes=comp_bytes, src="compress.hip"),
+             ms_median=float(np.median(comp_ms)), flops=0.0, bytes=comp_bytes,
+             src="compress.hip"),
     ]
-    return dict(ms_per_step=total_ms / steps, flops=att + gate, kernels=kernels, inputs=x)
+
+    # the same step composed of the unfused calls, for comparison: the ungated attention
+    # kernel writes O, then latent_gate rescales it in place
+    o2 = out.view(T, H * d)
+    ql2 = dev["q_lat"].view(T, -1)
+
+    def unfused():
+        lgsa.hca_compress(dev["k"], dev["v"], kc, vc)
+        lgsa.hca_attn_fwd(dev["q"], dev["pos0"], dev["k"], dev["v"], kc, vc, max_pos=T - 1,
+                          out=out)
+        lgsa.latent_gate(ql2, dev["w_gate"], o2, out=o2)
+
+    unfused()
+    torch.cuda.synchronize()
+    a = tm.event()
+    for _ in range(5):
+        unfused()
+    b = tm.event()
+    torch.cuda.synchronize()
+    unfused_ms = a.elapsed_time(b) / 5
+    return dict(ms_per_step=total_ms / steps, flops=att + gate, kernels=kernels, inputs=x,
+                step_ms_min=min(a_ + c_ for a_, c_ in zip(attn_ms, comp_ms)),
+                unfused_ms=unfused_ms)
 
 
 def kernel_roofline(k, traffic):
@@ -150,6 +166,7 @@ def kernel_roofline(k, traffic):
     return dict(bound=bound, achieved=round(ach, 2), peak=peak, unit=unit,
                 frac=round(ach / peak, 4), traffic=traffic, kernel=k["name"],
                 entry_point=k["call"], launch_ms=round(k["ms"], 4),
+                launch_ms_median=round(k.get("ms_median", k["ms"]), 4),
                 flops_per_launch=k["flops"], bytes_per_launch=k["bytes"])
 
 
@@ -571,7 +588,8 @@ def main():
     kern = [kernel_roofline(k, traffic_record(k)) for k in r1["kernels"]]
     dom = max(range(len(kern)), key=lambda i: r1["kernels"][i]["ms"])
     roofline = kern[dom]
-    secondary = dict(c1_kernels=[kern[i] for i in range(len(kern)) if i != dom])
+    secondary = dict(c1_kernels=[kern[i] for i in range(len(kern)) if i != dom],
+                     c1_unfused_step_ms=round(r1["unfused_ms"], 4))
     cpu = None
     if not args.no_cpu:
         log("[bench] CPU baseline: fp64 oracle on a sample of C1 rows")
@@ -619,8 +637,8 @@ def main():
         scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
         config=dict(workload="HCA prefill at model shape: seq 32768, 64 query heads + 1 shared "
                              "KV head, head dim 512, bf16, 256 mean-pooled entries + 128-token "
-                             "window, low-rank sigmoid gate (W_gate 1024x32768); step = "
-                             "hca_compress + hca_attn_fwd + latent_gate",
+                             "window, low-rank sigmoid gate (W_gate 1024x32768) fused into the "
+                             "attention epilogue; step = hca_compress + gated hca_attn_fwd",
                     seq_len=32768, heads=64, head_dim=512, batch=1, parallelism="none"),
         roofline=roofline, cpu_baseline=cpu, secondary=secondary)
     print(json.dumps(line))

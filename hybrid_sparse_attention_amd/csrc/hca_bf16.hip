@@ -373,6 +373,277 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_kernel(HcaParams p) {
   }
 }
 
+// ------------------------------------------------------------------ gated prefill (fused)
+// The gate is applied in the epilogue of the attention, so O never goes to memory: the HBM
+// traffic of the gated step is Q in and out once.  One workgroup of 8 waves per (sequence,
+// 128 query tokens, head): wave w owns tokens 16w .. 16w + 15 of the tile over the whole
+// 512-wide head, with the key loop above.  The workgroup streams the union of its waves' key
+// tiles; each wave computes only the tiles holding a key that one of its rows sees (5 of the 8
+// window tiles of a whole tile) and skips the masking of tiles its rows see in full.
+//
+// Then the gate for the wave's 16 rows and the head's 512 channels: G^T = W^T q_lat^T on the
+// MFMA shape of O^T += V^T P^T, with a 32-row slice of W in an LDS tile laid out as a value
+// tile (its transposed reads give W^T), and the lane's own q_lat row, read from memory, as the
+// B operand in the slot order of P.  The W slices stream through a four-stage ring (the four
+// key/value buffers of the key loop), three steps ahead.  O is kept as packed bfloat16 (the
+// value the unfused path would store) while the gate accumulates, then out = O * sigmoid(G)
+// leaves from the registers.
+constexpr int FQ = 128;  // query tokens per workgroup of the gated prefill kernel
+
+// Whether tile t holds a key visible to some row at positions [t_lo, t_hi] (all valid).
+__device__ __forceinline__ bool tile_touches(const Tile& t, int t_lo, int t_hi, int window,
+                                             int block) {
+  if (t.kind == 0) return block * t.start + block - 1 <= t_hi;
+  return t.start <= t_hi && t.start + t.count - 1 >= t_lo - window + 1;
+}
+
+// The gate loop's transfers are issued in inline assembly (LDS DMA, global_load_lds_dwordx4:
+// lane l's 16 bytes land at M0 + 16 l).  The compiler then does not see them and does not make
+// every LDS read wait for the transfers in flight into the other stages; the loop waits for
+// its own transfers (wait_vm) before the barrier that precedes their reads.  The instruction
+// writes no register, so nothing the compiler allocates is written late.
+// M0 is named as clobbered (the compiler warns that it keeps no value of its own there across
+// the statement; no code after these transfers relies on one).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_asm(const char* base, uint32_t lane_off, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %0"
+      :
+      : "s"(base), "v"(lane_off), "s"(lds)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Step k0 of the gate contraction into one stage: rows k0 + 4 wave .. + 3 of the head's W
+// slice (1 KiB each) into a tile of pitch VLD, and the wave's 16 q_lat rows, columns
+// k0 .. k0 + 31 (64 bytes each), into its own 1 KiB of the q_lat tile of the stage, which
+// holds the workgroup's 128 rows: lane l lands at row l / 4, 16-byte slot l % 4, and fetches
+// chunk (l % 4) ^ ((row / 4) % 4) of that row, so that the fragment reads of 16 rows hit
+// distinct banks.  Five transfers per wave.
+// ql_wave is the q_lat row of the wave's first row and q_off the lane's byte offset from it
+// (its row, clamped to the last row, and its chunk).
+__device__ __forceinline__ void gate_dma(const char* w_head, size_t ldw, const char* ql_wave,
+                                         uint32_t q_off, int k0, char* wdst, char* qdst,
+                                         int wave, int lane) {
+  const uint32_t lo = (uint32_t)opaque(16 * lane);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    dma16_asm(w_head + (size_t)(k0 + 4 * wave + u) * ldw, lo,
+              lds_addr(wdst + (4 * wave + u) * VLD));
+  dma16_asm(ql_wave + 2 * k0, (uint32_t)opaque((int)q_off), lds_addr(qdst + 1024 * wave));
+}
+
+// Byte offset in a q_lat tile of columns 8c' .. of row r, c' the 16-byte chunk (0..3).
+__device__ __forceinline__ int ql_chunk(int r, int c) { return 64 * r + 16 * (c ^ ((r >> 2) & 3)); }
+
+// One contraction step of 32 for the wave's 64 channels (64 wave .. + 63 of the head) and all
+// 128 rows of the tile: G^T = W^T q_lat^T, acc[i][j] = G^T of channels 64 wave + 16 i .. and
+// rows 16 j ..  W^T comes from the stage's W tile through the transposing read (rows 4g + a and
+// 16 + 4g + a: contraction columns 4g .. 4g + 3 in slots 8g .. 8g + 3, 16 + 4g .. in slots
+// 8g + 4 ..), q_lat^T from the stage's q_lat tile in the same slot order.  Each W^T fragment
+// feeds 8 products and each q_lat fragment 4.
+__device__ __forceinline__ void gate_step(f32x4_t (&acc)[4][8], const char* ws, const char* qs,
+                                          int wave, int lane) {
+  const int l16 = lane & 15, g = lane >> 4;
+  Frag8 wa[4];
+  const char* v0 = ws + (4 * g + (l16 >> 2)) * VLD + 8 * (l16 & 3) + 128 * wave;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint2 lo = lds_read_tr16(v0 + 32 * i);
+    const uint2 hi = lds_read_tr16(v0 + 32 * i + 16 * VLD);
+    wa[i].u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+  const int c0 = g >> 1, b8 = 8 * (g & 1);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 16 * j + l16;
+    Frag8 qf;
+    const uint2 lo = *(const uint2*)(qs + ql_chunk(r, c0) + b8);
+    const uint2 hi = *(const uint2*)(qs + ql_chunk(r, 2 + c0) + b8);
+    qf.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i][j] = mfma_16x16x32(wa[i], qf, acc[i][j]);
+  }
+}
+
+__shared__ __attribute__((aligned(1024))) char pf_q0[8 * 1024];
+__shared__ __attribute__((aligned(1024))) char pf_q1[8 * 1024];
+__shared__ __attribute__((aligned(1024))) char pf_q2[8 * 1024];
+
+__global__ __launch_bounds__(512, 1) void hca_prefill_gated_kernel(HcaParams p) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int n_qt = (p.Tq + FQ - 1) / FQ;
+  // XCD-aware order (consecutive ids go to the 8 XCDs in turn): XCD x takes the heads
+  // x H/8 .. x H/8 + H/8 - 1 of every token tile, token tiles in descending order (the longest
+  // key lists first) and the heads of a tile one after another.  The ~32 workgroups an XCD
+  // holds at once are then 4 token tiles x 8 heads: each key/value tile is read by 8 of them
+  // from the XCD's L2, and each head's W slice by 4.
+  int qt, h, b;
+  if (p.H % 8 == 0) {
+    const int hx = p.H / 8, idx = blockIdx.x / 8;
+    h = (blockIdx.x % 8) * hx + idx % hx;
+    const int tt = idx / hx;  // (sequence, token tile) in descending tile order
+    b = tt / n_qt;
+    qt = n_qt - 1 - tt % n_qt;
+  } else {
+    qt = n_qt - 1 - (int)blockIdx.x % n_qt;
+    h = (blockIdx.x / n_qt) % p.H;
+    b = blockIdx.x / (n_qt * p.H);
+  }
+  const int pos = p.pos0[b];
+  const int i_first = qt * FQ;
+  const int i_end = min(p.Tq, i_first + FQ);
+  const int t_first = pos + i_first, t_last = pos + i_end - 1;
+
+  const int ne = t_last >= 0 ? min(p.n_cap, (t_last + 1) / p.block) : 0;
+  const int s_lo = max(0, t_first - p.window + 1);
+  const int nw = max(0, t_last - s_lo + 1);
+  const int tiles_c = (ne + KT - 1) / KT, tiles_w = (nw + KT - 1) / KT;
+  auto tile_of = [&](int ti) {
+    Tile t;
+    if (ti < tiles_c) {
+      t.kind = 0;
+      t.start = KT * ti;
+      t.count = min(KT, ne - t.start);
+      t.row0 = t.start;
+    } else {
+      t.kind = 1;
+      t.start = s_lo + KT * (ti - tiles_c);
+      t.count = min(KT, t_last - t.start + 1);
+      t.row0 = t.start % p.win_len;
+    }
+    t.full = false;  // decided per wave
+    return t;
+  };
+  Src src;
+  src.kc = (const char*)p.kc + (size_t)b * p.n_cap * ROWB;
+  src.vc = (const char*)p.vc + (size_t)b * p.n_cap * ROWB;
+  src.kw = (const char*)p.k_win + (size_t)b * p.win_len * ROWB;
+  src.vw = (const char*)p.v_win + (size_t)b * p.win_len * ROWB;
+  src.win_len = p.win_len;
+
+  const int r_first = i_first + 16 * wave;  // token of the wave's row 0
+  const int n_valid = max(0, min(16, i_end - r_first));
+  RowPos rp;
+  rp.t0 = pos + r_first;
+  rp.n_rows = i_end - r_first;
+  rp.step = 1;
+  rp.window = p.window;
+  rp.block = p.block;
+  const int tw_lo = pos + r_first, tw_hi = pos + r_first + n_valid - 1;
+  // the lane's row; rows past the end read the last row and are never stored
+  const int i_row = min(r_first + l16, i_end - 1);
+  Frag8 qf[16];
+  {
+    const uint16_t* qr = (const uint16_t*)p.q + (((size_t)b * p.Tq + i_row) * p.H + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) qf[kk].u = *(const uint4*)(qr + 32 * kk + 8 * g);
+  }
+  RowState st;
+  init_row_state(st);
+  const float scale_log2 = p.scale * LOG2E;
+  tile_key_loop(src, tile_of, tiles_c + tiles_w, wave, 8, lane,
+                [&](const Tile& t0, const char* kcur, const char* vcur) {
+                  if (n_valid == 0 || tw_lo < 0 ||
+                      !tile_touches(t0, tw_lo, tw_hi, p.window, p.block))
+                    return;
+                  Tile t = t0;
+                  t.full = n_valid == 16 && tile_full(t, tw_lo, tw_hi, p.window, p.block);
+                  f32x4_t s[2];
+                  row_scores(s, qf, kcur, lane);
+                  row_softmax_pv(st, s, vcur, t, rp, scale_log2, lane);
+                });
+
+  const int i = r_first + l16;
+  const float lt = wave_sum16(st.l);
+  const float inv = final_scale(st.m, lt);
+  if (p.lse != nullptr && g == 0 && i < i_end)
+    p.lse[((size_t)b * p.Tq + i) * p.H + h] =
+        inv > 0.f ? (st.m + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
+  uint2 ob[32];  // O rounded to bfloat16, as the unfused path stores it
+#pragma unroll
+  for (int cb = 0; cb < 32; ++cb) {
+    ob[cb].x = pack_bf16x2(st.o[cb][0] * inv, st.o[cb][1] * inv);
+    ob[cb].y = pack_bf16x2(st.o[cb][2] * inv, st.o[cb][3] * inv);
+    // pins the packing here: left to itself the compiler sinks it to the epilogue and keeps
+    // the fp32 O (twice the registers) live through the gate loop
+    asm volatile("" : "+v"(ob[cb].x), "+v"(ob[cb].y));
+  }
+
+  // ------------------------------------------------------------------ gate
+  // Three stages (W tile + q_lat tile), two steps in flight ahead of the one being read.
+  const size_t ldw = (size_t)p.H * D * 2;  // bytes of one W row
+  const size_t ldq = (size_t)p.d_lat * 2;  // bytes of one q_lat row
+  const char* w_head = (const char*)p.w_gate + (size_t)h * ROWB;
+  // the wave's first q_lat row; rows past the end read the last row (and are never stored)
+  const int r_dma = min(r_first, i_end - 1);
+  const char* ql_wave = (const char*)p.q_lat + ((size_t)b * p.Tq + r_dma) * ldq;
+  const uint32_t q_off = (uint32_t)((min(r_first + (lane >> 2), i_end - 1) - r_dma) * (int)ldq +
+                                    16 * ((lane & 3) ^ ((lane >> 4) & 3)));
+  const int nk = p.d_lat / KT;  // contraction steps of 32
+  f32x4_t acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto wst = [](int i) { return i == 0 ? pf_k0 : (i == 1 ? pf_v0 : pf_k1); };
+  auto qst = [](int i) { return i == 0 ? pf_q0 : (i == 1 ? pf_q1 : pf_q2); };
+  // the key loop ended with a barrier: every stage is free
+  gate_dma(w_head, ldw, ql_wave, q_off, 0, wst(0), qst(0), wave, lane);
+  if (nk > 1) gate_dma(w_head, ldw, ql_wave, q_off, KT, wst(1), qst(1), wave, lane);
+  if (nk > 1) wait_vm<5>(); else wait_vm<0>();
+  lds_barrier();
+  for (int s = 0; s < nk; ++s) {
+    // step s + 2 goes into the stage step s - 1 read (free since the barrier that ended it)
+    const int st2 = (s + 2) % 3;
+    if (s + 2 < nk)
+      gate_dma(w_head, ldw, ql_wave, q_off, (s + 2) * KT, wst(st2), qst(st2), wave, lane);
+    gate_step(acc, wst(s % 3), qst(s % 3), wave, lane);
+    if (s + 2 < nk) wait_vm<5>(); else wait_vm<0>();  // step s + 1 has landed
+    lds_barrier();
+  }
+
+  // sigmoid(G) as bfloat16 into LDS, rows of the tile 32 to a buffer (pitch VLD): the last
+  // step ended with a barrier, so every buffer is free
+  auto sbuf = [](int q4) { return q4 == 0 ? pf_k0 : (q4 == 1 ? pf_v0 : (q4 == 2 ? pf_k1 : pf_v1)); };
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    char* rowp = sbuf(j >> 1) + (16 * (j & 1) + l16) * VLD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint2 v;
+      v.x = pack_bf16x2(sigmoidf_fast(acc[i][j][0]), sigmoidf_fast(acc[i][j][1]));
+      v.y = pack_bf16x2(sigmoidf_fast(acc[i][j][2]), sigmoidf_fast(acc[i][j][3]));
+      *(uint2*)(rowp + 2 * (64 * wave + 16 * i + 4 * g)) = v;
+    }
+  }
+  lds_barrier();
+  // out = O * sigmoid(G) for the wave's own rows, in the layout of O
+  if (i < i_end) {
+    const char* srow = sbuf(wave >> 1) + (16 * (wave & 1) + l16) * VLD + 8 * g;
+    uint16_t* orow = (uint16_t*)p.out + (((size_t)b * p.Tq + i) * p.H + h) * D;
+#pragma unroll
+    for (int cb = 0; cb < 32; ++cb) {
+      const uint2 sg = *(const uint2*)(srow + 32 * cb);
+      const float o0 = __uint_as_float(ob[cb].x << 16), o1 = __uint_as_float(ob[cb].x & 0xFFFF0000u);
+      const float o2 = __uint_as_float(ob[cb].y << 16), o3 = __uint_as_float(ob[cb].y & 0xFFFF0000u);
+      uint2 r;
+      r.x = pack_bf16x2(o0 * __uint_as_float(sg.x << 16), o1 * __uint_as_float(sg.x & 0xFFFF0000u));
+      r.y = pack_bf16x2(o2 * __uint_as_float(sg.y << 16), o3 * __uint_as_float(sg.y & 0xFFFF0000u));
+      *(uint2*)(orow + 16 * cb + 4 * g) = r;
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------- decode
 // One workgroup of 4 waves (16 heads each: the 64 heads of a group) per (sequence, key split).
 // Keys of a sequence: compressed entries 0..ne-1, then raw positions s_lo..t; every row is at
@@ -890,6 +1161,10 @@ hipError_t launch_hca_bf16(const HcaParams& p, hipStream_t stream) {
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
+  } else if (p.q_lat != nullptr) {  // the gate in the attention epilogue
+    const long long grid = (long long)p.B * ((p.Tq + FQ - 1) / FQ) * p.H;
+    hipLaunchKernelGGL(hca_prefill_gated_kernel, dim3((unsigned)grid), dim3(512), 0, stream, p);
+    return hipGetLastError();
   } else {
     const long long grid = (long long)p.B * ((p.Tq + 31) / 32) * ((p.H + 3) / 4);
     hipLaunchKernelGGL(hca_prefill_kernel, dim3((unsigned)grid), dim3(512), 0, stream, p);

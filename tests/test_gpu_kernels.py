@@ -111,6 +111,44 @@ def test_hca_prefill_chunked_positions(torch, orc):
     bf16_ok(from_dev(out).reshape(-1, H, 512), ref, "hca chunked")
 
 
+@pytest.mark.parametrize("d_lat", [384, 128, 192])
+def test_hca_prefill_gated_ring_positions(torch, orc, d_lat):
+    """The gated prefill over a ring of raw rows: two sequences whose 200 query rows start at
+    positions 0 and 1000, raw rows in a 512-row ring (position p in row p % 512; 512 >= window
+    + 199), entries from each whole prefix.  Gate contractions of 384 (two groups of four
+    steps of 32 before the last four) and 128 (the last four only) run in the attention
+    epilogue; 192 (not a multiple of 128) runs the gate GEMM after the attention kernel.  The
+    log-sum-exp written matches the ungated kernel's."""
+    B, Tq, H, W, ctx = 2, 200, 3, 512, 1200
+    pos0 = np.array([0, 1000], np.int32)
+    q = synth.normal(233, (B, Tq, H, 512), 1.0, True)
+    k = synth.normal(234, (B, ctx, 512), 1.0, True)
+    v = synth.normal(235, (B, ctx, 512), 1.0, True)
+    ql = synth.normal(236, (B, Tq, d_lat), 1.0, True)
+    wg = synth.normal(237, (d_lat, H * 512), 0.02, True)
+    ring_k = np.zeros((B, W, 512), np.uint16)
+    ring_v = np.zeros((B, W, 512), np.uint16)
+    for b in range(B):
+        last = pos0[b] + Tq - 1
+        for p_ in range(max(0, last - W + 1), last + 1):
+            ring_k[b, p_ % W] = k[b, p_]
+            ring_v[b, p_ % W] = v[b, p_]
+    kc, vc = lgsa.hca_compress(to_dev(k), to_dev(v))
+    args = (to_dev(q), to_dev(pos0), to_dev(ring_k), to_dev(ring_v), kc, vc)
+    lse_g = torch.empty((B, Tq, H), dtype=torch.float32, device="cuda")
+    lse_u = torch.empty_like(lse_g)
+    out = lgsa.hca_attn_fwd(*args, max_pos=ctx - 1, q_lat=to_dev(ql), w_gate=to_dev(wg),
+                            lse=lse_g)
+    lgsa.hca_attn_fwd(*args, max_pos=ctx - 1, lse=lse_u)
+    torch.cuda.synchronize()
+    ref = orc.hca_attn(q, pos0, ring_k, ring_v, orc.hca_compress(k), orc.hca_compress(v),
+                       q_lat=ql, w_gate=wg)
+    bf16_ok(from_dev(out).reshape(-1, H, 512), ref, "hca gated ring")
+    a, u = lse_g.cpu().numpy(), lse_u.cpu().numpy()
+    assert np.all(np.isfinite(a))
+    np.testing.assert_allclose(a, u, rtol=1e-5, atol=1e-5)
+
+
 def test_hca_prefill_f32_config0(torch, orc):
     """The tiny fp32 workload: T=1024, 4 heads, 8 compressed entries, gated."""
     x = synth.hca_prefill(0, T=1024, H=4, bf16=False, qkv_scale=1.0)
