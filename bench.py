@@ -1,6 +1,6 @@
 """Benchmark of the Latent-Gated Sparse Attention forward hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs 1,2,3,4] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs 0,1,2,3,4] [--no-cpu]
 
 A step is one pass of the hot path over one batch of synthetic input of the HCA prefill at
 model shape (seq 32768, 64 query heads sharing one KV head, head dim 512, bf16, 256 mean-pooled
@@ -32,6 +32,7 @@ METRIC = "HCA/DSA attention prefill TFLOP/s + decode GB/s; % of MI355X roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (matrix / packed vector)
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+ORACLE_TIMING = True        # --no-cpu turns the fp64 oracle timings off
 
 
 def log(*a):
@@ -181,6 +182,63 @@ def run_copy(torch, steps):
     print(json.dumps(dict(copy_bytes_read=4 * n, copy_bytes_written=4 * n, launches=steps)))
 
 
+def oracle_seconds(fn, repeats=1):
+    """Best wall time of `repeats` calls of an oracle computation on the host cores (None when
+    the oracle timings are off)."""
+    if not ORACLE_TIMING:
+        return None
+    best = None
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+    return best
+
+
+def run_c0(torch, lgsa, synth, to_dev, iters):
+    """The tiny fp32 HCA prefill: seq 1024, 4 heads, d 512, 8 entries, gated (W 1024 x 2048);
+    step = hca_compress + gated hca_attn_fwd.  Also the fp64 oracle on the whole workload,
+    best of 3."""
+    import oracle
+
+    T, H, d = 1024, 4, 512
+    x = synth.hca_prefill(0, T=T, H=H, bf16=False)
+    dev = {k: to_dev(v) for k, v in x.items()}
+    tm = Timer(torch, torch.cuda.current_stream())
+
+    def step():
+        kc, vc = lgsa.hca_compress(dev["k"], dev["v"])
+        return lgsa.hca_attn_fwd(dev["q"], dev["pos0"], dev["k"], dev["v"], kc, vc,
+                                 max_pos=T - 1, q_lat=dev["q_lat"], w_gate=dev["w_gate"])
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(iters):
+        a = tm.event()
+        step()
+        b = tm.event()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    att, gate = hca_prefill_flops(T, H, d)
+    oracle.build(force=False)
+
+    def orc():
+        kc = oracle.hca_compress(x["k"])
+        vc = oracle.hca_compress(x["v"])
+        oracle.hca_attn(x["q"], x["pos0"], x["k"], x["v"], kc, vc, q_lat=x["q_lat"],
+                        w_gate=x["w_gate"])
+
+    secs = oracle_seconds(orc, 3)
+    orec = None if secs is None else dict(
+        seconds=round(secs, 4), TFLOPs=(att + gate) / secs / 1e12, cores=oracle.max_threads(),
+        kind="oracle", sample="whole workload (1024 rows, 4 heads, gated), best of 3")
+    return dict(ms=float(np.median(ms)), ms_min=float(np.min(ms)), flops=att + gate,
+                oracle=orec)
+
+
 def run_c2(torch, lgsa, synth, to_dev, iters):
     B, ctx, H, d = 64, 131072, 64, 512
     log("[bench] C2: generating inputs (batch %d, context %d)" % (B, ctx))
@@ -206,7 +264,16 @@ def run_c2(torch, lgsa, synth, to_dev, iters):
         torch.cuda.synchronize()
         ms.append(a.elapsed_time(b))
     nbytes = sum(int(v.nbytes) for k, v in x.items() if k != "pos0") + int(x["q"].nbytes)
-    return dict(ms=float(np.median(ms)), ms_min=float(np.min(ms)), bytes=nbytes)
+    import oracle
+
+    oracle.build(force=False)
+    secs = oracle_seconds(lambda: oracle.hca_attn(x["q"], x["pos0"], x["k_win"], x["v_win"],
+                                                  x["kc"], x["vc"], q_lat=x["q_lat"],
+                                                  w_gate=x["w_gate"]))
+    orec = None if secs is None else dict(
+        seconds=round(secs, 3), GBps=nbytes / secs / 1e9, cores=oracle.max_threads(),
+        kind="oracle", sample="all 64 sequences, all heads, gated")
+    return dict(ms=float(np.median(ms)), ms_min=float(np.min(ms)), bytes=nbytes, oracle=orec)
 
 
 def run_c3(torch, lgsa, synth, to_dev, iters):
@@ -269,9 +336,47 @@ def run_c3(torch, lgsa, synth, to_dev, iters):
         torch.cuda.synchronize()
         bwd_ms.append(a.elapsed_time(b))
     del ws, dq, dk, dout, o_ung, lse
+
+    # the gathers alone: the same top-k lists over the 32 MiB table of 512-byte latent rows,
+    # the sparse kernel's DMA pattern with no arithmetic (the bound of its data movement)
+    lists = idx.view(T, k)
+    table = ds["kv_lat"].view(T, d)
+    lgsa.sparse_gather_probe(table, lists)
+    torch.cuda.synchronize()
+    g_ms = []
+    for _ in range(iters):
+        a = tm.event()
+        lgsa.sparse_gather_probe(table, lists)
+        b = tm.event()
+        torch.cuda.synchronize()
+        g_ms.append(a.elapsed_time(b))
+    gathered = float(pairs) * d * 2
+
+    # the fp64 oracle on a bounded sample: top-k of 64 evenly spaced rows, gated sparse
+    # attention of 128 evenly spaced rows over the GPU's own lists
+    import oracle
+
+    oracle.build(force=False)
+    rows_i = np.linspace(0, T - 1, 64).astype(np.int64)
+    rows_s = np.linspace(0, T - 1, 128).astype(np.int64)
+    idx_h = idx.cpu().numpy()
+    t_i = oracle_seconds(lambda: oracle.dsa_topk(xi["q_idx"], xi["w_idx"], xi["k_idx"],
+                                                 xi["pos0"], k, rows=rows_i))
+    t_s = oracle_seconds(lambda: oracle.sparse_attn(xs["q"], xs["kv_lat"], idx_h,
+                                                    q_lat=xs["q_lat"], w_gate=xs["w_gate"],
+                                                    rows=rows_s))
+    i_fl = float(np.sum((rows_i + 1) * (4 * 2 * 64 + 8)))
+    s_fl = float(np.sum(np.minimum(k, rows_s + 1))) * 4 * d * H + 2.0 * len(rows_s) * 1024 * H * d
+    orec = None if t_i is None else dict(
+        indexer_seconds=round(t_i, 3), indexer_TFLOPs=i_fl / t_i / 1e12,
+        sparse_seconds=round(t_s, 3), sparse_TFLOPs=s_fl / t_s / 1e12,
+        cores=oracle.max_threads(), kind="oracle",
+        sample="top-k of 64 and gated sparse attention of 128 evenly spaced query rows (all "
+               "64 heads)")
     return dict(index_ms=float(np.median(idx_ms)), sparse_ms=float(np.median(sp_ms)),
                 sparse_flops=sp_flops, index_flops=float(ind_flops),
-                bwd_ms=float(np.median(bwd_ms)), bwd_flops=10.0 * d * pairs * H)
+                bwd_ms=float(np.median(bwd_ms)), bwd_flops=10.0 * d * pairs * H,
+                gather_ms=float(np.median(g_ms)), gather_bytes=gathered, oracle=orec)
 
 
 def run_csa(torch, lgsa, synth, to_dev, iters):
@@ -385,7 +490,6 @@ def run_c4(torch, lgsa, synth, to_dev, iters):
     dh = {k: to_dev(v) for k, v in xh.items()}
     di = {k: to_dev(v) for k, v in xi.items()}
     ds = {k: to_dev(v) for k, v in xs.items()}
-    del xs["kv_lat"]
     out_h = torch.empty_like(dh["q"])
     out_s = torch.empty_like(ds["q"])
     idx = torch.empty((B, 1, 2048), dtype=torch.int32, device="cuda")
@@ -416,10 +520,27 @@ def run_c4(torch, lgsa, synth, to_dev, iters):
         ind.append(e[1].elapsed_time(e[2]))
     hbytes = sum(int(v.nbytes) for k, v in xh.items() if k != "pos0") + int(xh["q"].nbytes)
     ibytes = sum(int(v.nbytes) for k, v in xi.items() if k != "pos0") + B * 2048 * 4
-    sbytes = (sum(int(v.nbytes) for v in xs.values()) + B * 2048 * 256 * 2 +
-              int(xs["q"].nbytes))
+    sbytes = (sum(int(v.nbytes) for k_, v in xs.items() if k_ != "kv_lat") +
+              B * 2048 * 256 * 2 + int(xs["q"].nbytes))
+    # the fp64 oracle on the whole step: HCA of the 8 sequences, their top-k, then the gated
+    # sparse attention over the oracle's own lists
+    import oracle
+
+    oracle.build(force=False)
+    def orc():
+        oracle.hca_attn(xh["q"], xh["pos0"], xh["k_win"], xh["v_win"], xh["kc"], xh["vc"],
+                        q_lat=xh["q_lat"], w_gate=xh["w_gate"])
+        o_idx, _ = oracle.dsa_topk(xi["q_idx"], xi["w_idx"], xi["k_idx"], xi["pos0"], 2048)
+        oracle.sparse_attn(xs["q"], xs["kv_lat"], o_idx.reshape(B, 1, 2048), q_lat=xs["q_lat"],
+                           w_gate=xs["w_gate"])
+
+    secs = oracle_seconds(orc)
+    nb = hbytes + ibytes + sbytes
+    orec = None if secs is None else dict(
+        seconds=round(secs, 3), GBps=nb / secs / 1e9, cores=oracle.max_threads(),
+        kind="oracle", sample="whole step: all 8 sequences, both layers, gated")
     return dict(ms=float(np.median(tot)), index_ms=float(np.median(ind)),
-                bytes=hbytes + ibytes + sbytes, index_bytes=ibytes)
+                bytes=nb, index_bytes=ibytes, oracle=orec)
 
 
 def run_vha(torch, lgsa, synth, to_dev, iters):
@@ -554,12 +675,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--configs", default="1,2,3,4",
-                    help="workloads to run; 1 is the headline, 2-4 are reported as secondary")
+    ap.add_argument("--configs", default="0,1,2,3,4",
+                    help="workloads to run; 1 is the headline, 0 and 2-4 are reported as "
+                         "secondary")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy", action="store_true",
                     help="only run a 1 GiB device copy (calibrates the HBM traffic counters)")
     args = ap.parse_args()
+    global ORACLE_TIMING
+    ORACLE_TIMING = not args.no_cpu
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -595,42 +719,54 @@ def main():
         log("[bench] CPU baseline: fp64 oracle on a sample of C1 rows")
         cpu = cpu_baseline(r1["inputs"])
     del r1["inputs"]
+    if 0 in cfgs:
+        log("[bench] C0: tiny fp32 HCA prefill")
+        r0 = run_c0(torch, lgsa, synth, to_dev, 20)
+        tf0 = r0["flops"] / (r0["ms"] * 1e-3) / 1e12
+        secondary["c0_hca_prefill_f32"] = dict(
+            ms=round(r0["ms"], 4), ms_min=round(r0["ms_min"], 4), TFLOPs=round(tf0, 2),
+            fp32_frac=round(tf0 / PEAK_FP32_TFLOPS, 4), oracle=r0["oracle"])
     if 2 in cfgs:
         r2 = run_c2(torch, lgsa, synth, to_dev, 200)
         gbps = r2["bytes"] / (r2["ms"] * 1e-3) / 1e9
         secondary["c2_hca_decode"] = dict(ms=round(r2["ms"], 4), ms_min=round(r2["ms_min"], 4),
                                           GBps=round(gbps, 1),
                                           hbm_frac=round(gbps / PEAK_HBM_GBPS, 4),
-                                          bytes=r2["bytes"])
+                                          bytes=r2["bytes"], oracle=r2["oracle"])
     secondary["vha_mix_prefill"] = run_vha(torch, lgsa, synth, to_dev, 10)
     secondary["gate_bwd_prefill"] = run_gate_bwd(torch, lgsa, 3)
     secondary["hca_bwd_prefill"] = run_hca_bwd(torch, lgsa, 3)
     if 2 in cfgs or 4 in cfgs:
         secondary["decode_cache_append"] = run_append(torch, lgsa, synth, to_dev, 50)
     if 3 in cfgs:
-        r3 = run_c3(torch, lgsa, synth, to_dev, 3)
+        r3 = run_c3(torch, lgsa, synth, to_dev, 20)
         sp_tf = r3["sparse_flops"] / (r3["sparse_ms"] * 1e-3) / 1e12
         ix_tf = r3["index_flops"] / (r3["index_ms"] * 1e-3) / 1e12
         secondary["c3_dsa_prefill"] = dict(
             sparse_gate_ms=round(r3["sparse_ms"], 3), sparse_gate_TFLOPs=round(sp_tf, 1),
             sparse_mfma_frac=round(sp_tf / PEAK_BF16_TFLOPS, 4),
             indexer_ms=round(r3["index_ms"], 3), indexer_TFLOPs=round(ix_tf, 1),
-            indexer_fp32_frac=round(ix_tf / PEAK_FP32_TFLOPS, 4))
+            indexer_fp32_frac=round(ix_tf / PEAK_FP32_TFLOPS, 4),
+            gather_probe=dict(ms=round(r3["gather_ms"], 3), bytes=r3["gather_bytes"],
+                              TBps=round(r3["gather_bytes"] / (r3["gather_ms"] * 1e-3) / 1e12,
+                                         2)),
+            oracle=r3["oracle"])
         bw_tf = r3["bwd_flops"] / (r3["bwd_ms"] * 1e-3) / 1e12
         secondary["sparse_bwd_prefill"] = dict(ms=round(r3["bwd_ms"], 3), TFLOPs=round(bw_tf, 1),
                                                mfma_frac=round(bw_tf / PEAK_BF16_TFLOPS, 4))
     if 3 in cfgs:
-        rc = run_csa(torch, lgsa, synth, to_dev, 3)
+        rc = run_csa(torch, lgsa, synth, to_dev, 20)
         tf = rc["flops"] / (rc["ms"] * 1e-3) / 1e12
         secondary["csa_prefill"] = dict(ms=round(rc["ms"], 3), TFLOPs=round(tf, 1))
     if 4 in cfgs:
-        r4 = run_c4(torch, lgsa, synth, to_dev, 30)
+        r4 = run_c4(torch, lgsa, synth, to_dev, 200)
         gbps = r4["bytes"] / (r4["ms"] * 1e-3) / 1e9
         igbps = r4["index_bytes"] / (r4["index_ms"] * 1e-3) / 1e9
         secondary["c4_mixed_decode"] = dict(ms=round(r4["ms"], 4), GBps=round(gbps, 1),
                                             hbm_frac=round(gbps / PEAK_HBM_GBPS, 4),
                                             indexer_ms=round(r4["index_ms"], 4),
-                                            indexer_GBps=round(igbps, 1), bytes=r4["bytes"])
+                                            indexer_GBps=round(igbps, 1), bytes=r4["bytes"],
+                                            oracle=r4["oracle"])
     line = dict(
         metric=METRIC, value=round(value, 2), unit="TFLOP/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=round(r1["ms_per_step"], 4), higher_is_better=True,

@@ -25,7 +25,7 @@ EXPORTS = ["lgsa_last_error", "hca_compress", "latent_gate", "hca_attn_fwd",
            "sparse_attn_fwd", "sparse_attn_fwd_workspace", "hca_cache_append",
            "dsa_cache_append", "vha_mix", "latent_gate_bwd", "latent_gate_bwd_workspace",
            "hca_attn_bwd", "hca_attn_bwd_workspace",
-           "sparse_attn_bwd", "sparse_attn_bwd_workspace"]
+           "sparse_attn_bwd", "sparse_attn_bwd_workspace", "sparse_gather_probe"]
 
 
 class LibraryMissing(RuntimeError):
@@ -113,6 +113,7 @@ def load():
             getattr(lib, name + "_workspace").argtypes = [ctypes.POINTER(st),
                                                           ctypes.POINTER(_SZ)]
         lib.hca_attn_fwd_static.argtypes = [ctypes.POINTER(HcaArgs), _P]
+        lib.sparse_gather_probe.argtypes = [_P, _LL, _I, _P, _I, _I, _P, _P]
         lib.vha_mix.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
         lib.latent_gate_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _SZ,
                                         _P]
@@ -536,3 +537,17 @@ def vha_mix(o, u, v, out=None, stream=None):
                         _dt(o), _stream(stream))
     _check("vha_mix", rc)
     return out
+
+
+def sparse_gather_probe(rows, idx, sums=None, stream=None):
+    """Measurement helper: the gathers of sparse_attn_fwd alone (see include/lgsa.h).
+    rows [S, stride] bf16; idx [n_lists, k] int32.  Returns sums [n_lists, 2] uint32 (as int32)."""
+    torch = _torch()
+    n_lists, k = idx.shape
+    if sums is None:
+        sums = torch.empty((n_lists, 2), dtype=torch.int32, device=idx.device)
+    _check("sparse_gather_probe",
+           load().sparse_gather_probe(_dev(rows, "rows"), rows.shape[-1], rows.shape[0],
+                                      _dev(idx, "idx"), n_lists, k, _dev(sums, "sums"),
+                                      _stream(stream)))
+    return sums

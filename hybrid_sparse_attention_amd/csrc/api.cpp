@@ -629,4 +629,21 @@ lgsa_status sparse_attn_fwd(const lgsa_sparse_args* a, void* stream) {
   return hip_status(lgsa::launch_sparse(p, (hipStream_t)stream), "sparse_attn_fwd");
 }
 
+lgsa_status sparse_gather_probe(const void* rows, long long row_stride, int S,
+                                const int32_t* idx, int n_lists, int k, uint32_t* sums,
+                                void* stream) {
+  REQUIRE(rows && idx && sums, LGSA_EINVAL,
+          "sparse_gather_probe: rows, idx and sums must be non-NULL");
+  REQUIRE(S >= 1 && n_lists >= 0 && k >= 1, LGSA_EINVAL,
+          "sparse_gather_probe: S, k must be >= 1 and n_lists >= 0");
+  REQUIRE(row_stride >= 256 && row_stride % 8 == 0, LGSA_EUNSUPPORTED,
+          "sparse_gather_probe: row_stride must be >= 256 and a multiple of 8 (got %lld)",
+          row_stride);
+  REQUIRE(aligned(rows, 16) && aligned(idx, 4) && aligned(sums, 4), LGSA_EINVAL,
+          "sparse_gather_probe: rows must be 16-byte aligned, idx and sums 4-byte aligned");
+  return hip_status(lgsa::launch_gather_probe(rows, row_stride, S, idx, n_lists, k, sums,
+                                              (hipStream_t)stream),
+                    "sparse_gather_probe");
+}
+
 }  // extern "C"

@@ -540,10 +540,10 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_gated_kernel(HcaParams p) 
   rp.window = p.window;
   rp.block = p.block;
   const int tw_lo = pos + r_first, tw_hi = pos + r_first + n_valid - 1;
-  // the lane's row; rows past the end read the last row and are never stored
-  const int i_row = min(r_first + l16, i_end - 1);
   Frag8 qf[16];
   {
+    // rows past the end read the last row and are never stored
+    const int i_row = min(r_first + l16, i_end - 1);
     const uint16_t* qr = (const uint16_t*)p.q + (((size_t)b * p.Tq + i_row) * p.H + h) * D;
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) qf[kk].u = *(const uint4*)(qr + 32 * kk + 8 * g);
@@ -627,10 +627,11 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_gated_kernel(HcaParams p) 
     }
   }
   lds_barrier();
-  // out = O * sigmoid(G) for the wave's own rows, in the layout of O
-  if (i < i_end) {
-    const char* srow = sbuf(wave >> 1) + (16 * (wave & 1) + l16) * VLD + 8 * g;
-    uint16_t* orow = (uint16_t*)p.out + (((size_t)b * p.Tq + i) * p.H + h) * D;
+  // out = O * sigmoid(G) for the wave's own rows, in the layout of O, written over the gate
+  // factors it replaces; then the wave stores its 16 rows whole, 1 KiB per instruction
+  char* tile = sbuf(wave >> 1) + 16 * (wave & 1) * VLD;
+  {
+    char* srow = tile + l16 * VLD + 8 * g;
 #pragma unroll
     for (int cb = 0; cb < 32; ++cb) {
       const uint2 sg = *(const uint2*)(srow + 32 * cb);
@@ -639,9 +640,15 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_gated_kernel(HcaParams p) 
       uint2 r;
       r.x = pack_bf16x2(o0 * __uint_as_float(sg.x << 16), o1 * __uint_as_float(sg.x & 0xFFFF0000u));
       r.y = pack_bf16x2(o2 * __uint_as_float(sg.y << 16), o3 * __uint_as_float(sg.y & 0xFFFF0000u));
-      *(uint2*)(orow + 16 * cb + 4 * g) = r;
+      *(uint2*)(srow + 32 * cb) = r;
     }
   }
+  char* orow0 = (char*)p.out + (((size_t)b * p.Tq + r_first) * p.H + h) * ROWB + 16 * lane;
+  const size_t ldo = (size_t)p.H * ROWB;
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr)
+    if (r_first + rr < i_end)
+      *(uint4*)(orow0 + rr * ldo) = *(const uint4*)(tile + rr * VLD + 16 * lane);
 }
 
 // ------------------------------------------------------------------------------- decode

@@ -128,6 +128,9 @@ struct SparseParams {
 };
 
 size_t sparse_workspace(const SparseParams& p);
+// Measurement helper: the gathers of sparse attention alone (one checksum pair per list).
+hipError_t launch_gather_probe(const void* rows, long long stride, int S, const int32_t* idx,
+                               int n_lists, int k, uint32_t* sums, hipStream_t stream);
 hipError_t launch_sparse(const SparseParams& p, hipStream_t stream);
 
 struct SparseBwdParams {

@@ -327,3 +327,57 @@ hipError_t launch_sparse(const SparseParams& p, hipStream_t stream) {
 }
 
 }  // namespace lgsa
+
+// ------------------------------------------------------------------ gather probe (measurement)
+namespace lgsa {
+namespace {
+
+using namespace sparse_tile;
+
+// The gathers of sparse_kernel<true> alone: one workgroup of two waves per index list, tiles of
+// 32 listed rows brought to LDS by the same DMA pattern and double buffering.  So that the
+// transfers are used, wave w adds up the first 64 words of tile row 16 w of every tile (rows 0
+// and 16 are stored unswizzled), uint32 with wrap-around: sums[list][w].
+__global__ __launch_bounds__(128) void gather_probe_kernel(const uint16_t* __restrict__ rows,
+                                                           long long stride, int S,
+                                                           const int32_t* __restrict__ idx,
+                                                           int k, uint32_t* __restrict__ sums) {
+  __shared__ __attribute__((aligned(1024))) char t0[TILE];
+  __shared__ __attribute__((aligned(1024))) char t1[TILE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t* list = idx + (size_t)blockIdx.x * k;
+  const int n_tiles = (k + KT - 1) / KT;
+  uint32_t sum = 0;
+  if (n_tiles > 0) gather_tile<2>(rows, stride, valid_ix(load_ix(list, 0, k, lane), S), t0, wave, lane);
+  int ix_nxt = load_ix(list, KT, k, lane);
+  wait_all();
+  __syncthreads();
+  auto body = [&](int ti, const char* cur, char* nxt) {
+    if (ti + 1 < n_tiles) gather_tile<2>(rows, stride, valid_ix(ix_nxt, S), nxt, wave, lane);
+    const int ix_after = load_ix(list, KT * (ti + 2), k, lane);
+    sum += *(const uint32_t*)(cur + 16 * wave * TROW + 4 * lane);
+    wait_all();
+    __syncthreads();
+    ix_nxt = ix_after;
+  };
+  for (int ti = 0; ti < n_tiles; ti += 2) {
+    body(ti, t0, t1);
+    if (ti + 1 < n_tiles) body(ti + 1, t1, t0);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  if (lane == 0) sums[(size_t)blockIdx.x * 2 + wave] = sum;
+}
+
+}  // namespace
+
+hipError_t launch_gather_probe(const void* rows, long long stride, int S, const int32_t* idx,
+                               int n_lists, int k, uint32_t* sums, hipStream_t stream) {
+  if (n_lists == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_probe_kernel, dim3((unsigned)n_lists), dim3(128), 0, stream,
+                     (const uint16_t*)rows, stride, S, idx, k, sums);
+  return hipGetLastError();
+}
+
+}  // namespace lgsa

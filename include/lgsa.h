@@ -399,6 +399,23 @@ typedef struct {
  * row and kv_row_stride multiples of 8 (bf16) or 4 (f32); every tensor 16-byte aligned. */
 lgsa_status dsa_cache_append(const lgsa_dsa_append_args* a, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * sparse_gather_probe -- measurement helper, not a step of the method: the gathers of
+ * sparse_attn_fwd alone (its DMA pattern, tiles of 32 listed rows double buffered in LDS, one
+ * workgroup per list), with no arithmetic, so that the rate at which listed 512-byte latent
+ * rows can be gathered (the bound of sparse attention's data movement) can be timed.
+ *   rows [S, row_stride] bf16 (the first 256 elements of a row are gathered); idx [n_lists, k]
+ *   int32 (entries < 0 or >= S, and slots past k in the last tile, read row 0); sums
+ *   [n_lists, 2] uint32, written so that the transfers are used: sums[l][w] adds up, with
+ *   wrap-around, the first 64 32-bit words of the row listed in slot 32 t + 16 w of every
+ *   tile t of list l.
+ * Errors: LGSA_EINVAL for NULL or misaligned pointers and bad sizes, LGSA_EUNSUPPORTED for a
+ * row stride below 256 or not a multiple of 8.
+ * --------------------------------------------------------------------------------------- */
+lgsa_status sparse_gather_probe(const void* rows, long long row_stride, int S,
+                                const int32_t* idx, int n_lists, int k, uint32_t* sums,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -149,6 +149,15 @@ def test_hca_static_scratch_limit(lib):
     assert _call(lib, "hca_attn_fwd_static", _hca(q=FAKE_ODD)) == lgsa.LGSA_EINVAL
 
 
+def test_gather_probe_validation(lib):
+    f = lib.sparse_gather_probe
+    assert f(None, 256, 10, FAKE, 4, 32, FAKE, None) == lgsa.LGSA_EINVAL
+    assert f(FAKE, 256, 0, FAKE, 4, 32, FAKE, None) == lgsa.LGSA_EINVAL
+    assert f(FAKE, 200, 10, FAKE, 4, 32, FAKE, None) == lgsa.LGSA_EUNSUPPORTED
+    assert f(FAKE_ODD, 256, 10, FAKE, 4, 32, FAKE, None) == lgsa.LGSA_EINVAL
+    assert "aligned" in lgsa.last_error()
+
+
 def _idx(**kw):
     a = lgsa.IndexArgs()
     vals = dict(B=1, Tq=4096, S=4096, Hi=4, di=64, k=2048, q_idx=FAKE, w_idx=FAKE, k_idx=FAKE,

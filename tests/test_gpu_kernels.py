@@ -364,3 +364,26 @@ def test_sparse_empty_rows_are_zero(torch):
     torch.cuda.synchronize()
     o = from_dev(out)
     assert np.all(o[0, 0] == 0) and np.all(o[0, 2] == 0) and np.any(o[0, 1] != 0)
+
+
+def test_gather_probe_checksums(torch):
+    """The measurement helper gathers what the lists name: its checksums (first 64 words of
+    the row in slot 32t + 16w of every tile) match a host recomputation, for lists with
+    skipped and out-of-range entries and a ragged last tile."""
+    S, n_lists, k = 3000, 37, 100
+    rng = np.random.default_rng(71)
+    rows = rng.integers(0, 2 ** 16, size=(S, 264), dtype=np.uint16)  # stride 264 elements
+    idx = rng.integers(-5, S + 5, size=(n_lists, k)).astype(np.int32)
+    got = lgsa.sparse_gather_probe(to_dev(rows), to_dev(idx))
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().view(np.uint32)
+    words = rows[:, :128].copy().view(np.uint32)  # [S, 64]
+    want = np.zeros((n_lists, 2), np.uint64)
+    for l in range(n_lists):
+        for t in range((k + 31) // 32):
+            for w in range(2):
+                j = 32 * t + 16 * w
+                s = int(idx[l, j]) if j < k else -1
+                s = s if 0 <= s < S else 0
+                want[l, w] += int(words[s].astype(np.uint64).sum())
+    assert np.array_equal(got.astype(np.uint64), want % (1 << 32))
