@@ -305,6 +305,25 @@ def run_c3(torch, lgsa, synth, to_dev, iters):
         torch.cuda.synchronize()
         idx_ms.append(e[0].elapsed_time(e[1]))
         sp_ms.append(e[1].elapsed_time(e[2]))
+
+    # the same gated sparse attention followed by the head mix (VHA, rank 16), fused into its
+    # epilogue (the gate factors computed first)
+    vu = to_dev(synth.normal(62, (H, 16), 0.02, True))
+    vv = to_dev(synth.normal(63, (H, 16), 0.02, True))
+
+    def mixed():
+        lgsa.sparse_attn_fwd(ds["q"], ds["kv_lat"], idx, q_lat=ds["q_lat"], w_gate=ds["w_gate"],
+                             out=out, vha_u=vu, vha_v=vv)
+
+    mixed()
+    torch.cuda.synchronize()
+    mix_ms = []
+    for _ in range(iters):
+        a = tm.event()
+        mixed()
+        b = tm.event()
+        torch.cuda.synchronize()
+        mix_ms.append(a.elapsed_time(b))
     pairs = int(sum(min(k, t + 1) for t in range(T)))
     sp_flops = 4.0 * d * pairs * H + 2.0 * T * 1024 * H * d
     ind_pairs = T * (T + 1) // 2
@@ -376,7 +395,8 @@ def run_c3(torch, lgsa, synth, to_dev, iters):
     return dict(index_ms=float(np.median(idx_ms)), sparse_ms=float(np.median(sp_ms)),
                 sparse_flops=sp_flops, index_flops=float(ind_flops),
                 bwd_ms=float(np.median(bwd_ms)), bwd_flops=10.0 * d * pairs * H,
-                gather_ms=float(np.median(g_ms)), gather_bytes=gathered, oracle=orec)
+                gather_ms=float(np.median(g_ms)), gather_bytes=gathered, oracle=orec,
+                sparse_vha_ms=float(np.median(mix_ms)))
 
 
 def run_csa(torch, lgsa, synth, to_dev, iters):
@@ -747,6 +767,7 @@ def main():
             sparse_mfma_frac=round(sp_tf / PEAK_BF16_TFLOPS, 4),
             indexer_ms=round(r3["index_ms"], 3), indexer_TFLOPs=round(ix_tf, 1),
             indexer_fp32_frac=round(ix_tf / PEAK_FP32_TFLOPS, 4),
+            sparse_gate_vha_ms=round(r3["sparse_vha_ms"], 3),
             gather_probe=dict(ms=round(r3["gather_ms"], 3), bytes=r3["gather_bytes"],
                               TBps=round(r3["gather_bytes"] / (r3["gather_ms"] * 1e-3) / 1e12,
                                          2)),

@@ -47,7 +47,8 @@ class HcaArgs(ctypes.Structure):
                 ("pos0", _P), ("max_pos", _I), ("k_win", _P), ("v_win", _P),
                 ("win_len", _I), ("window", _I), ("kc", _P), ("vc", _P), ("n_cap", _I),
                 ("block", _I), ("scale", _F), ("q_lat", _P), ("w_gate", _P), ("d_lat", _I),
-                ("out", _P), ("workspace", _P), ("workspace_bytes", _SZ), ("lse", _P)]
+                ("out", _P), ("workspace", _P), ("workspace_bytes", _SZ), ("lse", _P),
+                ("vha_u", _P), ("vha_v", _P), ("vha_rank", _I)]
 
 
 class HcaBwdArgs(ctypes.Structure):
@@ -68,7 +69,8 @@ class SparseArgs(ctypes.Structure):
                 ("S", _I), ("k", _I), ("q", _P), ("k_lat", _P), ("k_row_stride", _LL),
                 ("v_lat", _P), ("v_row_stride", _LL), ("idx", _P), ("scale", _F),
                 ("q_lat", _P), ("w_gate", _P), ("d_lat", _I), ("out", _P),
-                ("workspace", _P), ("workspace_bytes", _SZ), ("lse", _P)]
+                ("workspace", _P), ("workspace_bytes", _SZ), ("lse", _P),
+                ("vha_u", _P), ("vha_v", _P), ("vha_rank", _I)]
 
 
 class SparseBwdArgs(ctypes.Structure):
@@ -229,15 +231,17 @@ def hca_args(q, pos0, k_win, v_win, kc=None, vc=None, *, max_pos, window=128, bl
 
 def hca_attn_fwd(q, pos0, k_win, v_win, kc=None, vc=None, *, max_pos, window=128, block=128,
                  scale=None, q_lat=None, w_gate=None, out=None, workspace=None, stream=None,
-                 lse=None):
-    """Heavily Compressed Attention forward (optionally gated); see include/lgsa.h.  lse: an
-    optional [B, Tq, H] fp32 tensor receiving each row's log-sum-exp (for hca_attn_bwd)."""
+                 lse=None, vha_u=None, vha_v=None):
+    """Heavily Compressed Attention forward (optionally gated, then optionally mixed across
+    heads by VHA with factors vha_u, vha_v [H, r]); see include/lgsa.h.  lse: an optional
+    [B, Tq, H] fp32 tensor receiving each row's log-sum-exp (for hca_attn_bwd)."""
     torch = _torch()
     if out is None:
         out = torch.empty_like(q)
     a = hca_args(q, pos0, k_win, v_win, kc, vc, max_pos=max_pos, window=window, block=block,
                  scale=scale, q_lat=q_lat, w_gate=w_gate, out=out)
     a.lse = _dev(lse, "lse")
+    _set_vha(a, vha_u, vha_v)
     need = hca_attn_fwd_workspace(a)
     if workspace is None:
         workspace, _ = _workspace(need, q.device)
@@ -336,10 +340,17 @@ def sparse_attn_fwd_workspace(a) -> int:
     return n.value
 
 
+def _set_vha(a, vha_u, vha_v):
+    """The optional head mix (VHA) factors [H, r] of an attention call."""
+    a.vha_u, a.vha_v = _dev(vha_u, "vha_u"), _dev(vha_v, "vha_v")
+    a.vha_rank = 0 if vha_u is None else vha_u.shape[-1]
+
+
 def sparse_attn_fwd(q, k_lat, idx, v_lat=None, *, scale=None, q_lat=None, w_gate=None,
-                    out=None, lse=None, workspace=None, stream=None):
-    """DSA sparse core attention over the latent rows listed in idx (optionally gated); lse
-    [B,Tq,H] fp32, when given, receives each row's log-sum-exp for sparse_attn_bwd."""
+                    out=None, lse=None, workspace=None, stream=None, vha_u=None, vha_v=None):
+    """DSA sparse core attention over the latent rows listed in idx (optionally gated, then
+    optionally mixed across heads by VHA with factors vha_u, vha_v [H, r]); lse [B,Tq,H] fp32,
+    when given, receives each row's log-sum-exp for sparse_attn_bwd."""
     torch = _torch()
     B, Tq, H, _ = q.shape
     dv = (k_lat if v_lat is None else v_lat).shape[-1]
@@ -347,6 +358,7 @@ def sparse_attn_fwd(q, k_lat, idx, v_lat=None, *, scale=None, q_lat=None, w_gate
         out = torch.empty((B, Tq, H, dv), dtype=q.dtype, device=q.device)
     a = sparse_args(q, k_lat, idx, v_lat, scale=scale, q_lat=q_lat, w_gate=w_gate, out=out)
     a.lse = _dev(lse, "lse")
+    _set_vha(a, vha_u, vha_v)
     if workspace is None:
         workspace, _ = _workspace(sparse_attn_fwd_workspace(a), q.device)
     a.workspace = None if workspace is None else workspace.data_ptr()

@@ -67,7 +67,26 @@ lgsa::HcaParams to_params(const lgsa_hca_args* a) {
   p.lse = a->lse;
   p.ws = a->workspace;
   p.ws_bytes = a->workspace_bytes;
+  p.vha_u = a->vha_u;
+  p.vha_v = a->vha_v;
+  p.vha_r = a->vha_rank;
   return p;
+}
+
+// The optional head mix (VHA) of an attention call: rank 0 turns it off; otherwise both
+// factors [H, rank] in the call's dtype, rank <= 16, and 64 heads on the bfloat16 path.
+lgsa_status check_vha(const char* who, int dt, int H, const void* u, const void* v, int rank) {
+  REQUIRE(rank >= 0 && rank <= 16, LGSA_EUNSUPPORTED, "%s: vha_rank must be in 0..16 (got %d)",
+          who, rank);
+  if (rank == 0) return LGSA_OK;
+  REQUIRE(u != nullptr && v != nullptr, LGSA_EINVAL,
+          "%s: vha_u and vha_v must be non-NULL when vha_rank > 0", who);
+  REQUIRE(dt != LGSA_BF16 || H == 64, LGSA_EUNSUPPORTED,
+          "%s: the bf16 head mix needs H == 64 (got %d)", who, H);
+  const uintptr_t al = dt == LGSA_BF16 ? 2 : 4;
+  REQUIRE(aligned(u, al) && aligned(v, al), LGSA_EINVAL,
+          "%s: vha_u and vha_v must be aligned to their element size", who);
+  return LGSA_OK;
 }
 
 lgsa_status check_hca(const lgsa_hca_args* a) {
@@ -116,7 +135,7 @@ lgsa_status check_hca(const lgsa_hca_args* a) {
     for (const void* p : ptrs)
       REQUIRE(aligned(p, 16), LGSA_EINVAL, "hca_attn_fwd: tensors must be 16-byte aligned");
   }
-  return LGSA_OK;
+  return check_vha("hca_attn_fwd", a->dt, a->H, a->vha_u, a->vha_v, a->vha_rank);
 }
 
 size_t hca_ws(const lgsa_hca_args* a) {
@@ -189,6 +208,9 @@ lgsa::SparseParams to_params(const lgsa_sparse_args* a) {
   p.ws = a->workspace;
   p.ws_bytes = a->workspace_bytes;
   p.lse = a->lse;
+  p.vha_u = a->vha_u;
+  p.vha_v = a->vha_v;
+  p.vha_r = a->vha_rank;
   return p;
 }
 
@@ -219,7 +241,7 @@ lgsa_status check_sparse(const lgsa_sparse_args* a) {
   const void* ptrs[] = {a->q, a->k_lat, a->v_lat, a->q_lat, a->w_gate, a->out};
   for (const void* p : ptrs)
     REQUIRE(aligned(p, 16), LGSA_EINVAL, "sparse_attn_fwd: tensors must be 16-byte aligned");
-  return LGSA_OK;
+  return check_vha("sparse_attn_fwd", a->dt, a->H, a->vha_u, a->vha_v, a->vha_rank);
 }
 
 lgsa_status check_workspace(const char* name, const void* ws, size_t have, size_t need) {

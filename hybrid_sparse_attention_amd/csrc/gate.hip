@@ -15,6 +15,9 @@
 //     8 bytes.
 //
 // float32 path: a plain tiled FMA GEMM (used for the small fp32 configuration).
+//
+// With o == NULL the bfloat16 kernels write the gate factors sigmoid(q_lat W) themselves (the
+// attention kernels that apply the gate in their own epilogue read them from there).
 #include "common.h"
 #include "kernels.h"
 
@@ -23,6 +26,8 @@ namespace lgsa {
 namespace {
 
 constexpr int GT_N = 128, GT_M = 128, GT_K = 64, GT_LD = GT_K + 8;  // LDS row: 72 bf16
+// two bfloat16 ones: the factor o takes when the gate alone is asked for (o == NULL)
+constexpr uint32_t BF16_ONES = 0x3F803F80u;
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -135,7 +140,7 @@ __global__ __launch_bounds__(256) void gate_bf16_kernel(const uint16_t* __restri
       const int n = n0 + wn + 16 * i + 4 * g;
       if (n >= N) continue;
       const size_t off = (size_t)m * N + n;
-      const uint2 ov = *(const uint2*)(o + off);
+      const uint2 ov = o != nullptr ? *(const uint2*)(o + off) : make_uint2(BF16_ONES, BF16_ONES);
       const float o0 = __uint_as_float(ov.x << 16), o1 = __uint_as_float(ov.x & 0xFFFF0000u);
       const float o2 = __uint_as_float(ov.y << 16), o3 = __uint_as_float(ov.y & 0xFFFF0000u);
       if constexpr (BWD) {
@@ -376,7 +381,8 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_big_kernel(const uint16_t* _
     for (int u = 0; u < 8; ++u) {
       int blk, rr, m, n;
       chunk_mn(hl, u, blk, rr, m, n);
-      ov[hl][u] = load16_nt(o + (size_t)min(m, M - 1) * N + min(n, N - 8));
+      ov[hl][u] = o != nullptr ? load16_nt(o + (size_t)min(m, M - 1) * N + min(n, N - 8))
+                               : make_uint4(BF16_ONES, BF16_ONES, BF16_ONES, BF16_ONES);
     }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -533,7 +539,7 @@ __global__ __launch_bounds__(256) void gate_bf16_skinny_kernel(const uint16_t* _
     const int n = n0 + 16 * cb + 4 * g;
     if (n >= N) continue;
     const size_t off = (size_t)qr * N + n;
-    const uint2 x = *(const uint2*)(o + off);
+    const uint2 x = o != nullptr ? *(const uint2*)(o + off) : make_uint2(BF16_ONES, BF16_ONES);
     uint2 r;
     r.x = pack_bf16x2(__uint_as_float(x.x << 16) * sigmoidf_fast(acc[cb][0]),
                       __uint_as_float(x.x & 0xFFFF0000u) * sigmoidf_fast(acc[cb][1]));

@@ -1168,19 +1168,27 @@ hipError_t launch_hca_bf16(const HcaParams& p, hipStream_t stream) {
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
+    if (p.q_lat != nullptr) {  // the gate GEMM multiplies sigmoid(q_lat W) into O in place
+      e = launch_gate(p.q_lat, p.w_gate, p.out, p.out, p.B * p.Tq, p.d_lat, p.H * D, DT_BF16,
+                      stream);
+      if (e != hipSuccess) return e;
+    }
   } else if (p.q_lat != nullptr) {  // the gate in the attention epilogue
     const long long grid = (long long)p.B * ((p.Tq + FQ - 1) / FQ) * p.H;
     hipLaunchKernelGGL(hca_prefill_gated_kernel, dim3((unsigned)grid), dim3(512), 0, stream, p);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   } else {
     const long long grid = (long long)p.B * ((p.Tq + 31) / 32) * ((p.H + 3) / 4);
     hipLaunchKernelGGL(hca_prefill_kernel, dim3((unsigned)grid), dim3(512), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (p.q_lat != nullptr)  // the gate GEMM multiplies sigmoid(q_lat W) into O in place
-    return launch_gate(p.q_lat, p.w_gate, p.out, p.out, p.B * p.Tq, p.d_lat, p.H * D, DT_BF16,
-                       stream);
+  // the head mix (VHA) of the gated output: a workgroup of these kernels holds one head of a
+  // token tile (prefill) or splits the keys (decode), so the mix runs as its own pass in place
+  if (p.vha_r > 0)
+    return launch_vha(p.out, p.vha_u, p.vha_v, p.out, p.B * p.Tq, p.H, D, p.vha_r, DT_BF16,
+                      stream);
   return hipSuccess;
 }
 

@@ -111,9 +111,16 @@ hipError_t launch_hca_f32(const HcaParams& p, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(hca_f32_kernel, dim3((unsigned)rows), dim3(NT), 0, stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.q_lat == nullptr) return e;
-  return launch_gate(p.q_lat, p.w_gate, p.out, p.out, (int)rows, p.d_lat, p.H * p.d, DT_F32,
-                     stream);
+  if (e != hipSuccess) return e;
+  if (p.q_lat != nullptr) {
+    e = launch_gate(p.q_lat, p.w_gate, p.out, p.out, (int)rows, p.d_lat, p.H * p.d, DT_F32,
+                    stream);
+    if (e != hipSuccess) return e;
+  }
+  if (p.vha_r > 0)  // the head mix of the gated output, in place
+    return launch_vha(p.out, p.vha_u, p.vha_v, p.out, (int)rows, p.H, p.d, p.vha_r, DT_F32,
+                      stream);
+  return hipSuccess;
 }
 
 }  // namespace lgsa

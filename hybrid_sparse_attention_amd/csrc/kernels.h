@@ -35,6 +35,7 @@ hipError_t launch_gate_bwd_elem(const void* q_lat, const void* w, const void* o,
 hipError_t launch_gemm(const void* a, long long lda, bool a_kmajor, const void* b,
                        long long ldb, bool b_kmajor, void* c, long long ldc, int M, int N, int K,
                        int dt, hipStream_t stream);
+// bfloat16 with o == NULL: out = sigmoid(q_lat w), the gate factors alone.
 hipError_t launch_gate(const void* q_lat, const void* w, const void* o, void* out, int M,
                        int d_lat, int N, int dt, hipStream_t stream);
 
@@ -57,6 +58,9 @@ struct HcaParams {
   void* ws;
   size_t ws_bytes;
   float* lse;  // optional per-row log-sum-exp of the scaled logits (prefill kernel only)
+  const void* vha_u;  // Virtual Head Attention factors [H, vha_r], applied to the gated output
+  const void* vha_v;
+  int vha_r;          // 0: no mixing
 };
 
 // Backward of HCA in prefill (every sequence from position 0, T query rows = T positions):
@@ -125,6 +129,9 @@ struct SparseParams {
   void* ws;
   size_t ws_bytes;
   float* lse;
+  const void* vha_u;  // Virtual Head Attention factors [H, vha_r], applied to the gated output
+  const void* vha_v;
+  int vha_r;          // 0: no mixing
 };
 
 size_t sparse_workspace(const SparseParams& p);

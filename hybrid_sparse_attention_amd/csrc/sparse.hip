@@ -21,6 +21,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "sparse_tile.h"
+#include "vha_tile.h"
 
 namespace lgsa {
 
@@ -36,6 +37,10 @@ constexpr float NEG_BIG = -1.0e30f;     // masked logit (finite: no inf - inf)
 // of 16 heads when a second (value) tile is gathered beside it (its LDS then allows two
 // workgroups per CU, and four waves keep eight waves on the CU).
 template <bool ALIAS> constexpr int waves_of() { return ALIAS ? 2 : 4; }
+// The key tiles double as the staging area of the epilogue's head mix: 64 head rows of 256
+// bfloat16 channels, 32 to a tile, rows padded to 544 bytes (conflict-free transposing reads).
+constexpr int MIX_ROW = 544;
+constexpr int KTILE_BYTES = TILE > 32 * MIX_ROW ? TILE : 32 * MIX_ROW;
 
 template <int NHB>
 struct WaveState {
@@ -135,8 +140,8 @@ __global__ __launch_bounds__(64 * waves_of<ALIAS>()) __attribute__((amdgpu_waves
 void sparse_kernel(SparseParams p, int n_split, int chunk, float* part_o, float* part_ml) {
   constexpr int NW = waves_of<ALIAS>();
   constexpr int NHB = 64 / (16 * NW);  // 16-head blocks per wave
-  __shared__ __attribute__((aligned(1024))) char kt0[TILE];
-  __shared__ __attribute__((aligned(1024))) char kt1[TILE];
+  __shared__ __attribute__((aligned(1024))) char kt0[KTILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kt1[KTILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vt0[ALIAS ? 16 : TILE];
   __shared__ __attribute__((aligned(1024))) char vt1[ALIAS ? 16 : TILE];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -216,6 +221,14 @@ void sparse_kernel(SparseParams p, int n_split, int chunk, float* part_o, float*
     if (ti + 1 < n_tiles) body(ti + 1, kt1, vt1, kt0, vt0);
   }
 
+  // Epilogue.  When p.q_lat is set (the launcher passes it only with the head mix), out
+  // already holds the gate factors sigmoid(q_lat W) of this row (written by the gate GEMM
+  // before this kernel): the output is O * sigmoid(G).  With the head mix (VHA) that gated
+  // output of all 64 heads is staged in the key tiles (the last barrier of the key loop has
+  // freed them), mixed across heads in place and stored row by row.
+  const bool gated = p.q_lat != nullptr;
+  const bool mix = n_split == 1 && p.vha_r > 0;
+  auto mrow = [&](int hl) -> char* { return (hl < 32 ? kt0 : kt1) + (hl & 31) * MIX_ROW; };
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     const int h = h0 + 16 * hb;
@@ -225,7 +238,20 @@ void sparse_kernel(SparseParams p, int n_split, int chunk, float* part_o, float*
       const float inv = (seen && lt > 0.f) ? 1.f / lt : 0.f;
       uint16_t* orow = (uint16_t*)p.out + ((size_t)r * p.H + h) * D;
 #pragma unroll
-      for (int cb = 0; cb < 16; ++cb) store4(orow + 16 * cb + 4 * g, st.o[hb][cb] * inv);
+      for (int cb = 0; cb < 16; ++cb) {
+        f32x4_t v = st.o[hb][cb] * inv;
+        if (gated) {
+          const uint2 sg = *(const uint2*)(orow + 16 * cb + 4 * g);
+          v[0] *= __uint_as_float(sg.x << 16);
+          v[1] *= __uint_as_float(sg.x & 0xFFFF0000u);
+          v[2] *= __uint_as_float(sg.y << 16);
+          v[3] *= __uint_as_float(sg.y & 0xFFFF0000u);
+        }
+        if (mix)
+          store4((uint16_t*)(mrow(h - hg * 64) + (16 * cb + 4 * g) * 2), v);
+        else
+          store4(orow + 16 * cb + 4 * g, v);
+      }
       if (p.lse != nullptr && g == 0)
         p.lse[(size_t)r * p.H + h] = inv > 0.f ? (st.m[hb] + __log2f(lt)) * LN2 : -INFINITY;
       continue;
@@ -241,13 +267,28 @@ void sparse_kernel(SparseParams p, int n_split, int chunk, float* part_o, float*
       part_ml[pr * 2 + 1] = seen ? lt : 0.f;
     }
   }
+  if (mix) {
+    vha_tile::Factors f;
+    vha_tile::load_factors(f, (const uint16_t*)p.vha_u, (const uint16_t*)p.vha_v, p.vha_r,
+                           lane);
+    __syncthreads();
+    vha_tile::mix_blocks(mrow, f, (16 / NW) * wave, 16 / NW, lane);
+    __syncthreads();
+    // 64 rows of 512 bytes leave as 16-byte chunks
+    uint16_t* out0 = (uint16_t*)p.out + ((size_t)r * p.H + hg * 64) * D;
+    for (int c = tid; c < 64 * 32; c += 64 * NW)
+      *(uint4*)(out0 + (size_t)(c >> 5) * D + 8 * (c & 31)) =
+          *(const uint4*)(mrow(c >> 5) + 16 * (c & 31));
+  }
 }
 
+// gated: out holds this row's gate factors (written before the attention kernel), which
+// multiply the merged O.
 __global__ __launch_bounds__(64) void sparse_combine_kernel(const float* __restrict__ part_o,
                                                             const float* __restrict__ part_ml,
                                                             uint16_t* __restrict__ out,
                                                             float* __restrict__ lse, int H,
-                                                            int n_split) {
+                                                            int n_split, bool gated) {
   const int rh = blockIdx.x;  // r * H + h
   const int r = rh / H, h = rh % H;
   float mt = -INFINITY;
@@ -267,10 +308,19 @@ __global__ __launch_bounds__(64) void sparse_combine_kernel(const float* __restr
   }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (lse != nullptr && threadIdx.x == 0) lse[rh] = lt > 0.f ? (mt + __log2f(lt)) * LN2 : -INFINITY;
+  float f[4] = {inv, inv, inv, inv};
+  uint2* dst = (uint2*)(out + (size_t)rh * D + 4 * threadIdx.x);
+  if (gated) {
+    const uint2 sg = *dst;
+    f[0] *= __uint_as_float(sg.x << 16);
+    f[1] *= __uint_as_float(sg.x & 0xFFFF0000u);
+    f[2] *= __uint_as_float(sg.y << 16);
+    f[3] *= __uint_as_float(sg.y & 0xFFFF0000u);
+  }
   uint2 o;
-  o.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  o.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-  *(uint2*)(out + (size_t)rh * D + 4 * threadIdx.x) = o;
+  o.x = pack_bf16x2(acc[0] * f[0], acc[1] * f[1]);
+  o.y = pack_bf16x2(acc[2] * f[2], acc[3] * f[3]);
+  *dst = o;
 }
 
 // Enough workgroups to fill the chip before a list is split, but at least four tiles per
@@ -304,25 +354,44 @@ hipError_t launch_sparse(const SparseParams& p, hipStream_t stream) {
   sparse_plan(p, n_split, chunk);
   float* part_o = (float*)p.ws;
   float* part_ml = part_o ? part_o + (size_t)rows * n_split * p.H * D : nullptr;
+  hipError_t e;
+  // With the head mix the gate must precede it inside the epilogue: the gate factors are
+  // computed first, into out, where the epilogue reads them.  Without it the gate GEMM rescales
+  // the attention output in place afterwards (the same bytes moved, measured 3% faster at the
+  // DSA prefill shape).
+  const bool gate_first = p.q_lat != nullptr && p.vha_r > 0;
+  SparseParams pk = p;
+  if (!gate_first) pk.q_lat = nullptr;  // the kernels read no gate factors
+  if (gate_first) {
+    e = launch_gate(p.q_lat, p.w_gate, nullptr, p.out, (int)rows, p.d_lat, p.H * D, DT_BF16,
+                    stream);
+    if (e != hipSuccess) return e;
+  }
   const long long grid = rows * (p.H / 64) * n_split;
   const bool alias = p.v_lat == p.k_lat && p.v_stride == p.k_stride;
   if (alias)
     hipLaunchKernelGGL(sparse_kernel<true>, dim3((unsigned)grid), dim3(64 * waves_of<true>()), 0,
-                       stream, p, n_split, chunk, part_o, part_ml);
+                       stream, pk, n_split, chunk, part_o, part_ml);
   else
     hipLaunchKernelGGL(sparse_kernel<false>, dim3((unsigned)grid), dim3(64 * waves_of<false>()), 0,
-                       stream, p, n_split, chunk, part_o, part_ml);
-  hipError_t e = hipGetLastError();
+                       stream, pk, n_split, chunk, part_o, part_ml);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (n_split > 1) {
     hipLaunchKernelGGL(sparse_combine_kernel, dim3((unsigned)(rows * p.H)), dim3(64), 0, stream,
-                       part_o, part_ml, (uint16_t*)p.out, p.lse, p.H, n_split);
+                       part_o, part_ml, (uint16_t*)p.out, p.lse, p.H, n_split, gate_first);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (p.q_lat != nullptr)
-    return launch_gate(p.q_lat, p.w_gate, p.out, p.out, (int)rows, p.d_lat, p.H * D, DT_BF16,
-                       stream);
+  if (p.q_lat != nullptr && !gate_first) {
+    e = launch_gate(p.q_lat, p.w_gate, p.out, p.out, (int)rows, p.d_lat, p.H * D, DT_BF16,
+                    stream);
+    if (e != hipSuccess) return e;
+  }
+  // a merged row's head mix (the merge works per head) runs as its own pass
+  if (p.vha_r > 0 && n_split > 1)
+    return launch_vha(p.out, p.vha_u, p.vha_v, p.out, (int)rows, p.H, D, p.vha_r, DT_BF16,
+                      stream);
   return hipSuccess;
 }
 

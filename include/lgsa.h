@@ -111,9 +111,11 @@ lgsa_status latent_gate_bwd_workspace(int M, int d_lat, int N, int dt, size_t* b
  *     k_win / v_win (prefill: win_len = T and the raw k, v; decode: a ring of >= window rows).
  * Both sets are used as they stand, also where they cover the same tokens.
  *   O[b,i,h,:] = sum_j softmax_j(scale * <q[b,i,h,:], key_j>) * value_j
- * and, when q_lat is non-NULL, out = O * sigmoid(q_lat[b,i,:] . w_gate[:, h*d + c]) (the
- * gate GEMM runs as a second kernel on the same stream and rescales out in place, exactly
- * what latent_gate(q_lat, w_gate, out, out, B*Tq, d_lat, H*d) does); otherwise out = O.
+ * and, when q_lat is non-NULL, out = O * sigmoid(q_lat[b,i,:] . w_gate[:, h*d + c]);
+ * otherwise out = O.  bf16 prefill (Tq > 1) computes the gate in the attention kernel's own
+ * epilogue (O never goes to memory); decode (Tq == 1) and fp32 run the gate GEMM as a second
+ * kernel that rescales out in place, exactly what latent_gate(q_lat, w_gate, out, out, B*Tq,
+ * d_lat, H*d) does.
  * --------------------------------------------------------------------------------------- */
 typedef struct {
   int dt;              /* LGSA_F32 or LGSA_BF16: q, k_win, v_win, kc, vc, q_lat, w_gate, out */
@@ -140,6 +142,12 @@ typedef struct {
   float* lse;          /* NULL, or [B, Tq, H] fp32: ln sum_j exp(scale <q, key_j>) of every row
                           (-inf for a row with no visible key), for hca_attn_bwd; bf16 with
                           Tq > 1 only */
+  const void* vha_u;   /* Virtual Head Attention (release blog, section 2.1: a light low-rank */
+  const void* vha_v;   /* mix across heads with an identity skip) of the gated output:        */
+  int vha_rank;        /* out[h] <- out[h] + sum_h' (U V^T)[h, h'] out[h'], U = vha_u and
+                          V = vha_v [H, vha_rank] (dt); vha_rank 0 (and NULL factors) turns it
+                          off, at most 16; bf16 needs H == 64.  It runs as a pass of its own
+                          after the attention kernels, in place (as vha_mix does). */
 } lgsa_hca_args;
 /* Validation: every size >= 1 (n_cap >= 0); unless max_pos < win_len (no window row wraps
  * around the ring), win_len >= window + Tq - 1: a call of Tq rows reads positions
@@ -273,10 +281,19 @@ typedef struct {
   float* lse;            /* [B, Tq, H] or NULL: natural log of each row's softmax denominator
                             over its scaled logits (-inf for a row with no valid entry), for
                             sparse_attn_bwd */
+  const void* vha_u;     /* Virtual Head Attention (release blog, section 2.1: a light low-rank */
+  const void* vha_v;     /* mix across heads with an identity skip) of the gated output:       */
+  int vha_rank;          /* out[h] <- out[h] + sum_h' (U V^T)[h, h'] out[h'], U = vha_u,
+                            V = vha_v [H, vha_rank] bf16; 0 turns it off, at most 16; H == 64 */
 } lgsa_sparse_args;
 /* Supported: LGSA_BF16, d_qk == d_v == 256, H % 64 == 0, row strides % 8 == 0,
- * d_lat % 64 == 0; every tensor 16-byte aligned.  The gate, when requested, runs as a second
- * kernel on the same stream that rescales out in place. */
+ * d_lat % 64 == 0; every tensor 16-byte aligned.  Gated without the head mix, the gate GEMM
+ * runs after the attention kernel and rescales out in place.  With the head mix, a GEMM first
+ * writes the gate factors sigmoid(q_lat w_gate) into out; the attention kernel's epilogue
+ * multiplies them into O, mixes the heads (a workgroup holds all 64 heads of its query row)
+ * and writes out over them.  A query row whose list is split over several workgroups (few
+ * rows, long lists) is merged, gated, by a combine kernel, and its head mix then runs as a
+ * pass of its own. */
 lgsa_status sparse_attn_fwd(const lgsa_sparse_args* a, void* stream);
 lgsa_status sparse_attn_fwd_workspace(const lgsa_sparse_args* a, size_t* bytes);
 
