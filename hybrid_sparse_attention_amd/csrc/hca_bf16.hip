@@ -27,10 +27,11 @@
 // of the first (the two transposed reads pick the key rows that lane group's accumulator
 // holds, so no data moves between lanes).
 //
-// Prefill: one workgroup of 8 waves per (32 query tokens, 4 heads).  Decode: one workgroup of
-// 4 waves (the 64 heads of one token) per (sequence, key split); partial (max, sum, O) of a
-// split go to the workspace and a combine kernel merges them.  When gated, the gate GEMM then
-// multiplies sigmoid(q_lat W) into O in place.
+// Prefill, ungated: one workgroup of 8 waves per (32 query tokens, 4 heads).  Prefill, gated:
+// one workgroup of 8 waves per (128 query tokens, 1 head) that applies the gate in its epilogue.
+// Decode: one workgroup of 4 waves (the 64 heads of one token) per (sequence, key split);
+// partial (max, sum, O) of a split go to the workspace and a combine kernel merges them; when
+// gated, the gate GEMM then multiplies sigmoid(q_lat W) into O in place.
 #include "common.h"
 #include "kernels.h"
 
@@ -381,13 +382,15 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_kernel(HcaParams p) {
 // tiles; each wave computes only the tiles holding a key that one of its rows sees (5 of the 8
 // window tiles of a whole tile) and skips the masking of tiles its rows see in full.
 //
-// Then the gate for the wave's 16 rows and the head's 512 channels: G^T = W^T q_lat^T on the
-// MFMA shape of O^T += V^T P^T, with a 32-row slice of W in an LDS tile laid out as a value
-// tile (its transposed reads give W^T), and the lane's own q_lat row, read from memory, as the
-// B operand in the slot order of P.  The W slices stream through a four-stage ring (the four
-// key/value buffers of the key loop), three steps ahead.  O is kept as packed bfloat16 (the
-// value the unfused path would store) while the gate accumulates, then out = O * sigmoid(G)
-// leaves from the registers.
+// Then the gate G = q_lat W for the tile's 128 rows and the head's 512 channels, sliced by
+// channel: wave w computes G^T for channels 64w .. 64w + 63 and all 128 rows, so each W^T
+// fragment feeds 8 products.  Each contraction step of 32 brings a 32-row slice of the head's
+// W columns (laid out as a value tile: its transposed reads give W^T) and the 128 q_lat rows'
+// 32 columns to LDS by LDS DMA, through a three-stage ring, two steps ahead of the one being
+// read.  Meanwhile O waits in the registers as packed bfloat16 (the value the unfused path
+// would store).  sigmoid(G), rounded to bfloat16, crosses to the row layout of O through LDS;
+// each wave writes out = O * sigmoid(G) over it and stores its 16 rows whole, 1 KiB per
+// instruction.
 constexpr int FQ = 128;  // query tokens per workgroup of the gated prefill kernel
 
 // Whether tile t holds a key visible to some row at positions [t_lo, t_hi] (all valid).
