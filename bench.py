@@ -693,7 +693,7 @@ def traffic_record(k):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--configs", default="0,1,2,3,4",
                     help="workloads to run; 1 is the headline, 0 and 2-4 are reported as "
