@@ -13,12 +13,15 @@
 //     while it is staged in LDS through registers, four waves of 64 x 64, K staged 64 at a
 //     time in double-buffered LDS; the lane multiplies its four channels into o and stores
 //     8 bytes.
+//   - gate_bf16_skinny_kernel (M <= 64 rows, d_lat = 1024: decode): the stream over W of
+//     gate_skinny.h, one workgroup per 64 channels.
 //
 // float32 path: a plain tiled FMA GEMM (used for the small fp32 configuration).
 //
 // With o == NULL the bfloat16 kernels write the gate factors sigmoid(q_lat W) themselves (the
 // attention kernels that apply the gate in their own epilogue read them from there).
 #include "common.h"
+#include "gate_skinny.h"
 #include "kernels.h"
 
 namespace lgsa {
@@ -423,130 +426,43 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_big_kernel(const uint16_t* _
   }
 }
 
-// Few-row bfloat16 path (M <= 64 and d_lat = 1024, decode): the gate is a stream over W.  Workgroup = 64
-// channels x all rows; wave w takes rows 16w .. 16w + 15 and all four channel blocks.  Each K
-// step of 64 brings an 8 KiB W chunk and an 8 KiB q_lat chunk to LDS by LDS DMA, four steps in
-// flight (four separate LDS objects, the K loop unrolled by four); W^T fragments come from the
-// transposing LDS read.  Rows of 128 bytes are XOR-swizzled by 16-byte chunk: W row r at chunk
-// c ^ (2 ((r >> 1) & 1) + 4 ((r >> 3) & 1)), q_lat row r at c ^ ((r >> 1) & 7), which keeps
-// both fragment reads free of bank conflicts.
-constexpr int SK_N = 64, SK_K = 64, SK_ROWB = 128;
-constexpr int SK_CHUNK = SK_K * SK_ROWB;  // 8 KiB: 64 rows of 128 bytes
-constexpr int SK_STAGE = 2 * SK_CHUNK;    // W chunk then q_lat chunk
+// Few-row bfloat16 path (M <= 64 and d_lat = 1024, decode): the tile of gate_skinny.h, one
+// workgroup per 64 channels, its four stages in four LDS objects of its own.
+__shared__ __attribute__((aligned(1024))) char sk_st0[gate_skinny::STAGE];
+__shared__ __attribute__((aligned(1024))) char sk_st1[gate_skinny::STAGE];
+__shared__ __attribute__((aligned(1024))) char sk_st2[gate_skinny::STAGE];
+__shared__ __attribute__((aligned(1024))) char sk_st3[gate_skinny::STAGE];
 
-__device__ __forceinline__ int sk_wsw(int r) { return 2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1); }
-__device__ __forceinline__ int sk_qsw(int r) { return (r >> 1) & 7; }
+// o of the lane's four 4-channel groups, loaded before the K loop (ones when o is NULL)
+struct OLoad {
+  const uint16_t* o;
+  int N;
+  uint2 x[4];
+  __device__ __forceinline__ void fetch(int m, int n) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+      x[cb] = o != nullptr ? *(const uint2*)(o + (size_t)m * N + min(n + 16 * cb, N - 4))
+                           : make_uint2(BF16_ONES, BF16_ONES);
+  }
+  __device__ __forceinline__ float4 value(int cb) const {
+    return make_float4(__uint_as_float(x[cb].x << 16), __uint_as_float(x[cb].x & 0xFFFF0000u),
+                       __uint_as_float(x[cb].y << 16), __uint_as_float(x[cb].y & 0xFFFF0000u));
+  }
+};
 
-__shared__ __attribute__((aligned(1024))) char sk_st0[SK_STAGE];
-__shared__ __attribute__((aligned(1024))) char sk_st1[SK_STAGE];
-__shared__ __attribute__((aligned(1024))) char sk_st2[SK_STAGE];
-__shared__ __attribute__((aligned(1024))) char sk_st3[SK_STAGE];
-
-// NK = d_lat / 64 K steps, fully unrolled: with straight-line code the compiler can tell that
-// the transfers into the stage being read have completed (the explicit waits guarantee it).
 template <int NK>
 __global__ __launch_bounds__(256) void gate_bf16_skinny_kernel(const uint16_t* __restrict__ ql,
                                                                const uint16_t* __restrict__ w,
                                                                const uint16_t* o, uint16_t* out,
                                                                int M, int N) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * SK_N;
-  constexpr int nk = NK;
-  const int d_lat = NK * SK_K;
-  // DMA of K step kt into stage st: 8 W instructions (8 k-rows each) and 8 q_lat instructions
-  // (8 rows each), 4 per wave
-  auto dma = [&](int kt, char* st) {
-    const int ln = opaque(lane);
-    const int k0 = kt * SK_K;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int ins = wave + 4 * u;                 // 0..7
-      const int r = 8 * ins + (ln >> 3);            // k-row
-      const int chunk = (ln & 7) ^ sk_wsw(r);
-      const int n = min(n0 + 8 * chunk, N - 8);     // columns past N repeat the last chunk
-      const uint16_t* rowp = w + (size_t)(k0 + 8 * ins) * N;
-      lds_dma16(rowp + (uint32_t)((ln >> 3) * N + n), st + ins * 8 * SK_ROWB);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int ins = wave + 4 * u;                 // 0..7
-      const int r = 8 * ins + (ln >> 3);            // q_lat row
-      const int chunk = (ln & 7) ^ sk_qsw(r);
-      const int m_first = min(8 * ins, M - 1);      // rows past M repeat the last row
-      const int rel = min(r, M - 1) - m_first;
-      const uint16_t* rowp = ql + (size_t)m_first * d_lat + k0;
-      lds_dma16(rowp + (uint32_t)(rel * d_lat + 8 * chunk), st + SK_CHUNK + ins * 8 * SK_ROWB);
-    }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  auto stage = [](int i) -> char* {
+    return i == 0 ? sk_st0 : i == 1 ? sk_st1 : i == 2 ? sk_st2 : sk_st3;
   };
-  // lane-constant fragment offsets.  B = q_lat^T: row 16 wave + l16, k 32ks + 8g .. +7.
-  const int qr = 16 * wave + l16;
-  int qoff[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) qoff[ks] = SK_CHUNK + qr * SK_ROWB + 16 * ((4 * ks + g) ^ sk_qsw(qr));
-  // A = W^T: channel 16cb + l16, k 32ks + 8g + 4h + 0..3 from the transposed read of rows
-  // 32ks + 8g + 4h + l16/4, columns 16cb + 4(l16 % 4) .. +3
-  const int a = l16 >> 2;
-  auto woff = [&](int ks, int h, int cb) {
-    const int r = 32 * ks + 8 * g + 4 * h + a;
-    const int c = 2 * cb + ((l16 & 3) >> 1);
-    return r * SK_ROWB + 16 * (c ^ sk_wsw(r)) + 8 * (l16 & 1);
-  };
-  f32x4_t acc[4];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const char* st) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      Frag8 bq;
-      bq.u = *(const uint4*)(st + qoff[ks]);
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const uint2 lo = lds_read_tr16(st + woff(ks, 0, cb));
-        const uint2 hi = lds_read_tr16(st + woff(ks, 1, cb));
-        Frag8 aw;
-        aw.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        acc[cb] = mfma_16x16x32(aw, bq, acc[cb]);
-      }
-    }
-  };
-  // four K steps in flight; stage of step kt = kt % 4.  At step kt the wave waits until its
-  // own transfers of step kt have landed (those of kt + 1 .. kt + 2 may still fly: 4 each),
-  // then a barrier makes every wave's share visible.
-  auto stage = [&](int kt) -> char* {
-    return (kt & 3) == 0 ? sk_st0 : (kt & 3) == 1 ? sk_st1 : (kt & 3) == 2 ? sk_st2 : sk_st3;
-  };
-#pragma unroll
-  for (int kt = 0; kt < 3 && kt < nk; ++kt) dma(kt, stage(kt));
-#pragma unroll
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 3 < nk) dma(kt + 3, stage(kt + 3));
-    // transfers issued after step kt's: min(3, nk - 1 - kt) steps of 4 instructions each
-    const int later = (nk - 1 - kt) < 3 ? (nk - 1 - kt) : 3;
-    if (later == 3) wait_vm<12>();
-    else if (later == 2) wait_vm<8>();
-    else if (later == 1) wait_vm<4>();
-    else wait_vm<0>();
-    lds_barrier();  // every wave's share of step kt has landed (each waited for its own)
-    compute(stage(kt));
-    lds_barrier();  // every wave is done with this stage before it is refilled
-  }
-  // epilogue: lane holds G[row 16 wave + l16][channels n0 + 16cb + 4g .. +3]
-  if (qr >= M) return;
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    const int n = n0 + 16 * cb + 4 * g;
-    if (n >= N) continue;
-    const size_t off = (size_t)qr * N + n;
-    const uint2 x = o != nullptr ? *(const uint2*)(o + off) : make_uint2(BF16_ONES, BF16_ONES);
-    uint2 r;
-    r.x = pack_bf16x2(__uint_as_float(x.x << 16) * sigmoidf_fast(acc[cb][0]),
-                      __uint_as_float(x.x & 0xFFFF0000u) * sigmoidf_fast(acc[cb][1]));
-    r.y = pack_bf16x2(__uint_as_float(x.y << 16) * sigmoidf_fast(acc[cb][2]),
-                      __uint_as_float(x.y & 0xFFFF0000u) * sigmoidf_fast(acc[cb][3]));
-    *(uint2*)(out + off) = r;
-  }
+  OLoad ov{o, N};
+  gate_skinny::tile<NK>(ql, w, ov, out, M, N, blockIdx.x * gate_skinny::N_TILE, stage, wave,
+                        lane);
 }
 
 // fp32: 64x64 output tile, each of 256 threads computes a 4x4 block.
@@ -616,8 +532,9 @@ hipError_t launch_gate(const void* q_lat, const void* w, const void* o, void* ou
     hipLaunchKernelGGL(gate_bf16_big_kernel<false>, dim3(grid), dim3(512), 0, stream,
                        (const uint16_t*)q_lat, (const uint16_t*)w, (const uint16_t*)o,
                        (uint16_t*)out, M, d_lat, N, nullptr, nullptr);
-  } else if (dt == DT_BF16 && M <= 64 && d_lat == 16 * SK_K) {
-    hipLaunchKernelGGL(gate_bf16_skinny_kernel<16>, dim3((N + SK_N - 1) / SK_N), dim3(256), 0,
+  } else if (dt == DT_BF16 && M <= 64 && d_lat == 16 * gate_skinny::K_STEP) {
+    hipLaunchKernelGGL(gate_bf16_skinny_kernel<16>,
+                       dim3((N + gate_skinny::N_TILE - 1) / gate_skinny::N_TILE), dim3(256), 0,
                        stream, (const uint16_t*)q_lat, (const uint16_t*)w, (const uint16_t*)o,
                        (uint16_t*)out, M, N);
   } else if (dt == DT_BF16) {

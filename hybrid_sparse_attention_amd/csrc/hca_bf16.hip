@@ -30,9 +30,11 @@
 // Prefill, ungated: one workgroup of 8 waves per (32 query tokens, 4 heads).  Prefill, gated:
 // one workgroup of 8 waves per (128 query tokens, 1 head) that applies the gate in its epilogue.
 // Decode: one workgroup of 4 waves (the 64 heads of one token) per (sequence, key split);
-// partial (max, sum, O) of a split go to the workspace and a combine kernel merges them; when
-// gated, the gate GEMM then multiplies sigmoid(q_lat W) into O in place.
+// partial (max, sum, O) of a split go to the workspace and a second kernel merges them.  When
+// gated, that kernel is the gate's: it streams W once, 64 channels of every row per workgroup,
+// and multiplies sigmoid(q_lat W) into the merged O of those channels.
 #include "common.h"
+#include "gate_skinny.h"
 #include "kernels.h"
 
 namespace lgsa {
@@ -657,11 +659,12 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_gated_kernel(HcaParams p) 
 // ------------------------------------------------------------------------------- decode
 // One workgroup of 4 waves (16 heads each: the 64 heads of a group) per (sequence, key split).
 // Keys of a sequence: compressed entries 0..ne-1, then raw positions s_lo..t; every row is at
-// position t.  A split writes its partial (max, sum, O) unless it is the only one.
-__global__ __launch_bounds__(256, 1) void hca_decode_kernel(HcaParams p, int n_split, int chunk,
-                                                            float* part_o, float* part_ml) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+// position t.  A split writes its partial (max, sum, O) to the workspace, unless it is the
+// only one and no gate follows (then it writes the output).
+// One key split of one sequence for the 64 heads of a group (the decode kernel's attention).
+__device__ __forceinline__ void decode_split(const HcaParams& p, int n_split, int chunk,
+                                             float* part_o, float* part_ml, bool partials,
+                                             int wave, int lane) {
   const int l16 = lane & 15, g = lane >> 4;
   const int n_hg = p.H / 64;
   const int hg = blockIdx.x % n_hg;
@@ -717,7 +720,7 @@ __global__ __launch_bounds__(256, 1) void hca_decode_kernel(HcaParams p, int n_s
   row_key_loop(st, qf, rp, src, tile_of, tiles_c + tiles_w, wave, 4, lane, p.scale * LOG2E);
 
   const float lt = wave_sum16(st.l);
-  if (n_split == 1) {
+  if (!partials) {  // the only split, not gated here: the output directly
     const float inv = final_scale(st.m, lt);
     uint16_t* orow = (uint16_t*)p.out + ((size_t)b * p.H + h) * D;
 #pragma unroll
@@ -734,6 +737,97 @@ __global__ __launch_bounds__(256, 1) void hca_decode_kernel(HcaParams p, int n_s
   }
 }
 
+__global__ __launch_bounds__(256, 1) void hca_decode_kernel(HcaParams p, int n_split, int chunk,
+                                                            float* part_o, float* part_ml,
+                                                            bool partials) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  decode_split(p, n_split, chunk, part_o, part_ml, partials, wave, lane);
+}
+
+// The merged O of the decode splits for the gate tile's epilogue (gate_skinny.h): the lane's
+// row b and its four 4-channel groups n .. n + 3 + 48 of head h.  The partials of the first
+// PRE splits are loaded before the gate's K loop, the others in the epilogue.  Values are
+// rounded to bfloat16, as the output stores O.
+template <int PRE>
+struct MergedO {
+  const float* part_o;
+  const float* part_ml;
+  int H, n_split;
+  size_t base;  // partial row (b, split 0, h) times D, plus the channel
+  size_t ml0;   // (b, split 0, h) in part_ml pairs
+  float2 ml[PRE];
+  float4 v[4][PRE];
+
+  __device__ __forceinline__ void fetch(int b, int n) {
+    const int h = n / D, j = n % D;
+    base = (((size_t)b * n_split) * H + h) * D + j;
+    ml0 = ((size_t)b * n_split) * H + h;
+#pragma unroll
+    for (int s = 0; s < PRE; ++s) {
+      if (s < n_split) {
+        ml[s] = *(const float2*)(part_ml + (ml0 + (size_t)s * H) * 2);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          v[cb][s] = *(const float4*)(part_o + base + (size_t)s * H * D + 16 * cb);
+      }
+    }
+  }
+  __device__ __forceinline__ float4 value(int cb) const {
+    float mt = NEG_BIG;
+#pragma unroll
+    for (int s = 0; s < PRE; ++s)
+      if (s < n_split) mt = fmaxf(mt, ml[s].x);
+    for (int s = PRE; s < n_split; ++s) mt = fmaxf(mt, part_ml[(ml0 + (size_t)s * H) * 2]);
+    float lt = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+    auto add = [&](float m, float l, float4 x) {
+      const float a = fast_exp2(m - mt);  // an empty split carries the sentinel
+      lt += a * l;
+      acc[0] += a * x.x;
+      acc[1] += a * x.y;
+      acc[2] += a * x.z;
+      acc[3] += a * x.w;
+    };
+#pragma unroll
+    for (int s = 0; s < PRE; ++s)
+      if (s < n_split) add(ml[s].x, ml[s].y, v[cb][s]);
+    for (int s = PRE; s < n_split; ++s) {
+      const float2 q = *(const float2*)(part_ml + (ml0 + (size_t)s * H) * 2);
+      add(q.x, q.y, *(const float4*)(part_o + base + (size_t)s * H * D + 16 * cb));
+    }
+    const float inv = final_scale(mt, lt);
+    auto rb = [](float x) { return __uint_as_float(pack_bf16x2(x, 0.f) << 16); };
+    return make_float4(rb(acc[0] * inv), rb(acc[1] * inv), rb(acc[2] * inv), rb(acc[3] * inv));
+  }
+};
+
+// Gated decode, second kernel: the gate tile of gate_skinny.h over channels 64 blockIdx .. + 63
+// of every sequence (rows of q_lat), whose epilogue merges the splits of those channels and
+// multiplies them: out = bf16(O) * sigmoid(q_lat W), what the gate GEMM does to a stored O.
+__shared__ __attribute__((aligned(1024))) char dg_st0[gate_skinny::STAGE];
+__shared__ __attribute__((aligned(1024))) char dg_st1[gate_skinny::STAGE];
+__shared__ __attribute__((aligned(1024))) char dg_st2[gate_skinny::STAGE];
+__shared__ __attribute__((aligned(1024))) char dg_st3[gate_skinny::STAGE];
+
+__global__ __launch_bounds__(256) void hca_decode_gate_kernel(HcaParams p, int n_split,
+                                                              const float* __restrict__ part_o,
+                                                              const float* __restrict__ part_ml) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  auto stage = [](int i) -> char* {
+    return i == 0 ? dg_st0 : i == 1 ? dg_st1 : i == 2 ? dg_st2 : dg_st3;
+  };
+  MergedO<4> ov;
+  ov.part_o = part_o;
+  ov.part_ml = part_ml;
+  ov.H = p.H;
+  ov.n_split = n_split;
+  gate_skinny::tile<16>((const uint16_t*)p.q_lat, (const uint16_t*)p.w_gate, ov,
+                        (uint16_t*)p.out, p.B, p.H * D, blockIdx.x * gate_skinny::N_TILE, stage,
+                        wave, lane);
+}
+
+// Merges the splits of one (sequence, head): 128 threads of 4 channels.
 __global__ __launch_bounds__(128) void hca_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           uint16_t* __restrict__ out, int H,
@@ -778,6 +872,13 @@ void decode_plan(const HcaParams& p, int& n_split, int& chunk) {
 // the decode kernel takes one query row per sequence and whole groups of 64 heads; the
 // prefill kernel takes groups of 4 heads and any number of rows
 bool use_decode(const HcaParams& p) { return p.Tq == 1 && p.H % 64 == 0; }
+
+// Whether the gate kernel of the decode path merges the splits (the tile of gate_skinny.h: at
+// most 64 rows, d_lat = 1024); otherwise a combine kernel merges them and the gate GEMM
+// follows.
+bool decode_fuses_gate(const HcaParams& p) {
+  return p.q_lat != nullptr && p.B * p.Tq <= 64 && p.d_lat == 16 * gate_skinny::K_STEP;
+}
 
 // ------------------------------------------------------------------------------ backward
 // Prefill backward (every sequence from position 0).  With P = softmax of the scaled logits
@@ -1148,7 +1249,7 @@ size_t hca_bf16_workspace(const HcaParams& p) {
   if (!use_decode(p)) return 0;
   int n_split, chunk;
   decode_plan(p, n_split, chunk);
-  if (n_split == 1) return 0;
+  if (n_split == 1 && !decode_fuses_gate(p)) return 0;
   const size_t rows = (size_t)p.B * n_split * p.H;
   return rows * D * sizeof(float) + rows * 2 * sizeof(float);
 }
@@ -1160,18 +1261,25 @@ hipError_t launch_hca_bf16(const HcaParams& p, hipStream_t stream) {
     decode_plan(p, n_split, chunk);
     float* part_o = (float*)p.ws;
     float* part_ml = part_o ? part_o + (size_t)p.B * n_split * p.H * D : nullptr;
+    const bool fuse = decode_fuses_gate(p);
     const long long grid = (long long)p.B * (p.H / 64) * n_split;
     hipLaunchKernelGGL(hca_decode_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p,
-                       n_split, chunk, part_o, part_ml);
+                       n_split, chunk, part_o, part_ml, n_split > 1 || fuse);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (n_split > 1) {
+    if (fuse) {  // the gate kernel merges the splits and multiplies the gate in
+      const int slices = (p.H * D + gate_skinny::N_TILE - 1) / gate_skinny::N_TILE;
+      hipLaunchKernelGGL(hca_decode_gate_kernel, dim3(slices), dim3(256), 0, stream, p, n_split,
+                         part_o, part_ml);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    } else if (n_split > 1) {
       hipLaunchKernelGGL(hca_combine_kernel, dim3(p.B * p.H), dim3(128), 0, stream, part_o,
                          part_ml, (uint16_t*)p.out, p.H, n_split);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    if (p.q_lat != nullptr) {  // the gate GEMM multiplies sigmoid(q_lat W) into O in place
+    if (p.q_lat != nullptr && !fuse) {  // the gate GEMM multiplies sigmoid(q_lat W) into O
       e = launch_gate(p.q_lat, p.w_gate, p.out, p.out, p.B * p.Tq, p.d_lat, p.H * D, DT_BF16,
                       stream);
       if (e != hipSuccess) return e;

@@ -113,9 +113,12 @@ lgsa_status latent_gate_bwd_workspace(int M, int d_lat, int N, int dt, size_t* b
  *   O[b,i,h,:] = sum_j softmax_j(scale * <q[b,i,h,:], key_j>) * value_j
  * and, when q_lat is non-NULL, out = O * sigmoid(q_lat[b,i,:] . w_gate[:, h*d + c]);
  * otherwise out = O.  bf16 prefill (Tq > 1) computes the gate in the attention kernel's own
- * epilogue (O never goes to memory); decode (Tq == 1) and fp32 run the gate GEMM as a second
- * kernel that rescales out in place, exactly what latent_gate(q_lat, w_gate, out, out, B*Tq,
- * d_lat, H*d) does.
+ * epilogue (O never goes to memory).  bf16 decode (Tq == 1) with B <= 64 and d_lat == 1024
+ * merges the key splits of the attention in the gate kernel's epilogue, which multiplies the
+ * merged O, rounded to bf16, by sigmoid(q_lat W).  Other decode shapes and fp32 run the gate
+ * GEMM as a second kernel that rescales out in place, exactly what latent_gate(q_lat, w_gate,
+ * out, out, B*Tq, d_lat, H*d) does.  All give the result of the unfused calls: O stored in the
+ * output type, then latent_gate.
  * --------------------------------------------------------------------------------------- */
 typedef struct {
   int dt;              /* LGSA_F32 or LGSA_BF16: q, k_win, v_win, kc, vc, q_lat, w_gate, out */

@@ -161,8 +161,13 @@ def test_hca_prefill_f32_config0(torch, orc):
 
 
 @pytest.mark.parametrize("contexts,gated", [([1000, 130, 5], True), ([131072], False),
-                                            ([128, 127, 129, 256], True)])
+                                            ([128, 127, 129, 256], True), ([20, 3], True),
+                                            ([300] * 65, True)])
 def test_hca_decode_bf16(torch, orc, contexts, gated):
+    """Decode against the oracle.  Gated with at most 64 sequences, the attention kernel's
+    workgroups compute the gate factors, with gate-only workgroups added when the key splits
+    are few ([1000, 130, 5]) and partials merged even for a single split ([20, 3]); 65
+    sequences take the gate GEMM after the merge."""
     B = len(contexts)
     x = synth.hca_decode(240 + B, B=B, context=max(contexts), H=64, contexts=contexts,
                          gated=gated)
