@@ -745,6 +745,9 @@ __global__ __launch_bounds__(256, 1) void hca_decode_kernel(HcaParams p, int n_s
   decode_split(p, n_split, chunk, part_o, part_ml, partials, wave, lane);
 }
 
+// splits whose partials the decode gate kernel loads before its K loop
+constexpr int MERGE_PRE = 4;
+
 // The merged O of the decode splits for the gate tile's epilogue (gate_skinny.h): the lane's
 // row b and its four 4-channel groups n .. n + 3 + 48 of head h.  The partials of the first
 // PRE splits are loaded before the gate's K loop, the others in the epilogue.  Values are
@@ -817,7 +820,7 @@ __global__ __launch_bounds__(256) void hca_decode_gate_kernel(HcaParams p, int n
   auto stage = [](int i) -> char* {
     return i == 0 ? dg_st0 : i == 1 ? dg_st1 : i == 2 ? dg_st2 : dg_st3;
   };
-  MergedO<4> ov;
+  MergedO<MERGE_PRE> ov;
   ov.part_o = part_o;
   ov.part_ml = part_ml;
   ov.H = p.H;
@@ -873,11 +876,16 @@ void decode_plan(const HcaParams& p, int& n_split, int& chunk) {
 // prefill kernel takes groups of 4 heads and any number of rows
 bool use_decode(const HcaParams& p) { return p.Tq == 1 && p.H % 64 == 0; }
 
-// Whether the gate kernel of the decode path merges the splits (the tile of gate_skinny.h: at
-// most 64 rows, d_lat = 1024); otherwise a combine kernel merges them and the gate GEMM
-// follows.
+// Whether the gate kernel of the decode path merges the splits: the tile of gate_skinny.h (at
+// most 64 rows, d_lat = 1024), with at most MERGE_PRE splits, whose partials it loads before
+// its K loop (more splits, for few long sequences, would be read after it, one after
+// another).  Otherwise a combine kernel merges them and the gate GEMM follows.
+
 bool decode_fuses_gate(const HcaParams& p) {
-  return p.q_lat != nullptr && p.B * p.Tq <= 64 && p.d_lat == 16 * gate_skinny::K_STEP;
+  if (p.q_lat == nullptr || p.B * p.Tq > 64 || p.d_lat != 16 * gate_skinny::K_STEP) return false;
+  int n_split, chunk;
+  decode_plan(p, n_split, chunk);
+  return n_split <= MERGE_PRE;
 }
 
 // ------------------------------------------------------------------------------ backward

@@ -14,10 +14,11 @@
 // to 2048 queries at a time, and a 1024-thread workgroup per query selects.
 // Decode (few queries, long context): one workgroup per (query, 16384-position segment)
 // streams its key rows once, scores them with fp32 FMA, selects the segment's top-k in LDS and
-// writes them as a candidate list in ascending position; 4-way reductions of candidate lists
-// (each keeping the top k of its four lists) then narrow them to one (the union of top-k sets
-// of disjoint parts contains the top k of the whole, and position order is kept throughout, so
-// the lower-index rule stays exact).
+// writes them as a candidate list in ascending position (the union of the top-k sets of
+// disjoint parts contains the top k of the whole).  Each full segment also reports a key that
+// bounds the row's k-th largest from below; a filter keeps the candidates at or above the
+// bound, which leaves a few thousand, and one workgroup per query selects the top k among
+// them.  Position order is kept throughout, so the lower-index rule stays exact.
 #include "common.h"
 #include "kernels.h"
 
@@ -519,7 +520,8 @@ constexpr int DEC_NT = 256;
 __global__ __launch_bounds__(DEC_NT) void index_segment_kernel(IndexParams p, int n_seg,
                                                                uint32_t* cand_key,
                                                                int32_t* cand_pos,
-                                                               int* cand_cnt) {
+                                                               int* cand_cnt,
+                                                               uint32_t* lo_key) {
   __shared__ uint32_t skey[SEG];
   __shared__ __attribute__((aligned(16))) float sq[4 * 64 + 4];
   __shared__ uint32_t hist[(DEC_NT / 64) * 256];
@@ -582,101 +584,211 @@ __global__ __launch_bounds__(DEC_NT) void index_segment_kernel(IndexParams p, in
   __syncthreads();
   const size_t cbase = ((size_t)r * n_seg + seg) * p.k;
   auto get = [&](int x) { return skey[x]; };
+  uint32_t kstar;
+  int need_eq;
   if (seg_n <= p.k) {
     for (int x = tid; x < seg_n; x += DEC_NT) {
       cand_key[cbase + x] = skey[x];
       cand_pos[cbase + x] = seg_start + x;
     }
-    return;
+  } else {
+    radix_threshold<DEC_NT>(get, seg_n, p.k, hist, sh, wsum, kstar, need_eq);
+    emit_topk<DEC_NT>(get, seg_n, kstar, need_eq, wsum, nullptr,
+                      [&](int slot, int x, uint32_t u) {
+      cand_key[cbase + slot] = u;
+      cand_pos[cbase + slot] = seg_start + x;
+      // compacted in place: slot <= x, and every key of x's chunk has been read
+      skey[slot] = u;
+    });
   }
-  uint32_t kstar;
-  int need_eq;
-  radix_threshold<DEC_NT>(get, seg_n, p.k, hist, sh, wsum, kstar, need_eq);
-  emit_topk<DEC_NT>(get, seg_n, kstar, need_eq, wsum, nullptr,
-                    [&](int slot, int x, uint32_t u) {
-    cand_key[cbase + slot] = u;
-    cand_pos[cbase + slot] = seg_start + x;
-  });
+  // the bound of a full segment (every segment of the row but the last): its k_lo-th largest
+  // key, k_lo = ceil(k / (full segments)), so that the full segments hold >= k keys at or
+  // above the smallest of their bounds.  k_lo <= k, so it is the k_lo-th largest of the
+  // segment's top k, now in skey[0 .. k).
+  const int n_full = (n + SEG - 1) / SEG - 1;
+  if (seg < n_full) {
+    const int k_lo = (p.k + n_full - 1) / n_full;  // <= k < SEG = seg_n
+    __syncthreads();
+    radix_threshold<DEC_NT>(get, p.k, k_lo, hist, sh, wsum, kstar, need_eq);
+    if (tid == 0) lo_key[(size_t)r * n_seg + seg] = kstar;
+  }
 }
 
-// One reduction level: workgroup (row, group g) takes the candidate lists g*G .. g*G + G - 1
-// (G = red_g(k)) of the previous level (each at most k entries in ascending position, the
-// lists themselves in ascending position order), concatenates them in LDS and keeps their top
-// k, still in ascending position.  The union of the top-k sets of disjoint lists holds the
-// top k of the whole, so levels of G-way reductions end with the row's top k; the last
-// level (one group) writes it to idx_out.  Rows with at most k positions are written there
-// directly (all positions, then -1).
-constexpr int RED_NT = 512;
-constexpr int RED_CAP = 16384;  // candidates a reduction holds in LDS: G * k
+// Filter: workgroup (row, group g) concatenates the candidate lists of segments
+// g G .. g G + G - 1 (in segment order, so in ascending position) and keeps the candidates
+// whose key is at least L, the smallest bound of the row's full segments.  Those segments hold
+// at least k keys >= L, so the row's k-th largest key is >= L and every key of the top k (ties
+// included) passes.  A row of one segment has no bound (L = 0: everything passes).  Output
+// list g has room for G k entries.
+constexpr int FLT_NT = 512;
+constexpr int FIN_NT = 512;
+constexpr int FIN_CAP = 16384;    // candidates the final selection holds in LDS
+constexpr int FIN_MAX_GRP = 1024; // filter groups per row (the group size grows past this)
 
-// lists merged per reduction (eight-way levels measured slower: fewer, longer workgroups)
-__host__ __device__ inline int red_g(int) { return 4; }
+__host__ __device__ inline int filter_g(int n_seg) {
+  return n_seg <= 4 * FIN_MAX_GRP ? 4 : (n_seg + FIN_MAX_GRP - 1) / FIN_MAX_GRP;
+}
 
-__global__ __launch_bounds__(RED_NT) void index_reduce_kernel(IndexParams p, int n_in,
+constexpr int FLT_MAX_G = 128;  // filter_g for up to 2^31 keys
+constexpr int FLT_R = 16;       // slots a thread holds per round
+
+__global__ __launch_bounds__(FLT_NT) void index_filter_kernel(IndexParams p, int n_seg,
                                                               const uint32_t* in_key,
                                                               const int32_t* in_pos,
                                                               const int* in_cnt,
+                                                              const uint32_t* lo_key,
                                                               uint32_t* out_key,
                                                               int32_t* out_pos, int* out_cnt) {
-  __shared__ uint32_t rkey[RED_CAP];
-  __shared__ int32_t rpos[RED_CAP];
-  __shared__ uint32_t hist[(RED_NT / 64) * 256];
+  __shared__ int wsum[2 * FLT_NT / 64];
+  __shared__ int s_cnt[FLT_MAX_G];
+  __shared__ uint32_t s_lo;
+  const int G = filter_g(n_seg);
+  const int n_grp = (n_seg + G - 1) / G;
+  const int r = blockIdx.x / n_grp, grp = blockIdx.x % n_grp;
+  const int b = r / p.Tq;
+  const int n = visible_keys(p.pos0[b] + r % p.Tq, p.block, min(p.S, (p.max_pos + 1) / p.block));
+  if (n <= p.k) return;  // written directly by the final selection
+  const int n_full = (n + SEG - 1) / SEG - 1;
+  if (threadIdx.x < 64) {
+    uint32_t m = 0xFFFFFFFFu;
+    for (int s = threadIdx.x; s < n_full; s += 64) m = min(m, lo_key[(size_t)r * n_seg + s]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = min(m, (uint32_t)__shfl_xor((int)m, off));
+    if (threadIdx.x == 0) s_lo = n_full >= 1 ? m : 0u;
+  }
+  for (int q = threadIdx.x; q < G; q += FLT_NT) {
+    const int li = grp * G + q;
+    s_cnt[q] = li < n_seg ? in_cnt[(size_t)r * n_seg + li] : 0;
+  }
+  __syncthreads();
+  const uint32_t lo = s_lo;
+  const int k = p.k;
+  // the group's lists laid end to end at a stride of k (list q's entries j < count are
+  // candidates), in rounds of FLT_NT FLT_R consecutive slots: thread t takes FLT_R consecutive
+  // slots of the round, loads their keys and positions once, counts the kept ones, and writes
+  // them after the block scan, so the output keeps slot (position) order.
+  const int n_slots = G * k;
+  const size_t gbase = ((size_t)r * n_seg + (size_t)grp * G) * k;  // slot 0 of the group
+  auto valid = [&](int x) { return x < G * k && x % k < s_cnt[x / k]; };
+  const size_t dst = (size_t)r * n_grp + grp;
+  uint32_t* ok = out_key + dst * G * k;
+  int32_t* op = out_pos + dst * G * k;
+  int base = 0;
+  for (int r0 = 0; r0 < n_slots; r0 += FLT_NT * FLT_R) {
+    const int x0 = r0 + (int)threadIdx.x * FLT_R;
+    uint32_t u[FLT_R];
+    int32_t ps[FLT_R];
+    bool keep[FLT_R];
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < FLT_R; ++j) {
+      const bool v = valid(x0 + j);
+      u[j] = v ? in_key[gbase + x0 + j] : 0u;
+      ps[j] = v ? in_pos[gbase + x0 + j] : 0;
+      keep[j] = v && u[j] >= lo;
+      c += keep[j] ? 1 : 0;
+    }
+    int ex, ex2, tot, tot2;
+    block_scan2<FLT_NT>(c, 0, ex, ex2, tot, tot2, wsum);
+    (void)ex2;
+    (void)tot2;
+    int o = base + ex;
+#pragma unroll
+    for (int j = 0; j < FLT_R; ++j)
+      if (keep[j]) {
+        ok[o] = u[j];
+        op[o] = ps[j];
+        ++o;
+      }
+    base += tot;
+  }
+  if (threadIdx.x == 0) out_cnt[dst] = base;
+}
+
+// Final selection, one workgroup per row: the filtered lists in group order (ascending
+// position), their top k by radix select, emitted in ascending position into idx_out.  Up to
+// FIN_CAP candidates are held in LDS; more (only when very many keys tie at the bound) are
+// selected over global memory.  Rows with at most k positions get all of them, then -1.
+__global__ __launch_bounds__(FIN_NT) void index_final_kernel(IndexParams p, int n_seg,
+                                                             const uint32_t* in_key,
+                                                             const int32_t* in_pos,
+                                                             const int* in_cnt) {
+  __shared__ uint32_t rkey[FIN_CAP];
+  __shared__ int32_t rpos[FIN_CAP];
+  __shared__ uint32_t hist[(FIN_NT / 64) * 256];
   __shared__ int sh[3];
-  __shared__ int wsum[2 * RED_NT / 64];
-  const int G = red_g(p.k);
-  const int n_out = (n_in + G - 1) / G;
-  const bool last = n_out == 1;
-  const int r = blockIdx.x / n_out, grp = blockIdx.x % n_out;
+  __shared__ int wsum[2 * FIN_NT / 64];
+  __shared__ int goff[FIN_MAX_GRP + 1];
+  const int G = filter_g(n_seg);
+  const int n_grp = (n_seg + G - 1) / G;
+  const int r = blockIdx.x;
   const int b = r / p.Tq, i = r % p.Tq;
   const int n = visible_keys(p.pos0[b] + i, p.block, min(p.S, (p.max_pos + 1) / p.block));
   const int k = p.k;
   int32_t* out = p.idx_out + (size_t)r * k;
   if (n <= k) {
-    if (last)
-      for (int j = threadIdx.x; j < k; j += RED_NT) out[j] = j < n ? j : -1;
+    for (int j = threadIdx.x; j < k; j += FIN_NT) out[j] = j < n ? j : -1;
     return;
   }
-  int total = 0;
-  for (int q = 0; q < G; ++q) {
-    const int li = grp * G + q;
-    if (li >= n_in) break;
-    const size_t src = (size_t)r * n_in + li;
-    const int c = in_cnt[src];
-    for (int x = threadIdx.x; x < c; x += RED_NT) {
-      rkey[total + x] = in_key[src * k + x];
-      rpos[total + x] = in_pos[src * k + x];
-    }
-    total += c;
+  {
+    // offsets of the lists: thread t sums lists 2t and 2t + 1 (n_grp <= 2 FIN_NT)
+    const int g0 = 2 * (int)threadIdx.x;
+    const int c0 = g0 < n_grp ? in_cnt[(size_t)r * n_grp + g0] : 0;
+    const int c1 = g0 + 1 < n_grp ? in_cnt[(size_t)r * n_grp + g0 + 1] : 0;
+    int ex, ex2, tot, tot2;
+    block_scan2<FIN_NT>(c0 + c1, 0, ex, ex2, tot, tot2, wsum);
+    if (g0 < n_grp) goff[g0] = ex;
+    if (g0 + 1 < n_grp) goff[g0 + 1] = ex + c0;
+    if (threadIdx.x == 0) goff[n_grp] = tot;
+    __syncthreads();
   }
-  __syncthreads();
-  const size_t dst = (size_t)r * n_out + grp;
-  if (total <= k) {  // nothing to drop
-    for (int x = threadIdx.x; x < k; x += RED_NT) {
-      if (last) {
-        out[x] = x < total ? rpos[x] : -1;
-      } else if (x < total) {
-        out_key[dst * k + x] = rkey[x];
-        out_pos[dst * k + x] = rpos[x];
-      }
-    }
-    if (!last && threadIdx.x == 0) out_cnt[dst] = total;
-    return;
-  }
-  auto get = [&](int x) { return rkey[x]; };
+  const int total = goff[n_grp];  // >= k: the top k passed the filter
+  const size_t lbase = (size_t)r * n_grp * G * k;  // list g starts at lbase + g G k
   uint32_t kstar;
   int need_eq;
-  radix_threshold<RED_NT>(get, total, k, hist, sh, wsum, kstar, need_eq);
-  if (last) {
-    emit_topk<RED_NT>(get, total, kstar, need_eq, wsum, nullptr,
+  // candidate x of the concatenation: list g with goff[g] <= x < goff[g + 1]
+  auto at = [&](int x) {
+    int lo = 0, hi = n_grp - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (goff[mid] <= x) lo = mid;
+      else hi = mid - 1;
+    }
+    return lbase + (size_t)lo * G * k + (x - goff[lo]);
+  };
+  if (total <= FIN_CAP) {
+    for (int x0 = threadIdx.x; x0 < total; x0 += 4 * FIN_NT) {
+      uint32_t u[4];
+      int32_t ps[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int x = x0 + j * FIN_NT;
+        if (x < total) {
+          const size_t a = at(x);
+          u[j] = in_key[a];
+          ps[j] = in_pos[a];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int x = x0 + j * FIN_NT;
+        if (x < total) {
+          rkey[x] = u[j];
+          rpos[x] = ps[j];
+        }
+      }
+    }
+    __syncthreads();
+    auto get = [&](int x) { return rkey[x]; };
+    radix_threshold<FIN_NT>(get, total, k, hist, sh, wsum, kstar, need_eq);
+    emit_topk<FIN_NT>(get, total, kstar, need_eq, wsum, nullptr,
                       [&](int slot, int x, uint32_t) { out[slot] = rpos[x]; });
-  } else {
-    emit_topk<RED_NT>(get, total, kstar, need_eq, wsum, nullptr,
-                      [&](int slot, int x, uint32_t u) {
-                        out_key[dst * k + slot] = u;
-                        out_pos[dst * k + slot] = rpos[x];
-                      });
-    if (threadIdx.x == 0) out_cnt[dst] = k;
+    return;
   }
+  auto get = [&](int x) { return in_key[at(x)]; };
+  radix_threshold<FIN_NT>(get, total, k, hist, sh, wsum, kstar, need_eq);
+  emit_topk<FIN_NT>(get, total, kstar, need_eq, wsum, rkey,
+                    [&](int slot, int x, uint32_t) { out[slot] = in_pos[at(x)]; });
 }
 
 bool use_decode_path(const IndexParams& p) { return p.Tq <= 4; }
@@ -691,24 +803,29 @@ int n_segments(const IndexParams& p) {
 
 }  // namespace
 
-// Candidate lists of the decode path: level 0 holds the segments' lists, each later level
-// red_g(k) times fewer; every list has room for k keys, k positions and a count.
-static size_t level_lists(int n_seg, int k) {
-  size_t total = 0;
-  const int G = red_g(k);
-  for (int n = n_seg;; n = (n + G - 1) / G) {
-    total += n;
-    if (n == 1) break;
+// Decode workspace: the segments' candidate lists (k keys, k positions and a count each),
+// their bounds, and the filtered lists (G k entries and a count each).
+struct DecodeWs {
+  size_t seg_lists, grp_lists, k;
+  int G;
+  size_t bytes() const {
+    return seg_lists * (k * 8 + 4 + 4) + grp_lists * ((size_t)G * k * 8 + 4);
   }
-  return total;
+};
+
+static DecodeWs decode_ws(const IndexParams& p) {
+  DecodeWs w;
+  const size_t rows = (size_t)p.B * p.Tq;
+  const int n_seg = n_segments(p);
+  w.G = filter_g(n_seg);
+  w.k = (size_t)p.k;
+  w.seg_lists = rows * n_seg;
+  w.grp_lists = rows * ((n_seg + w.G - 1) / w.G);
+  return w;
 }
 
 size_t index_workspace(const IndexParams& p) {
-  if (use_decode_path(p)) {
-    const size_t rows = (size_t)p.B * p.Tq;
-    const size_t lists = rows * level_lists(n_segments(p), p.k);
-    return lists * p.k * (sizeof(uint32_t) + sizeof(int32_t)) + lists * sizeof(int);
-  }
+  if (use_decode_path(p)) return decode_ws(p).bytes();
   const size_t q_chunk = std::min(p.Tq, 2048);
   return q_chunk * (size_t)key_bound(p) * sizeof(uint32_t);
 }
@@ -718,29 +835,26 @@ hipError_t launch_index(const IndexParams& p, hipStream_t stream) {
   if (use_decode_path(p)) {
     const int n_seg = n_segments(p);
     const size_t rows = (size_t)p.B * p.Tq;
-    const size_t lists = rows * level_lists(n_seg, p.k);
-    uint32_t* keys = (uint32_t*)p.ws;
-    int32_t* pos = (int32_t*)(keys + lists * p.k);
-    int* cnt = (int*)(pos + lists * p.k);
+    const DecodeWs w = decode_ws(p);
+    char* base = (char*)p.ws;
+    uint32_t* seg_key = (uint32_t*)base;
+    int32_t* seg_pos = (int32_t*)(seg_key + w.seg_lists * w.k);
+    int* seg_cnt = (int*)(seg_pos + w.seg_lists * w.k);
+    uint32_t* lo_key = (uint32_t*)(seg_cnt + w.seg_lists);
+    uint32_t* grp_key = lo_key + w.seg_lists;
+    int32_t* grp_pos = (int32_t*)(grp_key + w.grp_lists * w.G * w.k);
+    int* grp_cnt = (int*)(grp_pos + w.grp_lists * w.G * w.k);
     hipLaunchKernelGGL(index_segment_kernel, dim3((unsigned)(rows * n_seg)), dim3(DEC_NT), 0,
-                       stream, p, n_seg, keys, pos, cnt);
+                       stream, p, n_seg, seg_key, seg_pos, seg_cnt, lo_key);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    size_t off = 0;  // lists before the current level
-    for (int n_in = n_seg;;) {
-      const int n_out = (n_in + red_g(p.k) - 1) / red_g(p.k);
-      const size_t in_off = off, out_off = off + rows * n_in;
-      hipLaunchKernelGGL(index_reduce_kernel, dim3((unsigned)(rows * n_out)), dim3(RED_NT), 0,
-                         stream, p, n_in, keys + in_off * p.k, pos + in_off * p.k,
-                         cnt + in_off, keys + out_off * p.k, pos + out_off * p.k,
-                         cnt + out_off);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      if (n_out == 1) break;
-      off = out_off;
-      n_in = n_out;
-    }
-    return hipSuccess;
+    hipLaunchKernelGGL(index_filter_kernel, dim3((unsigned)w.grp_lists), dim3(FLT_NT), 0, stream,
+                       p, n_seg, seg_key, seg_pos, seg_cnt, lo_key, grp_key, grp_pos, grp_cnt);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(index_final_kernel, dim3((unsigned)rows), dim3(FIN_NT), 0, stream, p,
+                       n_seg, grp_key, grp_pos, grp_cnt);
+    return hipGetLastError();
   }
   const long long s_ld = key_bound(p);
   const long long q_chunk = std::min<long long>(p.Tq, (long long)(p.ws_bytes / (s_ld * 4)));

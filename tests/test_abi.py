@@ -208,10 +208,11 @@ def test_index_workspace(lib):
     assert _call(lib, "dsa_index_topk", a) == lgsa.LGSA_EWORKSPACE
     d = _idx(B=8, Tq=1, S=1 << 20, max_pos=(1 << 20) - 1)
     assert lib.dsa_index_topk_workspace(ctypes.byref(d), ctypes.byref(n)) == 0
-    # decode: candidate lists of 64 segments of 16384 positions, then of the 4-way
-    # reductions (16, 4, 1 lists); each list holds k keys, k positions and a count
-    lists = 8 * (64 + 16 + 4 + 1)
-    assert n.value == lists * 2048 * 8 + lists * 4
+    # decode: candidate lists of 64 segments of 16384 positions (k keys, k positions, a count
+    # and the segment's bound each), then 16 filtered lists of 4 segments (4k keys, 4k
+    # positions and a count each)
+    seg, grp = 8 * 64, 8 * 16
+    assert n.value == seg * (2048 * 8 + 8) + grp * (4 * 2048 * 8 + 4)
 
 
 def _sp(**kw):

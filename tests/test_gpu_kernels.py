@@ -320,6 +320,22 @@ def test_index_decode_heavy_ties(torch, orc):
     assert _check_index(orc, x, g, k, [1]) >= 0
 
 
+def test_index_decode_ties_beyond_lds(torch, orc):
+    """Row 0 scores all 262144 positions exactly 0: every segment's bound equals every key, so
+    all 16 x 2048 segment candidates pass the filter, more than the final selection holds on
+    chip, and it selects over global memory: the lower-index rule gives 0 .. k-1.  Row 1 is an
+    ordinary row over the same keys, checked against the oracle."""
+    S, k = 262144, 2048
+    x = synth.dsa_index(269, B=2, Tq=1, S=S, pos0=[S - 1, S - 1])
+    x["q_idx"][0] = 0.0
+    idx = lgsa.dsa_index_topk(to_dev(x["q_idx"]), to_dev(x["w_idx"]), to_dev(x["k_idx"]),
+                              to_dev(x["pos0"]), k, max_pos=S - 1)
+    torch.cuda.synchronize()
+    g = idx.cpu().numpy()
+    assert g[0, 0].tolist() == list(range(k))
+    assert _check_index(orc, x, g, k, [1]) >= 0
+
+
 # ------------------------------------------------------------------------------ sparse
 @pytest.mark.parametrize("Tq,S,k,distinct_v,gated", [(300, 300, 128, False, True),
                                                      (200, 1000, 96, True, False),
