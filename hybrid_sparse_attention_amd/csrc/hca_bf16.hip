@@ -900,7 +900,7 @@ bool decode_fuses_gate(const HcaParams& p) {
 //                       scale * dS of every (row, key) pair: for the entries to [rows][ne_pad],
 //                       for the window to [rows][window] at column t - s;
 //   entry gradients     dKc = dSc^T Q and dVc = Pc^T dO as split-K GEMMs over all rows;
-//   hca_bwd_dkv_kernel  per 32 keys: the window gradients as banded products over the query
+//   hca_bwd_dkv_kernel  per 64 keys: the window gradients as banded products over the query
 //                       tokens s .. s + window - 1 of every head, plus dKc / block and
 //                       dVc / block of the key's block, written as dK and dV.
 __global__ __launch_bounds__(256) void hca_bwd_delta_kernel(const uint16_t* __restrict__ dout,
@@ -1079,89 +1079,133 @@ __global__ __launch_bounds__(512, 1) void hca_bwd_dq_kernel(HcaBwdParams bp, Bwd
 }
 
 constexpr int BW_CLD = 32 + 8;  // LDS row of a coefficient tile (bf16)
+constexpr int BW_NK = 64;       // keys per workgroup of the dkv kernel
+constexpr int BW_NKB = BW_NK / 16;
 
-// Window gradients of 32 keys s0 .. s0 + 31 and the final dK, dV.  Wave w owns the dims
+// Window gradients of 64 keys s0 .. s0 + 63 and the final dK, dV.  Wave w owns the dims
 // 64w .. 64w + 63.  For every query-token tile of 32 and head h: the coefficient tiles
 // C[s][t] = scale dS (or P) of (t, h) at key s when 0 <= t - s < window, and the 32 rows of Q
 // (or dO) of head h go to LDS; then dK[s][c] += sum_t C[s][t] Q[t][c] on the MFMA (A = C rows,
 // B = Q^T by the transposing read).
+// The steps of a workgroup are (token tile t0, head h) pairs, heads fastest; the Q and dO rows
+// of step i + 1 stream into one pair of LDS buffers by LDS DMA (rows past T repeat the last row:
+// their coefficients are 0) and its coefficients into registers while step i's products run on
+// the other pair, with one barrier per step.
+__shared__ __attribute__((aligned(16))) uint16_t bw_ck0[BW_NK * BW_CLD];
+__shared__ __attribute__((aligned(16))) uint16_t bw_cv0[BW_NK * BW_CLD];
+__shared__ __attribute__((aligned(16))) uint16_t bw_ck1[BW_NK * BW_CLD];
+__shared__ __attribute__((aligned(16))) uint16_t bw_cv1[BW_NK * BW_CLD];
+
 __global__ __launch_bounds__(512, 1) void hca_bwd_dkv_kernel(HcaBwdParams bp, BwdWs ws) {
-  __shared__ __attribute__((aligned(16))) uint16_t ck[32 * BW_CLD];
-  __shared__ __attribute__((aligned(16))) uint16_t cv[32 * BW_CLD];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int T = bp.T, W = bp.window, H = bp.H;
-  const int n_kt = (T + 31) / 32;
-  const int b = blockIdx.x / n_kt, s0 = (blockIdx.x % n_kt) * 32;
-  char* sq = pf_k0;  // 32 rows of Q of one head
-  char* so = pf_v0;  // 32 rows of dO of the same head
-  f32x4_t ak[2][4], av[2][4];
+  const int n_kt = (T + BW_NK - 1) / BW_NK;
+  const int b = blockIdx.x / n_kt, s0 = (blockIdx.x % n_kt) * BW_NK;
+  f32x4_t ak[BW_NKB][4], av[BW_NKB][4];
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
+  for (int sb = 0; sb < BW_NKB; ++sb)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) ak[sb][cb] = av[sb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int t_end = min(T, s0 + 31 + W);  // tokens that see one of the keys: s0 .. t_end - 1
-  for (int t0 = s0; t0 < t_end; t0 += 32) {
-    for (int h = 0; h < H; ++h) {
-      __syncthreads();
-      // rows t0 .. t0 + 31 of Q and dO for head h: 2 x 2048 chunks of 16 bytes
+  // tokens that see one of the keys: s0 .. t_end - 1
+  const int t_end = min(T, s0 + BW_NK - 1 + W);
+  const int n_steps = (t_end - s0 + 31) / 32 * H;
+  // Q and dO rows of step i: 64 rows of 1 KiB (32 of Q, then 32 of dO), eight per wave
+  auto dma_step = [&](int i, char* dq, char* dd) {
+    const int t0 = s0 + 32 * (i / H), h = i % H;
+    const uint32_t lo = (uint32_t)opaque(16 * lane);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = tid + 512 * u;  // 0..2047
-        const int rr = c >> 6, ch = c & 63;
-        const int t = t0 + rr;
-        const size_t src = (((size_t)b * T + min(t, T - 1)) * H + h) * D + 8 * ch;
-        const uint4 zq = make_uint4(0, 0, 0, 0);
-        *(uint4*)(sq + rr * KLD + 16 * ch) = t < T ? *(const uint4*)((const uint16_t*)bp.q + src) : zq;
-        *(uint4*)(so + rr * KLD + 16 * ch) = t < T ? *(const uint4*)((const uint16_t*)bp.dout + src) : zq;
-      }
-      // coefficients of keys s0 + sr and tokens t0 + tc
+    for (int u = 0; u < 8; ++u) {
+      const int row = 8 * wave + u;  // wave-uniform
+      const int rr = row & 31;
+      const int t = min(t0 + rr, T - 1);
+      const char* src = (const char*)(row < 32 ? bp.q : bp.dout) +
+                        ((((size_t)b * T + t) * H + h) * D) * 2;
+      lds_dma16(src + lo, (row < 32 ? dq : dd) + rr * KLD);
+    }
+  };
+  // coefficients of keys s0 + sr and tokens t0 + tc, BW_NK / 16 (sr, tc) per thread
+  uint16_t cfk[BW_NK / 16], cfv[BW_NK / 16];
+  auto load_coef = [&](int i) {
+    const int t0 = s0 + 32 * (i / H), h = i % H;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = tid + 512 * u;  // 0..1023
-        const int sr = e >> 5, tc = e & 31;
-        const int s = s0 + sr, t = t0 + tc, jj = t - s;
-        uint16_t vk = 0, vv = 0;
-        if (t < T && s < T && jj >= 0 && jj < W) {
-          const size_t at = (((size_t)b * T + t) * H + h) * W + jj;
-          vk = ws.dsw[at];
-          vv = ws.pw[at];
-        }
-        ck[sr * BW_CLD + tc] = vk;
-        cv[sr * BW_CLD + tc] = vv;
-      }
-      __syncthreads();
-      // A = coefficient rows (keys 16sb + l16, tokens 8g .. 8g + 7); B = Q^T / dO^T columns
-      // 64 wave + 16cb + l16 of tokens 8g .. 8g + 7 (two transposed reads of 4 rows each)
-      Frag8 fk[2], fv[2];
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        fk[sb].u = *(const uint4*)(&ck[(16 * sb + l16) * BW_CLD + 8 * g]);
-        fv[sb].u = *(const uint4*)(&cv[(16 * sb + l16) * BW_CLD + 8 * g]);
-      }
-      const int rowa = (8 * g + (l16 >> 2)) * KLD + 2 * (64 * wave + 4 * (l16 & 3));
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        Frag8 bq, bo;
-        const uint2 q0 = lds_read_tr16(sq + rowa + 32 * cb);
-        const uint2 q1 = lds_read_tr16(sq + rowa + 32 * cb + 4 * KLD);
-        const uint2 o0 = lds_read_tr16(so + rowa + 32 * cb);
-        const uint2 o1 = lds_read_tr16(so + rowa + 32 * cb + 4 * KLD);
-        bq.u = make_uint4(q0.x, q0.y, q1.x, q1.y);
-        bo.u = make_uint4(o0.x, o0.y, o1.x, o1.y);
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          ak[sb][cb] = mfma_16x16x32(fk[sb], bq, ak[sb][cb]);
-          av[sb][cb] = mfma_16x16x32(fv[sb], bo, av[sb][cb]);
-        }
+    for (int u = 0; u < BW_NK / 16; ++u) {
+      const int e = tid + 512 * u;  // 0 .. 32 BW_NK - 1
+      const int sr = e >> 5, tc = e & 31;
+      const int s = s0 + sr, t = t0 + tc, jj = t - s;
+      cfk[u] = cfv[u] = 0;
+      if (t < T && s < T && jj >= 0 && jj < W) {
+        const size_t at = (((size_t)b * T + t) * H + h) * W + jj;
+        cfk[u] = ws.dsw[at];
+        cfv[u] = ws.pw[at];
       }
     }
+  };
+  auto store_coef = [&](uint16_t* ck, uint16_t* cv) {
+#pragma unroll
+    for (int u = 0; u < BW_NK / 16; ++u) {
+      const int e = tid + 512 * u;
+      const int sr = e >> 5, tc = e & 31;
+      ck[sr * BW_CLD + tc] = cfk[u];
+      cv[sr * BW_CLD + tc] = cfv[u];
+    }
+  };
+  // A = coefficient rows (keys 16sb + l16, tokens 8g .. 8g + 7); B = Q^T / dO^T columns
+  // 64 wave + 16cb + l16 of tokens 8g .. 8g + 7 (two transposed reads of 4 rows each)
+  const int rowa = (8 * g + (l16 >> 2)) * KLD + 2 * (64 * wave + 4 * (l16 & 3));
+  auto compute = [&](const char* sq, const char* so, const uint16_t* ck, const uint16_t* cv) {
+    Frag8 fk[BW_NKB], fv[BW_NKB];
+#pragma unroll
+    for (int sb = 0; sb < BW_NKB; ++sb) {
+      fk[sb].u = *(const uint4*)(&ck[(16 * sb + l16) * BW_CLD + 8 * g]);
+      fv[sb].u = *(const uint4*)(&cv[(16 * sb + l16) * BW_CLD + 8 * g]);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      Frag8 bq, bo;
+      const uint2 q0 = lds_read_tr16(sq + rowa + 32 * cb);
+      const uint2 q1 = lds_read_tr16(sq + rowa + 32 * cb + 4 * KLD);
+      const uint2 o0 = lds_read_tr16(so + rowa + 32 * cb);
+      const uint2 o1 = lds_read_tr16(so + rowa + 32 * cb + 4 * KLD);
+      bq.u = make_uint4(q0.x, q0.y, q1.x, q1.y);
+      bo.u = make_uint4(o0.x, o0.y, o1.x, o1.y);
+#pragma unroll
+      for (int sb = 0; sb < BW_NKB; ++sb) {
+        ak[sb][cb] = mfma_16x16x32(fk[sb], bq, ak[sb][cb]);
+        av[sb][cb] = mfma_16x16x32(fv[sb], bo, av[sb][cb]);
+      }
+    }
+  };
+  if (n_steps > 0) {
+    dma_step(0, pf_k0, pf_v0);
+    load_coef(0);
+  }
+  wait_all();
+  store_coef(bw_ck0, bw_cv0);
+  __syncthreads();
+  // step i reads buffers (q, o, ck, cv) of its parity; step i + 1 fills the other set, whose
+  // previous contents step i - 1 read before the barrier that ended it
+  auto step = [&](int i, const char* q, const char* o, const uint16_t* ck, const uint16_t* cv,
+                  char* qn, char* on, uint16_t* ckn, uint16_t* cvn) {
+    const bool more = i + 1 < n_steps;
+    if (more) {
+      dma_step(i + 1, qn, on);
+      load_coef(i + 1);
+    }
+    compute(q, o, ck, cv);
+    wait_all();  // this wave's transfers and coefficients of step i + 1
+    if (more) store_coef(ckn, cvn);
+    __syncthreads();
+  };
+  for (int i = 0; i < n_steps; i += 2) {
+    step(i, pf_k0, pf_v0, bw_ck0, bw_cv0, pf_k1, pf_v1, bw_ck1, bw_cv1);
+    if (i + 1 < n_steps) step(i + 1, pf_k1, pf_v1, bw_ck1, bw_cv1, pf_k0, pf_v0, bw_ck0, bw_cv0);
   }
   // lane holds dK, dV[s = s0 + 16sb + 4g + r][c = 64 wave + 16cb + l16]
   const float inv_blk = 1.0f / (float)bp.block;
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
+  for (int sb = 0; sb < BW_NKB; ++sb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int s = s0 + 16 * sb + 4 * g + r;
@@ -1248,7 +1292,8 @@ hipError_t launch_hca_bwd(const HcaBwdParams& p, hipStream_t stream) {
                                w.splits, w.part, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(hca_bwd_dkv_kernel, dim3((unsigned)(p.B * ((p.T + 31) / 32))), dim3(512),
+  hipLaunchKernelGGL(hca_bwd_dkv_kernel, dim3((unsigned)(p.B * ((p.T + BW_NK - 1) / BW_NK))),
+                     dim3(512),
                      0, stream, p, w);
   return hipGetLastError();
 }

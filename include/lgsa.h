@@ -300,6 +300,19 @@ typedef struct {
 lgsa_status sparse_attn_fwd(const lgsa_sparse_args* a, void* stream);
 lgsa_status sparse_attn_fwd_workspace(const lgsa_sparse_args* a, size_t* bytes);
 
+/* Compressed sparse attention (release blog, section 2.1: history compressed 4x, then a sparse
+ * part of it attended) has no entry point of its own: a caller composes it from the calls
+ * above, on one stream.
+ *   1. hca_compress(k, v, kc, vc, B, T, 256, block = 4, LGSA_BF16): pooled keys and values,
+ *      [B, T / 4, 256], used as separate key and value rows;
+ *   2. hca_compress(k_idx, k_idx, kic, kic2, B, T, 64, 4, LGSA_F32): pooled indexer keys
+ *      (kic2 receives the same values and may be discarded);
+ *   3. dsa_index_topk with k_idx = kic, S = T / 4 and block = 4: query t sees the entries whose
+ *      block is complete, s < (t + 1) / 4, and keeps the top k;
+ *   4. sparse_attn_fwd with k_lat = kc, v_lat = vc (row strides 256), S = T / 4, the lists of
+ *      step 3 and, when gated, q_lat and w_gate.
+ * The binding's csa_attn_fwd does exactly this. */
+
 /* ---------------------------------------------------------------------------------------
  * sparse_attn_bwd -- backward of sparse_attn_fwd (the chain rule of its definition; the
  * pages' training is the reason to have it).  For query row (b, i), head h, the listed keys
