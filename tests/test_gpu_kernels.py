@@ -162,12 +162,14 @@ def test_hca_prefill_f32_config0(torch, orc):
 
 @pytest.mark.parametrize("contexts,gated", [([1000, 130, 5], True), ([131072], False),
                                             ([128, 127, 129, 256], True), ([20, 3], True),
-                                            ([300] * 65, True)])
+                                            ([300] * 65, True), ([50] * 64, True),
+                                            ([100] * 63 + [20], True)])
 def test_hca_decode_bf16(torch, orc, contexts, gated):
-    """Decode against the oracle.  Gated with at most 64 sequences, the attention kernel's
-    workgroups compute the gate factors, with gate-only workgroups added when the key splits
-    are few ([1000, 130, 5]) and partials merged even for a single split ([20, 3]); 65
-    sequences take the gate GEMM after the merge."""
+    """Decode against the oracle.  Gated with at most 64 sequences and at most four key
+    splits, the gate kernel merges the splits in its epilogue: one split ([20, 3]), two
+    ([50] x 64) and four (63 sequences at 100 and one at 20, whose last splits are empty);
+    more splits ([1000, 130, 5], [128, 127, 129, 256]) and 65 sequences take the combine
+    kernel, then the gate GEMM."""
     B = len(contexts)
     x = synth.hca_decode(240 + B, B=B, context=max(contexts), H=64, contexts=contexts,
                          gated=gated)
@@ -293,9 +295,10 @@ def test_index_prefill_tie_group_in_threshold_bin(torch, orc):
     assert straddled > 0  # some row's k-th score lies in the group
 
 
-@pytest.mark.parametrize("pos0", [[39999, 20000, 1500], [16383, 16384, 2047]])
-def test_index_decode(torch, orc, pos0):
-    S, k = 40000, 2048
+@pytest.mark.parametrize("pos0,k", [([39999, 20000, 1500], 2048), ([16383, 16384, 2047], 2048),
+                                   ([39999, 33000, 999], 1000)])
+def test_index_decode(torch, orc, pos0, k):
+    S = 40000
     x = synth.dsa_index(267, B=3, Tq=1, S=S, pos0=pos0)
     idx = lgsa.dsa_index_topk(to_dev(x["q_idx"]), to_dev(x["w_idx"]), to_dev(x["k_idx"]),
                               to_dev(x["pos0"]), k, max_pos=max(pos0))
