@@ -4,14 +4,14 @@ whole compared set.
 
 What is compared:
   - tiny HCA prefill (fp32): every row, every head;
-  - model-shape HCA prefill: the compressor's entries in full; the attention output on the
-    declared row sample of helpers.declared_rows (first and last 256 rows, both rows at each
-    of the 256 block boundaries, 2048 seeded random rows: about 3000 of 32768 rows), all 64
-    heads, every channel;
+  - model-shape HCA prefill: the compressor's entries in full; the attention output in full
+    (every one of the 32768 rows, all 64 heads, every channel; the same shape with unit
+    variance inputs on the declared row sample of helpers.declared_rows);
   - HCA decode: all 64 sequences, all heads;
   - DSA prefill: the top-k of every row t = 2040 .. 2180 (the k-th score is exactly 0 there,
     so the lower-index rule decides) plus first/last rows and seeded random rows (about 300);
-    sparse attention on the declared row sample of its 65536 rows (about 3500);
+    sparse attention on the declared row sample of its 65536 rows (about 3500); every row of
+    both in test_gpu_full_rows.py, which runs with LGSA_FULL_PARITY=1 (five minutes of oracle);
   - mixed long-context decode: all 8 sequences of every part.
 Inputs are the seeded synthetic tensors of each configuration.
 """
@@ -67,7 +67,8 @@ def test_config0_hca_prefill_tiny_fp32(torch, orc):
 
 def test_config1_hca_prefill_model_shape(torch, orc):
     """seq 32768, 64 heads, head dim 512, bf16, inputs N(0,1)/sqrt(512), gated: the entries in
-    full and the declared row sample of the output (about 3000 rows, all heads)."""
+    full and every row of the output (all heads), compared in chunks of 4096 rows as the
+    oracle produces them; the tolerance is taken over the whole output tensor."""
     T, H = 32768, 64
     x = synth.hca_prefill(1, T=T, H=H, qkv_scale=1.0 / math.sqrt(512))
     kd, vd = to_dev(x["k"]), to_dev(x["v"])
@@ -78,11 +79,18 @@ def test_config1_hca_prefill_model_shape(torch, orc):
     okc, ovc = orc.hca_compress(x["k"]), orc.hca_compress(x["v"])
     bf16_ok(from_dev(kc), okc, "config1 compress k")
     bf16_ok(from_dev(vc), ovc, "config1 compress v")
-    rows = declared_rows(T, 11)
-    ref = orc.hca_attn(x["q"], x["pos0"], x["k"], x["v"], okc, ovc, q_lat=x["q_lat"],
-                       w_gate=x["w_gate"], rows=rows)
-    err, tol = bf16_ok(rows_of(out, rows), ref, "config1")
-    _report("config1", err, tol, len(rows))
+    err = ref_max = 0.0
+    for r0 in range(0, T, 4096):
+        rows = np.arange(r0, min(T, r0 + 4096))
+        ref = orc.hca_attn(x["q"], x["pos0"], x["k"], x["v"], okc, ovc, q_lat=x["q_lat"],
+                           w_gate=x["w_gate"], rows=rows)
+        got = from_dev(out[0, r0:r0 + len(rows)])
+        assert np.all(np.isfinite(got)), "config1: non-finite output"
+        err = max(err, float(np.max(np.abs(got - ref))))
+        ref_max = max(ref_max, float(np.max(np.abs(ref))))
+    tol = 1e-2 * ref_max + 1e-3
+    _report("config1", err, tol, T)
+    assert err <= tol, "config1: max|err| %.3g > tol %.3g" % (err, tol)
 
 
 def test_config1_shape_unit_variance(torch, orc):
