@@ -159,11 +159,14 @@ __shared__ __attribute__((aligned(1024))) char pf_v0[VTILE];
 __shared__ __attribute__((aligned(1024))) char pf_v1[VTILE];
 
 // S^T of one key tile over the whole head dimension for the wave's 16 rows: A = key row
-// 16mb + l16 with dims 32kk + 8g .. +7, B = query row l16 with the same dims.
+// 16mb + l16 with dims 32kk + 8g .. +7, B = query row l16 with the same dims.  The even and
+// odd contraction steps accumulate separately and are summed at the end: four independent
+// chains of 8 products instead of two of 16.
 __device__ __forceinline__ void row_scores(f32x4_t (&s)[2], const Frag8 (&qf)[16],
                                            const char* ks, int lane) {
   const int l16 = lane & 15, g = lane >> 4;
   s[0] = s[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t s_odd[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
   const char* a0 = ks + l16 * KLD + 16 * g;
 #pragma unroll
   for (int kk = 0; kk < 16; ++kk) {
@@ -171,8 +174,13 @@ __device__ __forceinline__ void row_scores(f32x4_t (&s)[2], const Frag8 (&qf)[16
     ka[0].u = *(const uint4*)(a0 + 64 * kk);
     ka[1].u = *(const uint4*)(a0 + 64 * kk + 16 * KLD);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) s[mb] = mfma_16x16x32(ka[mb], qf[kk], s[mb]);
+    for (int mb = 0; mb < 2; ++mb) {
+      if (kk & 1) s_odd[mb] = mfma_16x16x32(ka[mb], qf[kk], s_odd[mb]);
+      else s[mb] = mfma_16x16x32(ka[mb], qf[kk], s[mb]);
+    }
   }
+  s[0] += s_odd[0];
+  s[1] += s_odd[1];
 }
 
 // Online softmax of one tile's scores (masked unless the tile is fully visible), then
