@@ -44,17 +44,38 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(const Frag8& a, const Frag8& b,
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
 }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 that hold the same MFMA column, with the
+// VALU lane swaps of gfx950 instead of LDS permutes.  v_permlane16_swap(x, x) leaves in each
+// lane of rows 2i and 2i + 1 (16 lanes each) the pair (row 2i's x, row 2i + 1's x) of its
+// position; v_permlane32_swap(x, x) leaves the pair (lower half's x, upper half's x).  Every
+// lane thus combines the same two values in the same order, so all four lanes of a column
+// end with the same bits.
+__device__ __forceinline__ void pair16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ void pair32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_max16(float v) {
-  // reduce over the four lanes l, l^16, l^32, l^48 that hold the same MFMA column
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  float a, b;
+  pair16(v, a, b);
+  pair32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
 }
 
 __device__ __forceinline__ float wave_sum16(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  float a, b;
+  pair16(v, a, b);
+  pair32(a + b, a, b);
+  return a + b;
 }
 
 // Transposes an 8x8 block of bfloat16 held as eight 16-byte rows r[0..7] (row j holds
