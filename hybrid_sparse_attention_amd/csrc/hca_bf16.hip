@@ -196,12 +196,25 @@ __device__ __forceinline__ void row_softmax_pv(RowState& st, const f32x4_t (&s)[
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[mb][r] = s[mb][r] * scale_log2;
   } else {
+    // the keys j of the tile that the lane's row (position tr) sees form one range
+    // [j_lo, j_hi], the rule of visible() solved for j once per tile
     const int tr = row_t(rp, opaque(l16));
+    int j_lo, j_hi;
+    if (t.kind == 0) {  // entries: block (s + 1) <= tr + 1
+      j_lo = 0;
+      j_hi = tr >= 0 ? (tr + 1) / rp.block - 1 - t.start : -1;
+    } else {  // raw positions: tr - window + 1 <= s <= tr
+      j_lo = tr - rp.window + 1 - t.start;
+      j_hi = tr - t.start;
+    }
+    j_hi = min(j_hi, t.count - 1);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        x[mb][r] = visible(t, 16 * mb + 4 * g + r, tr, rp) ? s[mb][r] * scale_log2 : NEG_BIG;
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * mb + 4 * g + r;
+        x[mb][r] = (j >= j_lo && j <= j_hi) ? s[mb][r] * scale_log2 : NEG_BIG;
+      }
   }
   float mx = x[0][0];
 #pragma unroll
