@@ -448,7 +448,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // Step k0 of the gate contraction into one stage: rows k0 + 4 wave .. + 3 of the head's W
-// slice (1 KiB each) into a tile of pitch VLD, and the wave's 16 q_lat rows, columns
+// slice (1 KiB each) into a tile of pitch VLD, contraction index k0 + 8c + 4h + a (c, h, a
+// < 4, 2, 4) at tile row 16h + 4c + a, and the wave's 16 q_lat rows, columns
 // k0 .. k0 + 31 (64 bytes each), into its own 1 KiB of the q_lat tile of the stage, which
 // holds the workgroup's 128 rows: lane l lands at row l / 4, 16-byte slot l % 4, and fetches
 // chunk (l % 4) ^ ((row / 4) % 4) of that row, so that the fragment reads of 16 rows hit
@@ -460,9 +461,9 @@ __device__ __forceinline__ void gate_dma(const char* w_head, size_t ldw, const c
                                          int wave, int lane) {
   const uint32_t lo = (uint32_t)opaque(16 * lane);
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 4; ++u)  // index 4 wave + u: c = wave / 2, h = wave % 2, a = u
     dma16_asm(w_head + (size_t)(k0 + 4 * wave + u) * ldw, lo,
-              lds_addr(wdst + (4 * wave + u) * VLD));
+              lds_addr(wdst + (16 * (wave & 1) + 4 * (wave >> 1) + u) * VLD));
   dma16_asm(ql_wave + 2 * k0, (uint32_t)opaque((int)q_off), lds_addr(qdst + 1024 * wave));
 }
 
@@ -471,10 +472,11 @@ __device__ __forceinline__ int ql_chunk(int r, int c) { return 64 * r + 16 * (c 
 
 // One contraction step of 32 for the wave's 64 channels (64 wave .. + 63 of the head) and all
 // 128 rows of the tile: G^T = W^T q_lat^T, acc[i][j] = G^T of channels 64 wave + 16 i .. and
-// rows 16 j ..  W^T comes from the stage's W tile through the transposing read (rows 4g + a and
-// 16 + 4g + a: contraction columns 4g .. 4g + 3 in slots 8g .. 8g + 3, 16 + 4g .. in slots
-// 8g + 4 ..), q_lat^T from the stage's q_lat tile in the same slot order.  Each W^T fragment
-// feeds 8 products and each q_lat fragment 4.
+// rows 16 j ..  W^T comes from the stage's W tile through the transposing read of tile rows
+// 4g + a and 16 + 4g + a, which hold contraction indices 8g + a and 8g + 4 + a: slots
+// 8g .. 8g + 7 take indices 8g .. 8g + 7 in order, so the q_lat^T fragment of a lane is one
+// 16-byte chunk of its q_lat row.  Each W^T fragment feeds 8 products and each q_lat fragment
+// 4.
 __device__ __forceinline__ void gate_step(f32x4_t (&acc)[4][8], const char* ws, const char* qs,
                                           int wave, int lane) {
   const int l16 = lane & 15, g = lane >> 4;
@@ -486,14 +488,10 @@ __device__ __forceinline__ void gate_step(f32x4_t (&acc)[4][8], const char* ws, 
     const uint2 hi = lds_read_tr16(v0 + 32 * i + 16 * VLD);
     wa[i].u = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
-  const int c0 = g >> 1, b8 = 8 * (g & 1);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int r = 16 * j + l16;
     Frag8 qf;
-    const uint2 lo = *(const uint2*)(qs + ql_chunk(r, c0) + b8);
-    const uint2 hi = *(const uint2*)(qs + ql_chunk(r, 2 + c0) + b8);
-    qf.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    qf.u = *(const uint4*)(qs + ql_chunk(16 * j + l16, g));
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i][j] = mfma_16x16x32(wa[i], qf, acc[i][j]);
   }
