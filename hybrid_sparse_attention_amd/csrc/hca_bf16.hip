@@ -451,9 +451,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // slice (1 KiB each) into a tile of pitch VLD, contraction index k0 + 8c + 4h + a (c, h, a
 // < 4, 2, 4) at tile row 16h + 4c + a, and the wave's 16 q_lat rows, columns
 // k0 .. k0 + 31 (64 bytes each), into its own 1 KiB of the q_lat tile of the stage, which
-// holds the workgroup's 128 rows: lane l lands at row l / 4, 16-byte slot l % 4, and fetches
-// chunk (l % 4) ^ ((row / 4) % 4) of that row, so that the fragment reads of 16 rows hit
-// distinct banks.  Five transfers per wave.
+// holds the workgroup's 128 rows: chunk-major within each 16-row block, lane l fetching
+// 16-byte chunk l / 16 of row l % 16, so that a fragment read (chunk g of rows l16) is 1 KiB
+// read contiguously by the 64 lanes, which the LDS serves without bank conflicts.  Five
+// transfers per wave.
 // ql_wave is the q_lat row of the wave's first row and q_off the lane's byte offset from it
 // (its row, clamped to the last row, and its chunk).
 __device__ __forceinline__ void gate_dma(const char* w_head, size_t ldw, const char* ql_wave,
@@ -467,8 +468,8 @@ __device__ __forceinline__ void gate_dma(const char* w_head, size_t ldw, const c
   dma16_asm(ql_wave + 2 * k0, (uint32_t)opaque((int)q_off), lds_addr(qdst + 1024 * wave));
 }
 
-// Byte offset in a q_lat tile of columns 8c' .. of row r, c' the 16-byte chunk (0..3).
-__device__ __forceinline__ int ql_chunk(int r, int c) { return 64 * r + 16 * (c ^ ((r >> 2) & 3)); }
+// Byte offset in a q_lat tile of columns 8c .. 8c + 7 of row r, c the 16-byte chunk (0..3).
+__device__ __forceinline__ int ql_chunk(int r, int c) { return 1024 * (r >> 4) + 256 * c + 16 * (r & 15); }
 
 // One contraction step of 32 for the wave's 64 channels (64 wave .. + 63 of the head) and all
 // 128 rows of the tile: G^T = W^T q_lat^T, acc[i][j] = G^T of channels 64 wave + 16 i .. and
@@ -615,8 +616,8 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_gated_kernel(HcaParams p) 
   // the wave's first q_lat row; rows past the end read the last row (and are never stored)
   const int r_dma = min(r_first, i_end - 1);
   const char* ql_wave = (const char*)p.q_lat + ((size_t)b * p.Tq + r_dma) * ldq;
-  const uint32_t q_off = (uint32_t)((min(r_first + (lane >> 2), i_end - 1) - r_dma) * (int)ldq +
-                                    16 * ((lane & 3) ^ ((lane >> 4) & 3)));
+  const uint32_t q_off = (uint32_t)((min(r_first + (lane & 15), i_end - 1) - r_dma) * (int)ldq +
+                                    16 * (lane >> 4));
   const int nk = p.d_lat / KT;  // contraction steps of 32
   f32x4_t acc[4][8];
 #pragma unroll
