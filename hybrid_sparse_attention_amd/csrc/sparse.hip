@@ -12,9 +12,9 @@
 // rows) and double buffered.  When the value rows are the key rows the
 // single tile serves both products: S^T = K Q^T reads it row-wise, O^T = V^T P^T reads it
 // through the transposing LDS read, so each gathered row crosses the memory system once.
-// The 16-byte chunks of a row are XOR-swizzled (chunk c of row r sits at position c ^ sw(r))
-// so that both read patterns are free of bank conflicts; the DMA applies the swizzle by
-// choosing which chunk each lane fetches.  Long lists of few query rows are split over several
+// The 16-byte chunks of a row are rotated (chunk c of row r at position
+// (c + 2r + 16 (r & 1)) mod 32) so that both read patterns run at the LDS's full rate; the DMA
+// applies the rotation by choosing which chunk each lane fetches.  Long lists of few query rows are split over several
 // workgroups, whose partial (max, sum, O) a combine kernel merges.  The output gate runs
 // afterwards as the gate GEMM in place (a per-row workgroup would have to read the whole gate
 // matrix).
@@ -49,18 +49,21 @@ struct WaveState {
   float l[NHB];        // running partial sum of this lane's keys
 };
 
+// kr = l16 * TROW and kc = g + 2 l16 + 16 (l16 & 1): key row 16mb + l16, chunk 4kk + g sits at
+// position (4kk + kc) mod 32 (rows 16 apart share positions)
 template <int NHB>
 __device__ __forceinline__ void scores(f32x4_t (&s)[NHB][2], const Frag8 (&qf)[NHB][8],
-                                       const char* kt, const int (&kb)[4]) {
+                                       const char* kt, int kr, int kc) {
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) s[hb][0] = s[hb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int kc_t = opaque(kc);  // formed per tile, so the 8 positions are not kept live
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
     Frag8 ka[2];
-    // key row 16mb + l16, chunk 4kk + g: position ((4(kk & 3) + g) ^ sw) + 16(kk >> 2)
+    const int off = kr + 16 * ((4 * kk + kc_t) & 31);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
-      ka[mb].u = *(const uint4*)(kt + kb[kk & 3] + 256 * (kk >> 2) + 16 * TROW * mb);
+      ka[mb].u = *(const uint4*)(kt + off + 16 * TROW * mb);
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
@@ -71,7 +74,7 @@ __device__ __forceinline__ void scores(f32x4_t (&s)[NHB][2], const Frag8 (&qf)[N
 template <int NHB>
 __device__ __forceinline__ void softmax_pv(WaveState<NHB>& st, const f32x4_t (&s)[NHB][2],
                                            const char* vt, uint32_t valid, float scale_log2,
-                                           int vrow, int vsw, int vh, int lane) {
+                                           int vrow, int vc, int lane) {
   const int g = lane >> 4;
   Frag8 pf[NHB];
 #pragma unroll
@@ -106,14 +109,14 @@ __device__ __forceinline__ void softmax_pv(WaveState<NHB>& st, const f32x4_t (&s
     pf[hb].u = make_uint4(pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
                           pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3]));
   }
-  // V^T fragment of column block cb: transposed reads of rows vrow (slots 8g..8g+3) and
-  // vrow + 16 (slots 8g+4..8g+7), columns 16cb + 4(l16 % 4) .. +3 = chunk 2cb + vh, half
-  // l16 & 1 of it, the chunk found at its swizzled position; each fragment serves all the
-  // wave's head blocks
-  const int vh_t = opaque(vh);  // formed per tile, so the 16 positions are not kept live
+  // V^T fragment of column block cb: transposed reads of rows vr (slots 8g..8g+3) and
+  // vr + 16 (slots 8g+4..8g+7), columns 16cb + 4(l16 % 4) .. +3 = chunk 2cb + vh, half
+  // l16 & 1 of it, the chunk found at position (2cb + vc) mod 32, vc = vh + 2vr + 16 (vr & 1);
+  // each fragment serves all the wave's head blocks
+  const int vc_t = opaque(vc);  // formed per tile, so the 16 positions are not kept live
 #pragma unroll
   for (int cb = 0; cb < 16; ++cb) {
-    const int pos = (2 * cb + vh_t) ^ vsw;
+    const int pos = (2 * cb + vc_t) & 31;
     const char* a = vt + vrow + 16 * pos;
     Frag8 va;
     const uint2 lo = lds_read_tr16(a);
@@ -175,14 +178,10 @@ void sparse_kernel(SparseParams p, int n_split, int chunk, float* part_o, float*
 
   // lane-constant LDS offsets: key reads (row l16 / l16 + 16, chunk 4kk + g) and transposed
   // value reads (rows 4g + l16/4 and +16, chunk 2cb + (l16 & 3)/2, half l16 & 1)
-  const int ksw = sw(l16);
-  int kb[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) kb[q] = l16 * TROW + 16 * ((4 * q + g) ^ ksw);
+  const int kr = l16 * TROW, kcol = g + 2 * l16 + 16 * (l16 & 1);
   const int vr = 4 * g + (l16 >> 2);
   const int vrow = vr * TROW + 8 * (l16 & 1);
-  const int vsw = sw(vr);
-  const int vh = (l16 & 3) >> 1;
+  const int vcol = ((l16 & 3) >> 1) + 2 * vr + 16 * (vr & 1);
 
   const int32_t* idx = p.idx + (size_t)r * p.k;
   const uint16_t* kl = (const uint16_t*)p.k_lat + (size_t)b * p.S * p.k_stride;
@@ -209,8 +208,8 @@ void sparse_kernel(SparseParams p, int n_split, int chunk, float* part_o, float*
     }
     const int ix_after = load_ix(idx, j_begin + KT * (ti + 2), j_end, lane);
     f32x4_t s[NHB][2];
-    scores(s, qf, kc, kb);
-    softmax_pv(st, s, ALIAS ? kc : vc, valid_cur, scale_log2, vrow, vsw, vh, lane);
+    scores(s, qf, kc, kr, kcol);
+    softmax_pv(st, s, ALIAS ? kc : vc, valid_cur, scale_log2, vrow, vcol, lane);
     wait_all();  // this wave's gathers of tile ti + 1 and the positions of tile ti + 2
     __syncthreads();
     valid_cur = valid_nxt;
@@ -406,7 +405,7 @@ using namespace sparse_tile;
 // The gathers of sparse_kernel<true> alone: one workgroup of two waves per index list, tiles of
 // 32 listed rows brought to LDS by the same DMA pattern and double buffering.  So that the
 // transfers are used, wave w adds up the first 64 words of tile row 16 w of every tile (rows 0
-// and 16 are stored unswizzled), uint32 with wrap-around: sums[list][w].
+// and 16 are stored unrotated), uint32 with wrap-around: sums[list][w].
 __global__ __launch_bounds__(128) void gather_probe_kernel(const uint16_t* __restrict__ rows,
                                                            long long stride, int S,
                                                            const int32_t* __restrict__ idx,

@@ -218,14 +218,12 @@ void sparse_bwd_kernel(SparseBwdParams p, long long row0, const int32_t* __restr
 
   // lane-constant LDS offsets: key rows 16kh + l16 read row-wise (as the forward's scores) and
   // the transposing reads of K^T (rows 4g + l16/4 and +16, as the forward's V^T)
-  const int ksw = sw(l16);
-  int kb[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) kb[c] = l16 * TROW + 16 * ((4 * c + g) ^ ksw) + 16 * TROW * kh;
+  // key row 16kh + l16, chunk 4kk + g at position (4kk + kcol) mod 32
+  const int kb = l16 * TROW + 16 * TROW * kh, kcol = g + 2 * l16 + 16 * (l16 & 1);
   const int vr = 4 * g + (l16 >> 2);
   const int vrow = vr * TROW + 8 * (l16 & 1);
-  const int vsw = sw(vr);
-  const int vh = (l16 & 3) >> 1;
+  // K^T reads: chunk 2j + vh of rows vr, vr + 16 at position (2j + vcol) mod 32
+  const int vcol = ((l16 & 3) >> 1) + 2 * vr + 16 * (vr & 1);
   // dS^T operand of dq^T: column = head hl, contraction slots 8g .. 8g+7 = keys 4g .. 4g+3 and
   // 16 + 4g .. 16 + 4g + 3 (the order the K^T read gives)
   const int dsb = (4 * g + (l16 >> 2)) * PROW + 2 * (16 * hb + 4 * (l16 & 3));
@@ -241,13 +239,14 @@ void sparse_bwd_kernel(SparseBwdParams p, long long row0, const int32_t* __restr
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       Frag8 ka;
-      ka.u = *(const uint4*)(kx + kb[kk & 3] + 256 * (kk >> 2));
+      const int ko = kb + 16 * ((4 * kk + kcol) & 31);
+      ka.u = *(const uint4*)(kx + ko);
       s = mfma_16x16x32(ka, qf[kk], s);
       if (ALIAS) {
         dp = mfma_16x16x32(ka, df[kk], dp);
       } else {
         Frag8 va;
-        va.u = *(const uint4*)(vx + kb[kk & 3] + 256 * (kk >> 2));
+        va.u = *(const uint4*)(vx + ko);
         dp = mfma_16x16x32(va, df[kk], dp);
       }
     }
@@ -280,12 +279,13 @@ void sparse_bwd_kernel(SparseBwdParams p, long long row0, const int32_t* __restr
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) ck[mb][nb] = cv[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int vh_t = opaque(vh);
+    const int vc_t = opaque(vcol);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       Frag8 ka;
-      ka.u = *(const uint4*)(kx + kb[kk & 3] + 256 * (kk >> 2));
-      const int pos = (2 * (8 * kh + kk) + vh_t) ^ vsw;
+      const int ko = kb + 16 * ((4 * kk + kcol) & 31);
+      ka.u = *(const uint4*)(kx + ko);
+      const int pos = (2 * (8 * kh + kk) + vc_t) & 31;
       const char* at = kc + vrow + 16 * pos;
       const uint2 lo = lds_read_tr16(at);
       const uint2 hi = lds_read_tr16(at + 16 * TROW);
@@ -296,7 +296,7 @@ void sparse_bwd_kernel(SparseBwdParams p, long long row0, const int32_t* __restr
         dp = mfma_16x16x32(ka, df[kk], dp);
       } else {
         Frag8 va;
-        va.u = *(const uint4*)(vx + kb[kk & 3] + 256 * (kk >> 2));
+        va.u = *(const uint4*)(vx + ko);
         dp = mfma_16x16x32(va, df[kk], dp);
       }
       dq[kk] = mfma_16x16x32(kq, bds, dq[kk]);
