@@ -508,21 +508,22 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_gated_kernel(HcaParams p) 
   const int l16 = lane & 15, g = lane >> 4;
   const int n_qt = (p.Tq + FQ - 1) / FQ;
   // XCD-aware order (consecutive ids go to the 8 XCDs in turn): XCD x takes the heads
-  // x H/8 .. x H/8 + H/8 - 1 of every token tile, token tiles taken alternately from the
-  // longest and the shortest key lists, and the heads of a tile one after another.  The ~32
-  // workgroups an XCD holds at once are then 4 token tiles x 8 heads: each key/value tile is
-  // read by 8 of them from the XCD's L2, and each head's W slice by 4.
+  // x H/8 .. x H/8 + H/8 - 1 of every token tile, token tiles in descending order (longer key
+  // lists first) from a starting point of its own, and the heads of a tile one after another.
+  // The ~32 workgroups an XCD holds at once are then 4 token tiles x 8 heads: each key/value
+  // tile is read by 8 of them from the XCD's L2, and each head's W slice by 4.
   int qt, h, b;
   if (p.H % 8 == 0) {
     const int hx = p.H / 8, idx = blockIdx.x / 8;
     h = (blockIdx.x % 8) * hx + idx % hx;
     const int tt = idx / hx;  // (sequence, rank of the token tile in the order below)
     b = tt / n_qt;
-    // alternately from the long end and the short end of the tile order, so the workgroups
-    // in flight differ in key-list length and drift apart: their Q loads and out stores then
-    // spread over the launch instead of all CUs moving Q or out at the same moment
+    // descending from a starting tile that differs by XCD (x n_qt / 8), wrapping around: the
+    // workgroups of one XCD stay in step (they share W slices and key tiles in its L2), while
+    // the 8 XCDs are at different points of the order, so their Q loads and out stores spread
+    // over the launch instead of all CUs moving Q or out at the same moment
     const int u = tt % n_qt;
-    qt = (u & 1) ? u / 2 : n_qt - 1 - u / 2;
+    qt = n_qt - 1 - (u + (int)(blockIdx.x % 8) * (n_qt / 8)) % n_qt;
   } else {
     qt = n_qt - 1 - (int)blockIdx.x % n_qt;
     h = (blockIdx.x / n_qt) % p.H;
