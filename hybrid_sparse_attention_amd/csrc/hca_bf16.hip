@@ -968,7 +968,14 @@ __global__ __launch_bounds__(512, 1) void hca_bwd_dq_kernel(HcaBwdParams bp, Bwd
   const int hw = wave & 3, rh = wave >> 2;
   const int n_hg = bp.H / 4;
   const int n_qt = (bp.T + 31) / 32;
-  const int unit = blockIdx.x / n_hg, hgi = blockIdx.x % n_hg;
+  // XCD-aware order as in the forward: the head groups of one token tile share an XCD
+  const int n_units = bp.B * n_qt;
+  const int xcd = blockIdx.x % 8, jj = blockIdx.x / 8;
+  int unit = (jj / n_hg) * 8 + xcd, hgi = jj % n_hg;
+  if ((int)gridDim.x % (8 * n_hg) != 0 || unit >= n_units) {  // ragged grid: plain order
+    unit = blockIdx.x / n_hg;
+    hgi = blockIdx.x % n_hg;
+  }
   const int b = unit / n_qt, qt = unit % n_qt;
   const int h = hgi * 4 + hw;
   const int T = bp.T, W = bp.window;
