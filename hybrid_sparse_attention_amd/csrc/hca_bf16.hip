@@ -258,14 +258,15 @@ __device__ __forceinline__ void row_softmax_pv(RowState& st, const f32x4_t (&s)[
 // buffer: tile ti is read from (k0, v0) or (k1, v1) while tile ti + 1 streams into the other
 // pair by LDS DMA.  The four buffers are separate LDS objects: the compiler can then prove that
 // reading one pair does not touch the transfers into the other and does not wait for them.
-template <class TileOf, class Consume>
+// WITH_V = false streams the key tiles alone.
+template <bool WITH_V = true, class TileOf, class Consume>
 __device__ __forceinline__ void tile_key_loop(const Src& src, const TileOf& tile_of, int n_tiles,
                                               int wave, int n_waves, int lane,
                                               const Consume& consume) {
   if (n_tiles > 0) {
     const Tile t0 = tile_of(0);
     dma_rows(src, t0, false, pf_k0, KLD, wave, n_waves, lane);
-    dma_rows(src, t0, true, pf_v0, VLD, wave, n_waves, lane);
+    if (WITH_V) dma_rows(src, t0, true, pf_v0, VLD, wave, n_waves, lane);
   }
   wait_all();
   __syncthreads();
@@ -274,7 +275,7 @@ __device__ __forceinline__ void tile_key_loop(const Src& src, const TileOf& tile
     if (ti + 1 < n_tiles) {
       const Tile tn = tile_of(ti + 1);
       dma_rows(src, tn, false, knxt, KLD, wave, n_waves, lane);
-      dma_rows(src, tn, true, vnxt, VLD, wave, n_waves, lane);
+      if (WITH_V) dma_rows(src, tn, true, vnxt, VLD, wave, n_waves, lane);
     }
     consume(t, kcur, vcur);
     wait_all();  // this wave's transfers of tile ti + 1 have landed
@@ -1039,7 +1040,30 @@ __global__ __launch_bounds__(512, 1) void hca_bwd_dq_kernel(HcaBwdParams bp, Bwd
   uint16_t* pw = ws.pw + row * W;
   uint16_t* dsw = ws.dsw + row * W;
 
-  for (int hf = 0; hf < 2; ++hf) {
+  // dQ^T += K^T (scale dS)^T over 16 column blocks (256 columns, half hf of the head), K read
+  // through the transposing read as V is in the forward; the B operand is scale dS rounded to
+  // bfloat16, the value the workspace holds
+  auto dq_tile = [&](f32x4_t (&dq)[16], const Frag8& pf, const char* kcur, int hf) {
+    const char* k0 = kcur + (4 * g + (l16 >> 2)) * KLD + 8 * (l16 & 3) + 512 * hf;
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) {
+      Frag8 ka;
+      const uint2 lo = lds_read_tr16(k0 + 32 * cb);
+      const uint2 hi = lds_read_tr16(k0 + 32 * cb + 16 * KLD);
+      ka.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      dq[cb] = mfma_16x16x32(ka, pf, dq[cb]);
+    }
+  };
+  auto store_dq = [&](const f32x4_t (&dq)[16], int hf) {
+    if (row_ok) {
+      uint16_t* dr = (uint16_t*)bp.dq + row * D + 256 * hf;
+#pragma unroll
+      for (int cb = 0; cb < 16; ++cb) store4(dr + 16 * cb + 4 * g, dq[cb]);
+    }
+  };
+  {
+    // First half: S and dP from K, V and the rows' Q, dO; P and scale dS of every (row, key)
+    // to the workspace.
     f32x4_t dq[16];
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb) dq[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1056,9 +1080,13 @@ __global__ __launch_bounds__(512, 1) void hca_bwd_dq_kernel(HcaBwdParams bp, Bwd
         for (int r = 0; r < 4; ++r) {
           const bool vis = t.full || visible(t, 16 * mb + 4 * g + r, tr, rp);
           pr[mb][r] = vis ? fast_exp2(sc[mb][r] * scale_log2 - lse2) : 0.f;
-          ds[mb][r] = pr[mb][r] * (dp[mb][r] - dlt);
+          ds[mb][r] = pr[mb][r] * (dp[mb][r] - dlt) * bp.scale;
         }
-      if (hf == 0 && row_ok) {
+      uint2 dsb[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        dsb[mb] = make_uint2(pack_bf16x2(ds[mb][0], ds[mb][1]), pack_bf16x2(ds[mb][2], ds[mb][3]));
+      if (row_ok) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
           const int j0 = t.start + 16 * mb + 4 * g;  // keys j0 .. j0 + 3
@@ -1066,9 +1094,7 @@ __global__ __launch_bounds__(512, 1) void hca_bwd_dq_kernel(HcaBwdParams bp, Bwd
             if (j0 < ws.ne_pad) {
               *(uint2*)(pc + j0) = make_uint2(pack_bf16x2(pr[mb][0], pr[mb][1]),
                                               pack_bf16x2(pr[mb][2], pr[mb][3]));
-              *(uint2*)(dsc + j0) =
-                  make_uint2(pack_bf16x2(ds[mb][0] * bp.scale, ds[mb][1] * bp.scale),
-                             pack_bf16x2(ds[mb][2] * bp.scale, ds[mb][3] * bp.scale));
+              *(uint2*)(dsc + j0) = dsb[mb];
             }
           } else {
 #pragma unroll
@@ -1076,31 +1102,50 @@ __global__ __launch_bounds__(512, 1) void hca_bwd_dq_kernel(HcaBwdParams bp, Bwd
               const int jj = i - (j0 + r);  // column t - s of the window arrays
               if (jj >= 0 && jj < W) {
                 pw[jj] = f32_to_bf16(pr[mb][r]);
-                dsw[jj] = f32_to_bf16(ds[mb][r] * bp.scale);
+                dsw[jj] = (uint16_t)((r & 1 ? (r < 2 ? dsb[mb].x : dsb[mb].y) >> 16
+                                            : (r < 2 ? dsb[mb].x : dsb[mb].y)) & 0xFFFFu);
               }
             }
           }
         }
       }
       Frag8 pf;
-      pf.u = make_uint4(pack_bf16x2(ds[0][0], ds[0][1]), pack_bf16x2(ds[0][2], ds[0][3]),
-                        pack_bf16x2(ds[1][0], ds[1][1]), pack_bf16x2(ds[1][2], ds[1][3]));
-      // dQ^T += K^T dS^T over this half's 16 column blocks (K read as V is in the forward)
-      const char* k0 = kcur + (4 * g + (l16 >> 2)) * KLD + 8 * (l16 & 3) + 512 * hf;
-#pragma unroll
-      for (int cb = 0; cb < 16; ++cb) {
-        Frag8 ka;
-        const uint2 lo = lds_read_tr16(k0 + 32 * cb);
-        const uint2 hi = lds_read_tr16(k0 + 32 * cb + 16 * KLD);
-        ka.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        dq[cb] = mfma_16x16x32(ka, pf, dq[cb]);
-      }
+      pf.u = make_uint4(dsb[0].x, dsb[0].y, dsb[1].x, dsb[1].y);
+      dq_tile(dq, pf, kcur, 0);
     });
-    if (row_ok) {
-      uint16_t* dr = (uint16_t*)bp.dq + row * D + 256 * hf;
+    store_dq(dq, 0);
+  }
+  {
+    // Second half: scale dS read back from the workspace (this lane wrote it above; 0 where the
+    // row does not see the key), so S and dP are not formed again and only K is streamed.
+    f32x4_t dq[16];
 #pragma unroll
-      for (int cb = 0; cb < 16; ++cb) store4(dr + 16 * cb + 4 * g, dq[cb] * bp.scale);
-    }
+    for (int cb = 0; cb < 16; ++cb) dq[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    tile_key_loop<false>(src, tile_of, n_tiles, wave, 8, lane,
+                         [&](const Tile& t, const char* kcur, const char*) {
+      uint2 dsb[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int j0 = t.start + 16 * mb + 4 * g;
+        dsb[mb] = make_uint2(0u, 0u);
+        if (!row_ok) continue;
+        if (t.kind == 0) {
+          if (j0 < ws.ne_pad) dsb[mb] = *(const uint2*)(dsc + j0);
+        } else {
+          uint32_t h4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int jj = i - (j0 + r);
+            h4[r] = (jj >= 0 && jj < W) ? (uint32_t)dsw[jj] : 0u;
+          }
+          dsb[mb] = make_uint2(h4[0] | (h4[1] << 16), h4[2] | (h4[3] << 16));
+        }
+      }
+      Frag8 pf;
+      pf.u = make_uint4(dsb[0].x, dsb[0].y, dsb[1].x, dsb[1].y);
+      dq_tile(dq, pf, kcur, 1);
+    });
+    store_dq(dq, 1);
   }
   // entries past the workgroup's last tile are invisible to its rows: zeros
   if (row_ok)
