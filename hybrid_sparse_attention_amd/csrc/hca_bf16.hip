@@ -33,6 +33,8 @@
 // partial (max, sum, O) of a split go to the workspace and a second kernel merges them.  When
 // gated, that kernel is the gate's: it streams W once, 64 channels of every row per workgroup,
 // and multiplies sigmoid(q_lat W) into the merged O of those channels.
+#include <type_traits>
+
 #include "common.h"
 #include "gate_skinny.h"
 #include "kernels.h"
@@ -448,52 +450,61 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// W stage of the gate: 32 tile rows of 1 KiB, unpadded; the 16-byte chunk c of tile row r sits
+// at position c ^ gw_sw(r), which keeps the transposing reads free of bank conflicts (measured
+// as fast as rows padded by 32 bytes) and leaves room in LDS for a fourth stage.
+constexpr int GROW = 1024;
+__device__ __forceinline__ int gw_sw(int r) { return 2 * (r & 7) + 16 * ((r >> 3) & 1); }
+
 // Step k0 of the gate contraction into one stage: rows k0 + 4 wave .. + 3 of the head's W
-// slice (1 KiB each) into a tile of pitch VLD, contraction index k0 + 8c + 4h + a (c, h, a
-// < 4, 2, 4) at tile row 16h + 4c + a, and the wave's 16 q_lat rows, columns
-// k0 .. k0 + 31 (64 bytes each), into its own 1 KiB of the q_lat tile of the stage, which
-// holds the workgroup's 128 rows: chunk-major within each 16-row block, lane l fetching
-// 16-byte chunk l / 16 of row l % 16, so that a fragment read (chunk g of rows l16) is 1 KiB
-// read contiguously by the 64 lanes, which the LDS serves without bank conflicts.  Five
-// transfers per wave.
+// slice (1 KiB each) into the stage's W tile, contraction index k0 + 8c + 4h + a (c, h, a
+// < 4, 2, 4) at tile row 16h + 4c + a (lane l fetching chunk l ^ gw_sw of that row), and the
+// wave's 16 q_lat rows, columns k0 .. k0 + 31 (64 bytes each), into its own 1 KiB block qdst
+// of the stage's q_lat tile, which holds the workgroup's 128 rows in 8 such blocks:
+// chunk-major within a block, lane l fetching 16-byte chunk l / 16 of row l % 16, so that a
+// fragment read (chunk g of rows l16) is 1 KiB read contiguously by the 64 lanes, which the
+// LDS serves without bank conflicts.  Five transfers per wave.
 // ql_wave is the q_lat row of the wave's first row and q_off the lane's byte offset from it
 // (its row, clamped to the last row, and its chunk).
 __device__ __forceinline__ void gate_dma(const char* w_head, size_t ldw, const char* ql_wave,
                                          uint32_t q_off, int k0, char* wdst, char* qdst,
                                          int wave, int lane) {
-  const uint32_t lo = (uint32_t)opaque(16 * lane);
 #pragma unroll
-  for (int u = 0; u < 4; ++u)  // index 4 wave + u: c = wave / 2, h = wave % 2, a = u
-    dma16_asm(w_head + (size_t)(k0 + 4 * wave + u) * ldw, lo,
-              lds_addr(wdst + (16 * (wave & 1) + 4 * (wave >> 1) + u) * VLD));
-  dma16_asm(ql_wave + 2 * k0, (uint32_t)opaque((int)q_off), lds_addr(qdst + 1024 * wave));
+  for (int u = 0; u < 4; ++u) {  // index 4 wave + u: c = wave / 2, h = wave % 2, a = u
+    const int tr = 16 * (wave & 1) + 4 * (wave >> 1) + u;
+    dma16_asm(w_head + (size_t)(k0 + 4 * wave + u) * ldw,
+              (uint32_t)opaque(16 * (lane ^ gw_sw(tr))), lds_addr(wdst + tr * GROW));
+  }
+  dma16_asm(ql_wave + 2 * k0, (uint32_t)opaque((int)q_off), lds_addr(qdst));
 }
-
-// Byte offset in a q_lat tile of columns 8c .. 8c + 7 of row r, c the 16-byte chunk (0..3).
-__device__ __forceinline__ int ql_chunk(int r, int c) { return 1024 * (r >> 4) + 256 * c + 16 * (r & 15); }
 
 // One contraction step of 32 for the wave's 64 channels (64 wave .. + 63 of the head) and all
 // 128 rows of the tile: G^T = W^T q_lat^T, acc[i][j] = G^T of channels 64 wave + 16 i .. and
 // rows 16 j ..  W^T comes from the stage's W tile through the transposing read of tile rows
 // 4g + a and 16 + 4g + a, which hold contraction indices 8g + a and 8g + 4 + a: slots
 // 8g .. 8g + 7 take indices 8g .. 8g + 7 in order, so the q_lat^T fragment of a lane is one
-// 16-byte chunk of its q_lat row.  Each W^T fragment feeds 8 products and each q_lat fragment
-// 4.
-__device__ __forceinline__ void gate_step(f32x4_t (&acc)[4][8], const char* ws, const char* qs,
+// 16-byte chunk of its q_lat row (qblk(j): the stage's block of rows 16j ..).  Each W^T
+// fragment feeds 8 products and each q_lat fragment 4.
+template <class QBlk>
+__device__ __forceinline__ void gate_step(f32x4_t (&acc)[4][8], const char* ws, const QBlk& qblk,
                                           int wave, int lane) {
   const int l16 = lane & 15, g = lane >> 4;
+  const int r = 4 * g + (l16 >> 2);  // tile row of the lo read; the hi read is row r + 16
+  const int fx = gw_sw(r);           // = gw_sw(r + 16)
+  const char* wr = ws + r * GROW + 8 * (l16 & 1);
+  const int cl = (l16 & 3) >> 1;
   Frag8 wa[4];
-  const char* v0 = ws + (4 * g + (l16 >> 2)) * VLD + 8 * (l16 & 3) + 128 * wave;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint2 lo = lds_read_tr16(v0 + 32 * i);
-    const uint2 hi = lds_read_tr16(v0 + 32 * i + 16 * VLD);
+    const char* a = wr + 16 * ((8 * wave + 2 * i + cl) ^ fx);
+    const uint2 lo = lds_read_tr16(a);
+    const uint2 hi = lds_read_tr16(a + 16 * GROW);
     wa[i].u = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     Frag8 qf;
-    qf.u = *(const uint4*)(qs + ql_chunk(16 * j + l16, g));
+    qf.u = *(const uint4*)(qblk(j) + 256 * g + 16 * l16);
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i][j] = mfma_16x16x32(wa[i], qf, acc[i][j]);
   }
@@ -502,6 +513,9 @@ __device__ __forceinline__ void gate_step(f32x4_t (&acc)[4][8], const char* ws, 
 __shared__ __attribute__((aligned(1024))) char pf_q0[8 * 1024];
 __shared__ __attribute__((aligned(1024))) char pf_q1[8 * 1024];
 __shared__ __attribute__((aligned(1024))) char pf_q2[8 * 1024];
+// the fourth q_lat stage: blocks 0..3 in the 1 KiB past the W tile in each key/value buffer,
+// blocks 4..7 here
+__shared__ __attribute__((aligned(1024))) char pf_q3h[4 * 1024];
 
 __global__ __launch_bounds__(512, 1) void hca_prefill_gated_kernel(HcaParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -611,7 +625,7 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_gated_kernel(HcaParams p) 
   }
 
   // ------------------------------------------------------------------ gate
-  // Three stages (W tile + q_lat tile), two steps in flight ahead of the one being read.
+  // Four stages (W tile + q_lat tile), three steps in flight ahead of the one being read.
   const size_t ldw = (size_t)p.H * D * 2;  // bytes of one W row
   const size_t ldq = (size_t)p.d_lat * 2;  // bytes of one q_lat row
   const char* w_head = (const char*)p.w_gate + (size_t)h * ROWB;
@@ -626,21 +640,38 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_gated_kernel(HcaParams p) 
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto wst = [](int i) { return i == 0 ? pf_k0 : (i == 1 ? pf_v0 : pf_k1); };
-  auto qst = [](int i) { return i == 0 ? pf_q0 : (i == 1 ? pf_q1 : pf_q2); };
+  // stage st: W tile in key/value buffer st, q_lat blocks in pf_q<st> (st < 3) or split over
+  // the four buffers' last KiB and pf_q3h (st = 3)
+  auto wst = [](int st) { return st == 0 ? pf_k0 : (st == 1 ? pf_v0 : (st == 2 ? pf_k1 : pf_v1)); };
+  auto qblk = [&](int st, int j) -> char* {
+    if (st < 3) return (st == 0 ? pf_q0 : (st == 1 ? pf_q1 : pf_q2)) + 1024 * j;
+    return j < 4 ? wst(j) + 32 * GROW : pf_q3h + 1024 * (j - 4);
+  };
+  auto issue = [&](int step, int st) {
+    gate_dma(w_head, ldw, ql_wave, q_off, step * KT, wst(st), qblk(st, wave), wave, lane);
+  };
   // the key loop ended with a barrier: every stage is free
-  gate_dma(w_head, ldw, ql_wave, q_off, 0, wst(0), qst(0), wave, lane);
-  if (nk > 1) gate_dma(w_head, ldw, ql_wave, q_off, KT, wst(1), qst(1), wave, lane);
-  if (nk > 1) wait_vm<5>(); else wait_vm<0>();
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  if (nk > 2) issue(2, 2);
+  if (nk > 2) wait_vm<10>(); else if (nk > 1) wait_vm<5>(); else wait_vm<0>();
   lds_barrier();
-  for (int s = 0; s < nk; ++s) {
-    // step s + 2 goes into the stage step s - 1 read (free since the barrier that ended it)
-    const int st2 = (s + 2) % 3;
-    if (s + 2 < nk)
-      gate_dma(w_head, ldw, ql_wave, q_off, (s + 2) * KT, wst(st2), qst(st2), wave, lane);
-    gate_step(acc, wst(s % 3), qst(s % 3), wave, lane);
-    if (s + 2 < nk) wait_vm<5>(); else wait_vm<0>();  // step s + 1 has landed
+  // step s on stage ST = s % 4; step s + 3 goes into the stage step s - 1 read (free since the
+  // barrier that ended it); at the end, step s + 1 must have landed while the transfers of
+  // steps s + 2 and s + 3 (5 each, when they exist) may still fly
+  auto one = [&](int s, auto stc) {
+    constexpr int ST = decltype(stc)::value;
+    if (s + 3 < nk) issue(s + 3, (ST + 3) & 3);
+    gate_step(acc, wst(ST), [&](int j) { return qblk(ST, j); }, wave, lane);
+    const int later = min(nk - 1, s + 3) - (s + 1);
+    if (later >= 2) wait_vm<10>(); else if (later == 1) wait_vm<5>(); else wait_vm<0>();
     lds_barrier();
+  };
+  for (int s = 0; s < nk; s += 4) {
+    one(s, std::integral_constant<int, 0>());
+    if (s + 1 < nk) one(s + 1, std::integral_constant<int, 1>());
+    if (s + 2 < nk) one(s + 2, std::integral_constant<int, 2>());
+    if (s + 3 < nk) one(s + 3, std::integral_constant<int, 3>());
   }
 
   // sigmoid(G) as bfloat16 into LDS, rows of the tile 32 to a buffer (pitch VLD): the last
