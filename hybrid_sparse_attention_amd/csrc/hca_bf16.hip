@@ -411,9 +411,9 @@ __global__ __launch_bounds__(512, 1) void hca_prefill_kernel(HcaParams p) {
 // Then the gate G = q_lat W for the tile's 128 rows and the head's 512 channels, sliced by
 // channel: wave w computes G^T for channels 64w .. 64w + 63 and all 128 rows, so each W^T
 // fragment feeds 8 products.  Each contraction step of 32 brings a 32-row slice of the head's
-// W columns (laid out as a value tile: its transposed reads give W^T) and the 128 q_lat rows'
-// 32 columns to LDS by LDS DMA, through a three-stage ring, two steps ahead of the one being
-// read.  Meanwhile O waits in the registers as packed bfloat16 (the value the unfused path
+// W columns (its transposed reads give W^T) and the 128 q_lat rows' 32 columns to LDS by LDS
+// DMA, through a four-stage ring, three steps ahead of the one being read (the stages reuse
+// the key/value buffers, 160 KiB of LDS in all).  Meanwhile O waits in the registers as packed bfloat16 (the value the unfused path
 // would store).  sigmoid(G), rounded to bfloat16, crosses to the row layout of O through LDS;
 // each wave writes out = O * sigmoid(G) over it and stores its 16 rows whole, 1 KiB per
 // instruction.

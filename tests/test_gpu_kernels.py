@@ -111,14 +111,14 @@ def test_hca_prefill_chunked_positions(torch, orc):
     bf16_ok(from_dev(out).reshape(-1, H, 512), ref, "hca chunked")
 
 
-@pytest.mark.parametrize("d_lat", [384, 128, 192])
+@pytest.mark.parametrize("d_lat", [384, 128, 192, 64])
 def test_hca_prefill_gated_ring_positions(torch, orc, d_lat):
     """The gated prefill over a ring of raw rows: two sequences whose 200 query rows start at
     positions 0 and 1000, raw rows in a 512-row ring (position p in row p % 512; 512 >= window
-    + 199), entries from each whole prefix.  Gate contractions of 384 (two groups of four
-    steps of 32 before the last four) and 128 (the last four only) run in the attention
-    epilogue; 192 (not a multiple of 128) runs the gate GEMM after the attention kernel.  The
-    log-sum-exp written matches the ungated kernel's."""
+    + 199), entries from each whole prefix.  The gate runs in the attention epilogue through a
+    ring of four stages, steps of 32: contractions of 384 (three rounds of the four stages),
+    128 (one round), 192 (a round and a half) and 64 (two steps, fewer than the three the ring
+    keeps in flight).  The log-sum-exp written matches the ungated kernel's."""
     B, Tq, H, W, ctx = 2, 200, 3, 512, 1200
     pos0 = np.array([0, 1000], np.int32)
     q = synth.normal(233, (B, Tq, H, 512), 1.0, True)
