@@ -13,7 +13,7 @@ namespace sparse_tile {
 
 constexpr int D = 256;                  // head width of query/key and value
 constexpr int KT = 32;                  // keys per tile
-constexpr int TROW = 2 * D;             // bytes of one gathered row (no padding: swizzled)
+constexpr int TROW = 2 * D;             // bytes of one gathered row (no padding: rotated)
 constexpr int TILE = KT * TROW;         // 16 KiB
 
 // 16-byte position of chunk c (0..31) of tile row r, and the chunk held at position q
