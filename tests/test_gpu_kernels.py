@@ -80,9 +80,11 @@ def _hca_gpu(x, kc, vc, max_pos, gated, window=128, dev_out=None):
 
 
 # (1100, 30) leaves half of the last 4-head group idle; (1500, 64) is the full head count with
-# 752 (token tile, head group) workgroups
+# 752 (token tile, head group) workgroups; (1100, 8) gated takes the fused kernel's XCD order
+# (head count a multiple of 8) over 9 token tiles, each XCD starting one tile further on
 @pytest.mark.parametrize("T,H,gated", [(1100, 3, True), (1100, 2, False), (100, 2, True),
-                                       (257, 1, True), (1100, 30, True), (1500, 64, False)])
+                                       (257, 1, True), (1100, 30, True), (1500, 64, False),
+                                       (1100, 8, True)])
 def test_hca_prefill_bf16(torch, orc, T, H, gated):
     x = synth.hca_prefill(220 + T % 7, T=T, H=H, bf16=True, gated=gated)
     kd, vd = to_dev(x["k"]), to_dev(x["v"])
