@@ -1195,10 +1195,10 @@ constexpr int BW_NKB = BW_NK / 16;
 // C[s][t] = scale dS (or P) of (t, h) at key s when 0 <= t - s < window, and the 32 rows of Q
 // (or dO) of head h go to LDS; then dK[s][c] += sum_t C[s][t] Q[t][c] on the MFMA (A = C rows,
 // B = Q^T by the transposing read).
-// The steps of a workgroup are (token tile t0, head h) pairs, heads fastest; the Q and dO rows
-// of step i + 1 stream into one pair of LDS buffers by LDS DMA (rows past T repeat the last row:
-// their coefficients are 0) and its coefficients into registers while step i's products run on
-// the other pair, with one barrier per step.
+// The steps of a workgroup are (head h, token tile t0) pairs, token tiles fastest; the Q and dO
+// rows of step i + 1 stream into one pair of LDS buffers by LDS DMA (rows past T repeat the
+// last row: their coefficients are 0) and its coefficients into registers while step i's
+// products run on the other pair, with one barrier per step.
 __shared__ __attribute__((aligned(16))) uint16_t bw_ck0[BW_NK * BW_CLD];
 __shared__ __attribute__((aligned(16))) uint16_t bw_cv0[BW_NK * BW_CLD];
 __shared__ __attribute__((aligned(16))) uint16_t bw_ck1[BW_NK * BW_CLD];
@@ -1210,18 +1210,26 @@ __global__ __launch_bounds__(512, 1) void hca_bwd_dkv_kernel(HcaBwdParams bp, Bw
   const int l16 = lane & 15, g = lane >> 4;
   const int T = bp.T, W = bp.window, H = bp.H;
   const int n_kt = (T + BW_NK - 1) / BW_NK;
-  const int b = blockIdx.x / n_kt, s0 = (blockIdx.x % n_kt) * BW_NK;
+  // XCD-aware order: XCD x takes a contiguous run of key blocks, so the ~32 blocks it holds at
+  // once are neighbours, whose token bands overlap (each Q and dO row is needed by about three
+  // of them) and are served from its L2
+  const int n_blk = (int)gridDim.x;
+  const int lin = n_blk % 8 == 0 ? (int)(blockIdx.x % 8) * (n_blk / 8) + (int)blockIdx.x / 8
+                                 : (int)blockIdx.x;
+  const int b = lin / n_kt, s0 = (lin % n_kt) * BW_NK;
   f32x4_t ak[BW_NKB][4], av[BW_NKB][4];
 #pragma unroll
   for (int sb = 0; sb < BW_NKB; ++sb)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) ak[sb][cb] = av[sb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // tokens that see one of the keys: s0 .. t_end - 1
+  // tokens that see one of the keys: s0 .. t_end - 1; steps are (head, token tile) pairs, token
+  // tiles fastest, so neighbouring key blocks need the same rows within a few steps
   const int t_end = min(T, s0 + BW_NK - 1 + W);
-  const int n_steps = (t_end - s0 + 31) / 32 * H;
+  const int n_tt = (t_end - s0 + 31) / 32;
+  const int n_steps = n_tt * H;
   // Q and dO rows of step i: 64 rows of 1 KiB (32 of Q, then 32 of dO), eight per wave
   auto dma_step = [&](int i, char* dq, char* dd) {
-    const int t0 = s0 + 32 * (i / H), h = i % H;
+    const int t0 = s0 + 32 * (i % n_tt), h = i / n_tt;
     const uint32_t lo = (uint32_t)opaque(16 * lane);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -1233,14 +1241,16 @@ __global__ __launch_bounds__(512, 1) void hca_bwd_dkv_kernel(HcaBwdParams bp, Bw
       lds_dma16(src + lo, (row < 32 ? dq : dd) + rr * KLD);
     }
   };
-  // coefficients of keys s0 + sr and tokens t0 + tc, BW_NK / 16 (sr, tc) per thread
+  // coefficients of keys s0 + sr and tokens t0 + tc, BW_NK / 16 (sr, tc) per thread; the keys
+  // run fastest across lanes, so a wave's loads read one token's BW_NK consecutive window
+  // offsets (one row of the workspace) instead of one value from each of 32 rows
   uint16_t cfk[BW_NK / 16], cfv[BW_NK / 16];
   auto load_coef = [&](int i) {
-    const int t0 = s0 + 32 * (i / H), h = i % H;
+    const int t0 = s0 + 32 * (i % n_tt), h = i / n_tt;
 #pragma unroll
     for (int u = 0; u < BW_NK / 16; ++u) {
       const int e = tid + 512 * u;  // 0 .. 32 BW_NK - 1
-      const int sr = e >> 5, tc = e & 31;
+      const int sr = e % BW_NK, tc = e / BW_NK;
       const int s = s0 + sr, t = t0 + tc, jj = t - s;
       cfk[u] = cfv[u] = 0;
       if (t < T && s < T && jj >= 0 && jj < W) {
@@ -1254,7 +1264,7 @@ __global__ __launch_bounds__(512, 1) void hca_bwd_dkv_kernel(HcaBwdParams bp, Bw
 #pragma unroll
     for (int u = 0; u < BW_NK / 16; ++u) {
       const int e = tid + 512 * u;
-      const int sr = e >> 5, tc = e & 31;
+      const int sr = e % BW_NK, tc = e / BW_NK;
       ck[sr * BW_CLD + tc] = cfk[u];
       cv[sr * BW_CLD + tc] = cfv[u];
     }
