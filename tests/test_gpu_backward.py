@@ -93,11 +93,13 @@ def _hca_case(torch, seed, B, T, H, window, block):
 
 
 @pytest.mark.parametrize("B,T,H,window,block", [(2, 300, 4, 48, 32), (1, 1100, 4, 128, 128),
-                                                (1, 40, 8, 64, 128), (1, 260, 4, 100, 64)])
+                                                (1, 40, 8, 64, 128), (1, 260, 4, 100, 64),
+                                                (2, 1024, 4, 128, 128)])
 def test_hca_backward(torch, B, T, H, window, block):
     """dq, dk, dv against the float64 oracle (which rebuilds everything from q, k, v): the
     window path, the pooled path (an entry's gradient spread over its block) and a sequence
-    shorter than a block."""
+    shorter than a block.  (2, 1024) gives the dq and dkv kernels workgroup counts that are
+    multiples of 8 (64 and 32), so both take their XCD-aware orders across two sequences."""
     (q, k, v, dout), (dq, dk, dv) = _hca_case(torch, 150 + T, B, T, H, window, block)
     r_q, r_k, r_v = backward.hca_attn_bwd(q, np.zeros(B, np.int32), k, v, dout, window=window,
                                           block=block)
